@@ -1,0 +1,120 @@
+"""Quantizers and canonical packing of the oracle (TEST INFRASTRUCTURE ONLY).
+
+Weights are handled in the "nt" orientation of the BitBLAS problem descriptor
+(Bitblas lecture 033, API example: ``layout="nt"``) and of the FP4 preparation step
+(FlashInfer PR #4466 analysis, section 2: the weight is ``[n, k/2]``): row n of ``wt``
+holds column n of the logical W[K, N], i.e. ``wt[n, k] = W[k, n]``.
+
+Readings where the pages are silent (each is listed in the design notes):
+* rounding is round-half-even everywhere, divisions are done in float64 and rounded
+  once to the target format;
+* the quantizer divides by the *stored* (already rounded) scale, so that dequantizing
+  the stored codes and scales is self-consistent;
+* an all-zero INT4 group gets scale 0 and codes 8 (signed 0); an all-zero FP4 block gets
+  scale code 0 and codes 0; an all-zero FP8 tensor gets alpha 0 and codes 0.
+"""
+import numpy as np
+
+from . import codecs
+
+
+# ----------------------------------------------------------------------------- INT4
+def quantize_int4(wt, group_size):
+    """Symmetric absmax INT4 per (K-group, column).
+
+    Low Bit Triton Kernels (lecture 034), core pattern: one scale per group of
+    ``group_size`` consecutive K, group 128 being the common choice; gemlite snippet:
+    the stored nibble is the signed value + 8.  The scale is absmax / 7 rounded to
+    fp16, the code is clamp(rint(w / s), -8, 7) + 8.
+
+    wt: float32 [N, K].  Returns (codes uint8 [N, K] in 0..15, scale_bits uint16 [K/G, N]).
+    """
+    wt = np.asarray(wt, dtype=np.float32)
+    N, K = wt.shape
+    G = int(group_size)
+    if K % G:
+        raise ValueError("K must be a multiple of group_size")
+    w = wt.astype(np.float64).reshape(N, K // G, G)
+    amax = np.abs(w).max(axis=2)                        # [N, K/G]
+    s = codecs.f16_round(amax / 7.0)                    # stored scale value
+    safe = np.where(s == 0, 1.0, s)
+    q = np.clip(np.rint(w / safe[:, :, None]), -8, 7)
+    q = np.where(s[:, :, None] == 0, 0.0, q)
+    codes = (q + 8).astype(np.uint8).reshape(N, K)
+    scale_bits = codecs.f16_bits(s).T.copy()            # [K/G, N]
+    return codes, scale_bits
+
+
+# ----------------------------------------------------------------------------- FP8
+def quantize_fp8(wt):
+    """Per-tensor FP8 e4m3 (FlashInfer PR #7495 analysis, introduction).
+
+    alpha = absmax / 448 rounded to fp32; code = e4m3(clamp(w / alpha, +-448)).
+    Returns (codes uint8 [N, K], alpha as a Python float that is an fp32 value).
+    """
+    w = np.asarray(wt, dtype=np.float32).astype(np.float64)
+    amax = float(np.abs(w).max()) if w.size else 0.0
+    alpha = float(np.float32(amax / 448.0))
+    if alpha == 0.0:
+        return np.zeros(w.shape, np.uint8), 0.0
+    x = np.clip(w / alpha, -codecs.E4M3_MAX, codecs.E4M3_MAX)
+    return codecs.e4m3_encode(x), alpha
+
+
+# ----------------------------------------------------------------------------- FP4
+def quantize_fp4(wt):
+    """FP4 e2m1 with an e4m3 scale per 16 consecutive K and one fp32 alpha.
+
+    The pages give only the operands (FlashInfer PR #4466 analysis, section 2: weight,
+    per-block descale, optional alpha); the recipe is the plainest two-level absmax:
+      alpha = absmax(W) / (6 * 448)                  (rounded to fp32)
+      s_b   = e4m3(min(absmax_b / (6 * alpha), 448))  per (n, block of 16 k)
+      code  = e2m1(clamp(w / (s_b * alpha), +-6)),    code 0 where s_b == 0.
+    Returns (codes uint8 [N, K] in 0..15, sf codes uint8 [N, K/16], alpha float).
+    """
+    w = np.asarray(wt, dtype=np.float32).astype(np.float64)
+    N, K = w.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    amax = float(np.abs(w).max()) if w.size else 0.0
+    alpha = float(np.float32(amax / (6.0 * 448.0)))
+    wb = w.reshape(N, K // 16, 16)
+    if alpha == 0.0:
+        return np.zeros((N, K), np.uint8), np.zeros((N, K // 16), np.uint8), 0.0
+    bmax = np.abs(wb).max(axis=2)
+    sf_codes = codecs.e4m3_encode(np.minimum(bmax / (6.0 * alpha), codecs.E4M3_MAX))
+    sb = codecs.e4m3_decode(sf_codes)                  # stored block scale
+    denom = sb * alpha                                  # exact in float64
+    safe = np.where(denom == 0, 1.0, denom)
+    x = np.clip(wb / safe[:, :, None], -codecs.E2M1_MAX, codecs.E2M1_MAX)
+    x = np.where(denom[:, :, None] == 0, 0.0, x)
+    codes = codecs.e2m1_encode(x).reshape(N, K)
+    return codes, sf_codes.astype(np.uint8), alpha
+
+
+# ----------------------------------------------------------------------------- canonical packing
+def pack_nibbles(codes):
+    """Two 4-bit codes per byte along K, low nibble = even k (two per byte, low first).
+
+    codes uint8 [N, K] (values 0..15) -> uint8 [N, K/2].
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    if c.shape[1] % 2:
+        raise ValueError("K must be even")
+    if np.any(c > 15):
+        raise ValueError("nibble codes must be < 16")
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed):
+    """Inverse of pack_nibbles: uint8 [N, K/2] -> codes uint8 [N, K]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def int4_signed(codes):
+    """Signed INT4 value of a stored nibble: nibble - 8 (gemlite snippet, lecture 034)."""
+    return np.asarray(codes, dtype=np.int64) - 8

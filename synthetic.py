@@ -1,0 +1,50 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds none of the method's arithmetic: it only draws Gaussian numbers and
+casts activations to their 16-bit type with torch's own cast.  Quantization, packing and
+the GEMM live in the library (GPU path) and, independently, in the oracle.
+
+Workloads (LLM linear layers; no dataset or trained weights are involved):
+  A ~ N(0, 1) cast to fp16 (INT4 shapes) or bf16 (FP8 / FP4 shapes);
+  W ~ N(0, sigma) in fp32, sigma = 0.02 (INT4, FP4) or 0.05 (FP8), drawn in the
+  "nt" orientation [N, K] (row n = output column n).
+Seeds are numpy ``default_rng([workload, shape, role])`` with role 0 = A, 1 = W.
+"""
+import numpy as np
+
+ROLE_A, ROLE_W = 0, 1
+
+# named workloads: (name, format, list of (M, N, K), extra)
+WORKLOADS = {
+    "int4_tiny": dict(fmt="int4", shapes=[(1, 256, 512)], group_sizes=[128], sigma=0.02),
+    "int4_decode": dict(fmt="int4", shapes=[(1, 4096, 4096), (16, 4096, 4096),
+                                            (1, 11008, 4096), (16, 11008, 4096)],
+                        group_sizes=[128], sigma=0.02),
+    "int4_prefill": dict(fmt="int4", shapes=[(4096, 4096, 4096)],
+                         group_sizes=[32, 64, 128, 256], sigma=0.02),
+    "fp8": dict(fmt="fp8", shapes=[(1, 10240, 5120), (16, 10240, 5120), (8192, 10240, 5120),
+                                   (32768, 3200, 5120), (16384, 12800, 5120)],
+                group_sizes=[0], sigma=0.05),
+    "fp4": dict(fmt="fp4", shapes=[(1, 8192, 8192), (128, 8192, 8192), (8192, 8192, 8192)],
+                group_sizes=[16], sigma=0.02),
+}
+WORKLOAD_INDEX = {name: i for i, name in enumerate(WORKLOADS)}
+
+
+def rng(*key):
+    return np.random.default_rng([int(k) for k in key])
+
+
+def activations(M, K, kind, key):
+    """A ~ N(0,1) as a CPU torch tensor of dtype fp16 ('f16') or bf16 ('bf16')."""
+    import torch
+    x = rng(*key, ROLE_A).standard_normal((M, K), dtype=np.float32)
+    t = torch.from_numpy(x)
+    return t.to(torch.float16 if kind == "f16" else torch.bfloat16)
+
+
+def weights(N, K, sigma, key):
+    """W ~ N(0, sigma) as float32 [N, K] (row n holds output column n)."""
+    w = rng(*key, ROLE_W).standard_normal((N, K), dtype=np.float32)
+    w *= np.float32(sigma)
+    return w
