@@ -1,0 +1,184 @@
+/*
+ * qgemm.h -- C ABI of a weight-only quantized GEMM for AMD MI355X (gfx950).
+ *
+ *   out[M, N] = A[M, K] . dequant(W)[K, N]            (times alpha for FP8 / FP4)
+ *
+ * A holds 16-bit activations; W is stored packed at low precision and is dequantized
+ * in registers inside the kernels -- no 16-bit copy of W is ever written to memory.
+ *
+ * Formats (all other combinations return QGEMM_ERR_UNSUPPORTED):
+ *   a_dtype  w_dtype        scale_layout          out_dtype     source
+ *   F16      INT4           GROUP_F16 (G=32..256) F16 or F32    Low Bit Triton Kernels (GPU MODE
+ *                                                               lecture 034), core pattern and
+ *                                                               gemlite snippet; Bitblas lecture 033,
+ *                                                               API example (MatmulConfig)
+ *   BF16     FP8_E4M3       TENSOR_F32            BF16 or F32   FlashInfer PR #7495 analysis
+ *                                                               (mm_bf16_fp8), introduction and
+ *                                                               section 2 (public API)
+ *   BF16     FP4_E2M1       BLOCK16_E4M3          BF16 or F32   FlashInfer PR #4466 analysis
+ *                                                               (BF16 x FP4 GEMM), sections 1-3
+ *
+ * Value semantics (what the kernels compute):
+ *   INT4 : w[k][n] = RNE_fp16((nibble - 8) * s[k / G][n]) -- the 16-bit operand the
+ *          gemlite snippet forms -- accumulated in fp32.  No alpha.
+ *   FP8  : w = e4m3(code) (exact in bf16); the fp32 per-tensor alpha multiplies the fp32
+ *          accumulator once, in the epilogue, as the PR #7495 analysis prescribes.
+ *   FP4  : w = e2m1(code) * e4m3(s_b) (exact in bf16) with one scale per 16 consecutive
+ *          K of a column; alpha multiplies the fp32 accumulator in the epilogue.
+ *   The 16-bit output is the round-to-nearest-even cast of the fp32 result, so a call
+ *   with out_dtype F32 yields exactly the values a 16-bit call rounds.
+ *
+ * Threading and ownership: the library allocates no device memory, frees nothing and keeps
+ * no per-call state; every buffer belongs to the caller.  All entry points are thread-safe.
+ * Errors are returned synchronously before anything is enqueued; a detail string naming
+ * the offending argument is available from qgemm_last_error() on the calling thread.
+ * No C++ exception ever crosses this interface.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qgemm_status {
+  QGEMM_OK = 0,
+  QGEMM_ERR_INVALID_ARGUMENT = 1,   /* bad shape, NULL pointer, bad enum value          */
+  QGEMM_ERR_UNSUPPORTED = 2,        /* valid but unsupported dtype / layout combination  */
+  QGEMM_ERR_MISALIGNED = 3,         /* a pointer violates its alignment requirement      */
+  QGEMM_ERR_WORKSPACE_TOO_SMALL = 4,
+  QGEMM_ERR_HIP = 5                 /* the HIP runtime reported an error at launch       */
+} qgemm_status_t;
+
+typedef enum qgemm_dtype {
+  QGEMM_DT_F16 = 0,
+  QGEMM_DT_BF16 = 1,
+  QGEMM_DT_F32 = 2,
+  QGEMM_DT_INT4 = 3,
+  QGEMM_DT_FP8_E4M3 = 4,   /* OCP e4m3 ("fn"): max 448, code S.1111.111 is NaN        */
+  QGEMM_DT_FP4_E2M1 = 5    /* e2m1: +-{0, .5, 1, 1.5, 2, 3, 4, 6}                      */
+} qgemm_dtype_t;
+
+typedef enum qgemm_scale_layout {
+  QGEMM_SCALE_GROUP_F16 = 0,     /* INT4: fp16 scale per (group of G consecutive K, column) */
+  QGEMM_SCALE_TENSOR_F32 = 1,    /* FP8 : no weight scales; one fp32 alpha (device pointer) */
+  QGEMM_SCALE_BLOCK16_E4M3 = 2   /* FP4 : e4m3 scale per (16 consecutive K, column) + alpha */
+} qgemm_scale_layout_t;
+
+/* kernel_hint values (testing and tuning; 0 is the right choice for applications) */
+#define QGEMM_KERNEL_AUTO 0
+#define QGEMM_KERNEL_DECODE 1     /* memory-bound skinny kernel, M <= 16 only            */
+#define QGEMM_KERNEL_PREFILL 2    /* MFMA tile kernel, any M                              */
+
+/*
+ * The problem descriptor, after the BitBLAS MatmulConfig (Bitblas lecture 033, API
+ * example): sizes, operand dtypes, group size and scale layout.  Fields are fixed-width
+ * so the struct has the same layout from C, C++ and ctypes (56 bytes).
+ *   M >= 1 (any value); N % 16 == 0; K % 128 == 0; for INT4 also K % group_size == 0.
+ *   group_size: INT4 only, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
+ *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
+ *   slices (1..64) the chosen kernel uses.  Both only change the reduction order of the
+ *   fp32 accumulation, never the packed layout.
+ */
+typedef struct qgemm_problem {
+  int64_t M, N, K;
+  int32_t a_dtype, w_dtype, out_dtype;
+  int32_t group_size;
+  int32_t scale_layout;
+  int32_t kernel_hint;
+  int32_t split_k_hint;
+  int32_t reserved;          /* must be 0 */
+} qgemm_problem_t;
+
+/*
+ * qgemm_quantize -- offline, host memory only, no GPU needed.
+ * Quantizes fp32 weights W given in the "nt" orientation w_nk[N][K] (row n is output
+ * column n; the BitBLAS "nt" layout) into the canonical form that qgemm_pack takes:
+ *   INT4: codes_canonical uint8[N][K/2], byte j of row n = code(k=2j) | code(k=2j+1) << 4,
+ *         code = clamp(rint(w / s), -8, 7) + 8; scales_canonical fp16 [K/G][N] with
+ *         s = RNE_fp16(absmax_group / 7)   (Low Bit Triton Kernels, core pattern: one
+ *         scale per 128-ish group along K; gemlite snippet: nibble - 8).
+ *   FP8 : codes uint8[N][K] = e4m3(clamp(w / alpha, +-448)), alpha = absmax / 448 (fp32);
+ *         scales_canonical unused (may be NULL).
+ *   FP4 : codes uint8[N][K/2] (nibble order as INT4) = e2m1(clamp(w / (s_b alpha), +-6)),
+ *         scales_canonical e4m3 uint8[N][K/16] = e4m3(min(absmax_b / (6 alpha), 448)),
+ *         alpha = absmax / (6 * 448) (fp32).
+ * Rounding is round-half-even; divisions are done in double and rounded once.  An
+ * all-zero group / block / tensor gets scale 0 and signed code 0.  alpha_out receives
+ * alpha (FP8, FP4) or 1.0 (INT4); it may be NULL for INT4.
+ */
+qgemm_status_t qgemm_quantize(const qgemm_problem_t* problem, const float* w_nk,
+                              void* codes_canonical, void* scales_canonical, float* alpha_out);
+
+/*
+ * qgemm_pack -- offline, host memory only, no GPU needed.
+ * Reorders canonical weights and scales (the layout qgemm_quantize writes) into the
+ * device layout whose 16-byte lane chunks are gfx950 16x16x32 MFMA operand fragments, so
+ * that no layout conversion happens at run time (Bitblas lecture 033, layout section: a
+ * mismatched fragment layout forces a re-layout through shared memory).  Byte map, with
+ * lane l of a 64-lane wavefront owning bytes [16 l, 16 l + 16) of every 1 KiB block:
+ *   INT4 / FP4 weights: block (nb, kb) = columns 16nb..16nb+15 x k 128kb..128kb+127, block
+ *     index nb*(K/128) + kb; dword t (0..3) of lane l holds column 16nb + (l & 15) at
+ *     k = 128kb + 32t + 8(l >> 4) + J[s] in nibble s (bits 4s..4s+3), with
+ *     J = (0,2,4,6,1,3,5,7) for INT4 and J = (0,1,...,7) for FP4.
+ *   FP8 weights: block (nb, kb) = 16 columns x 64 k, index nb*(K/64) + kb; byte 8t + j
+ *     (t = 0..1, j = 0..7) of lane l is column 16nb + (l & 15), k = 64kb + 32t + 8(l>>4) + j.
+ *   INT4 scales (fp16): span = max(G, 128), T = max(1, 128/G); element
+ *     ((nb*(K/span) + kb)*16 + c)*T + t = scale of column 16nb + c, group kb*(span/G) + t.
+ *   FP4 scales (e4m3): byte ((nb*(K/128) + kb)*16 + c)*8 + 4h + t = scale of column
+ *     16nb + c, 16-k block 8kb + 2t + h.
+ * Size query: pass w_packed == NULL and/or s_packed == NULL to receive the sizes only.
+ * w_packed_bytes / s_packed_bytes are in/out: on input the capacity of the buffer (when
+ * the buffer is non-NULL), on output the bytes needed.  FP8 has no packed scales
+ * (s_packed_bytes = 0).  problem->M is ignored.
+ */
+qgemm_status_t qgemm_pack(const qgemm_problem_t* problem, const void* w_canonical,
+                          const void* scales_canonical, void* w_packed, size_t* w_packed_bytes,
+                          void* s_packed, size_t* s_packed_bytes);
+
+/*
+ * qgemm_workspace_bytes -- bytes of device workspace qgemm_run needs for this problem
+ * (0 when none).  Workspace contract (for split-K reductions, FlashInfer PR #7495
+ * analysis, section 2 names a workspace argument and a size query): the caller allocates
+ * it, ZERO-FILLED, once; every completed qgemm_run returns its counter words to zero, so
+ * it can be reused by later calls on the same stream without clearing.  Calls that overlap
+ * in time (different streams) must use different workspaces.
+ */
+qgemm_status_t qgemm_workspace_bytes(const qgemm_problem_t* problem, size_t* bytes);
+
+/*
+ * qgemm_run -- enqueue out = A . dequant(W) (* alpha) on `stream`.
+ *   A        device, row-major [M][K] of a_dtype, 16-byte aligned.
+ *   w_packed device, qgemm_pack output, 16-byte aligned.
+ *   s_packed device, qgemm_pack scale output (INT4, FP4; NULL for FP8), 16-byte aligned.
+ *   alpha    device pointer to one fp32 (FP8, FP4; NULL for INT4); 4-byte alignment only
+ *            (FlashInfer PR #7495 analysis, section 3(a): scalar pointers must not be
+ *            assumed 16-byte aligned).
+ *   out      device, row-major [M][N] of out_dtype, 16-byte aligned.
+ *   workspace / workspace_bytes: see qgemm_workspace_bytes; 256-byte aligned; may be
+ *            NULL when 0 bytes are needed.
+ *   stream   a hipStream_t; NULL means the default stream.
+ * Returns after enqueueing; kernel faults surface at the caller's next synchronisation.
+ * The result is bitwise deterministic for a given problem (including its hints).
+ */
+qgemm_status_t qgemm_run(const qgemm_problem_t* problem, const void* A, const void* w_packed,
+                         const void* s_packed, const float* alpha, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* qgemm_status_string(qgemm_status_t status);
+
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* qgemm_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t qgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

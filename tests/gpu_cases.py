@@ -1,0 +1,100 @@
+"""Shared machinery of the GPU parity tests: seeded inputs, oracle references, a runner
+that calls the library through the C ABI, and the comparison against the oracle."""
+import functools
+import sys
+
+import numpy as np
+
+import synthetic
+from oracle import codecs, quant, reference, tolerance
+
+FMT_ACT = {"int4": "f16", "fp8": "bf16", "fp4": "bf16"}
+SIGMA = {"int4": 0.02, "fp8": 0.05, "fp4": 0.02}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_weights(fmt, N, K, G, key):
+    """Oracle quantization of seeded weights: canonical bytes, scales, alpha, dequant [N,K]."""
+    w = synthetic.weights(N, K, SIGMA[fmt], key)
+    if fmt == "int4":
+        codes, sbits = quant.quantize_int4(w, G)
+        return quant.pack_nibbles(codes), sbits, 1.0, reference.dequant_int4(codes, sbits, G)
+    if fmt == "fp8":
+        codes, alpha = quant.quantize_fp8(w)
+        return codes, None, alpha, reference.dequant_fp8(codes)
+    codes, sf, alpha = quant.quantize_fp4(w)
+    return quant.pack_nibbles(codes), sf, alpha, reference.dequant_fp4(codes, sf)
+
+
+def a_values(A16):
+    """fp64 values of a 16-bit torch CPU tensor (exact)."""
+    import torch
+    return A16.to(torch.float64).numpy()
+
+
+class Prepared:
+    """Device-resident packed weights for one (format, N, K, G)."""
+
+    def __init__(self, q, fmt, N, K, G, key, alpha_override=None):
+        import torch
+        self.fmt, self.N, self.K, self.G = fmt, N, K, G
+        canon, scales, alpha, self.wdq = oracle_weights(fmt, N, K, G, key)
+        self.alpha = alpha if alpha_override is None else alpha_override
+        p = q.problem(1, N, K, fmt, group_size=G if fmt == "int4" else None)
+        wpk, spk = q.pack(p, canon, scales)
+        self.w = torch.from_numpy(wpk).cuda()
+        self.s = None if spk is None else torch.from_numpy(spk).cuda()
+        self.alpha_t = torch.tensor([self.alpha], dtype=torch.float32, device="cuda")
+
+
+def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=None):
+    """Run through the C ABI; returns (out as numpy float64 or 16-bit bits, the workspace)."""
+    import torch
+    M, K = A16.shape
+    p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt == "int4" else None,
+                  out_dtype=out_dtype, kernel_hint=kernel_hint, split_k_hint=split_k_hint)
+    tdt = {q.DT_F32: torch.float32, q.DT_F16: torch.float16, q.DT_BF16: torch.bfloat16}[out_dtype]
+    out = torch.full((M, prep.N), float("nan"), dtype=tdt, device="cuda")
+    A = A16.cuda()
+    if workspace is None:
+        workspace = q.alloc_workspace(p)
+    q.run(p, A, prep.w, prep.s, None if prep.fmt == "int4" else prep.alpha_t, out, workspace)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    if out_dtype == q.DT_F32:
+        return o.numpy().astype(np.float64), workspace
+    return o.view(torch.int16).numpy().view(np.uint16), workspace
+
+
+def ref_rows(prep, A16, rows):
+    return reference.gemm_fp64_rows(a_values(A16), prep.wdq, rows, prep.alpha)
+
+
+def out16_kind(fmt):
+    return "f16" if fmt == "int4" else "bf16"
+
+
+def out16_dtype(q, fmt):
+    return q.DT_F16 if fmt == "int4" else q.DT_BF16
+
+
+def out16_values(bits, fmt):
+    return codecs.f16_from_bits(bits) if fmt == "int4" else codecs.bf16_from_bits(bits)
+
+
+def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0):
+    """E1/E2 on the fp32 output, E2 on the 16-bit output, E3 between them."""
+    M = A16.shape[0]
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    y32, ws = run_gpu(q, prep, A16, q.DT_F32, kernel_hint, split_k_hint)
+    r = ref_rows(prep, A16, rows)
+    st = tolerance.check_e1_e2(y32[rows], r)
+    y16, _ = run_gpu(q, prep, A16, out16_dtype(q, prep.fmt), kernel_hint, split_k_hint, ws)
+    tolerance.check_e3(y16, y32.astype(np.float32), out16_kind(prep.fmt))
+    tolerance.check_e2(out16_values(y16[rows], prep.fmt), r)
+    return st, y32

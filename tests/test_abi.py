@@ -1,0 +1,125 @@
+"""C-ABI contract on the CPU: exported symbols, status strings, validation errors that
+return before anything is enqueued, workspace sizing.  No kernel is launched here."""
+import os
+import re
+
+import pytest
+
+import weight_only_quantized_qgemm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(qgemm_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) >= {"qgemm_pack", "qgemm_run", "qgemm_workspace_bytes", "qgemm_quantize",
+                          "qgemm_status_string", "qgemm_last_error", "qgemm_version"}
+    for n in names:
+        assert hasattr(q.lib, n), n
+
+
+def test_status_strings_and_version():
+    assert q.status_string(q.OK) == "QGEMM_OK"
+    assert q.status_string(q.ERR_MISALIGNED) == "QGEMM_ERR_MISALIGNED"
+    assert q.status_string(99) == "QGEMM_ERR_UNKNOWN_STATUS"
+    assert q.version() >= 100
+
+
+BAD = [
+    (dict(M=0, N=256, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "M must be"),
+    (dict(M=1, N=250, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "N must be"),
+    (dict(M=1, N=256, K=500, fmt="int4"), q.ERR_INVALID_ARGUMENT, "K must be"),
+    (dict(M=1, N=256, K=640, fmt="int4", group_size=256), q.ERR_INVALID_ARGUMENT, "multiple of group_size"),
+    (dict(M=1, N=256, K=512, fmt="int4", group_size=48), q.ERR_UNSUPPORTED, "group_size"),
+    (dict(M=1, N=256, K=512, fmt="int4", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "INT4 weights need"),
+    (dict(M=1, N=256, K=512, fmt="fp8", out_dtype=q.DT_F16), q.ERR_UNSUPPORTED, "FP8_E4M3 weights need"),
+    (dict(M=1, N=256, K=512, fmt="fp8", group_size=128), q.ERR_INVALID_ARGUMENT, "group_size 0"),
+    (dict(M=1, N=256, K=512, fmt="fp4", group_size=32), q.ERR_INVALID_ARGUMENT, "group_size 16"),
+    (dict(M=17, N=256, K=512, fmt="int4", kernel_hint=q.KERNEL_DECODE), q.ERR_INVALID_ARGUMENT, "DECODE needs"),
+    (dict(M=1, N=256, K=512, fmt="int4", kernel_hint=7), q.ERR_INVALID_ARGUMENT, "kernel_hint"),
+    (dict(M=1, N=256, K=512, fmt="int4", split_k_hint=5), q.ERR_INVALID_ARGUMENT, "split_k_hint"),
+    (dict(M=1, N=256, K=512, fmt="int4", split_k_hint=-1), q.ERR_INVALID_ARGUMENT, "split_k_hint"),
+]
+
+
+@pytest.mark.parametrize("kw,status,text", BAD)
+def test_validation_errors(kw, status, text):
+    p = q.problem(**kw)
+    with pytest.raises(q.QgemmError) as ei:
+        q.workspace_bytes(p)
+    assert ei.value.status == status
+    assert text in ei.value.detail
+
+
+def test_bad_enums_and_reserved():
+    p = q.problem(1, 256, 512, "int4")
+    p.a_dtype = 17
+    assert q.run_raw(p, 16, 16, 16, None, 16, None, 0, None) == q.ERR_INVALID_ARGUMENT
+    p = q.problem(1, 256, 512, "int4")
+    p.reserved = 1
+    assert q.run_raw(p, 16, 16, 16, None, 16, None, 0, None) == q.ERR_INVALID_ARGUMENT
+    p = q.problem(1, 256, 512, "int4")
+    p.w_dtype = q.DT_F16
+    assert q.run_raw(p, 16, 16, 16, None, 16, None, 0, None) == q.ERR_UNSUPPORTED
+
+
+def _valid_run_status(p, A=0x1000, W=0x2000, S=0x3000, alpha=0x4000, out=0x5000, ws=None, wsb=0):
+    return q.run_raw(p, A, W, S, alpha, out, ws, wsb, None)
+
+
+def test_null_and_misaligned_pointers_fail_before_launch():
+    p = q.problem(1, 256, 512, "int4")
+    assert _valid_run_status(p, A=None) == q.ERR_INVALID_ARGUMENT
+    assert _valid_run_status(p, S=None) == q.ERR_INVALID_ARGUMENT
+    assert _valid_run_status(p, A=0x1008) == q.ERR_MISALIGNED
+    assert "A must be 16-byte aligned" in q.last_error()
+    assert _valid_run_status(p, W=0x2004) == q.ERR_MISALIGNED
+    assert _valid_run_status(p, out=0x5002) == q.ERR_MISALIGNED
+    f8 = q.problem(1, 256, 512, "fp8")
+    assert _valid_run_status(f8, alpha=None) == q.ERR_INVALID_ARGUMENT
+    assert _valid_run_status(f8, alpha=0x4002) == q.ERR_MISALIGNED     # 2 mod 4
+    f4 = q.problem(1, 256, 512, "fp4")
+    assert _valid_run_status(f4, S=0x3008) == q.ERR_MISALIGNED
+
+
+def test_scalar_alpha_needs_only_4_byte_alignment():
+    # alpha at addr % 16 == 4 passes the alignment check: the call then fails only on the
+    # deliberately missing workspace (a check that also precedes any launch)
+    p = q.problem(16, 256, 4096, "fp8")
+    need = q.workspace_bytes(p)
+    assert need > 0
+    st = _valid_run_status(p, alpha=0x4004, ws=None, wsb=0)
+    assert st == q.ERR_WORKSPACE_TOO_SMALL, q.last_error()
+
+
+def test_workspace_too_small_and_misaligned():
+    p = q.problem(16, 256, 4096, "int4")
+    need = q.workspace_bytes(p)
+    assert need > 0
+    assert _valid_run_status(p, ws=0x100000, wsb=need - 1) == q.ERR_WORKSPACE_TOO_SMALL
+    assert _valid_run_status(p, ws=0x100010, wsb=need) == q.ERR_MISALIGNED
+
+
+def test_workspace_sizes_do_not_depend_on_out_dtype():
+    for fmt, o in (("int4", q.DT_F32), ("fp8", q.DT_F32), ("fp4", q.DT_F32)):
+        for M in (1, 16, 128, 4096):
+            a = q.workspace_bytes(q.problem(M, 8192, 8192, fmt))
+            b = q.workspace_bytes(q.problem(M, 8192, 8192, fmt, out_dtype=o))
+            assert a == b
+
+
+def test_pack_size_query():
+    assert q.packed_sizes(q.problem(1, 256, 512, "int4")) == (256 * 256, 256 * 4 * 2)
+    assert q.packed_sizes(q.problem(1, 256, 512, "int4", group_size=32)) == (256 * 256, 256 * 16 * 2)
+    assert q.packed_sizes(q.problem(1, 256, 512, "fp8")) == (256 * 512, 0)
+    assert q.packed_sizes(q.problem(1, 256, 512, "fp4")) == (256 * 256, 256 * 32)

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: dequantized weights bit-exact (identity activations); GEMM outputs within
+E1 <= 1e-3 and E2 (|y - r| <= max(5e-3 |r|, 2e-2)) of the fp64 oracle, 16-bit outputs
+bitwise equal to the RNE cast of the fp32 output (E3), runs bitwise deterministic."""
+import numpy as np
+import pytest
+
+import synthetic
+from gpu_cases import (Prepared, check_against_oracle, oracle_weights, out16_dtype, out16_kind,
+                       run_gpu, say)
+from oracle import codecs, reference, tolerance
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_quantized_qgemm_amd as lib
+    return lib
+
+
+def _act(fmt, M, K, key):
+    return synthetic.activations(M, K, "f16" if fmt == "int4" else "bf16", key)
+
+
+def _identity_rows(fmt, rows, K):
+    import torch as T
+    dt = T.float16 if fmt == "int4" else T.bfloat16
+    A = T.zeros((len(rows), K), dtype=dt)
+    for i, k in enumerate(rows):
+        A[i, k] = 1.0
+    return A
+
+
+def _dequant_16bit_values(fmt, prep):
+    """The 16-bit operand the method feeds the MFMA, [N, K] float64."""
+    canon, scales, _, wdq = oracle_weights(fmt, prep.N, prep.K, prep.G, (7, prep.N, prep.K))
+    if fmt == "int4":
+        from oracle import quant
+        return reference.dequant_int4_f16(quant.unpack_nibbles(canon), scales, prep.G)
+    return wdq.astype(np.float64)        # exact in bf16 for FP8 (alpha not applied) and FP4
+
+
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 64), ("int4", 128), ("int4", 256),
+                                   ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("hint", [1, 2])
+def test_identity_activations_give_dequantized_weights_bit_exact(q, fmt, G, hint):
+    N, K = 48, 512
+    say(f"case identity fmt={fmt} G={G} hint={hint}")
+    prep = Prepared(q, fmt, N, K, G or 0, (7, N, K), alpha_override=1.0)
+    want = _dequant_16bit_values(fmt, prep)              # [N, K]
+    step = 16 if hint == 1 else K
+    for k0 in range(0, K, step):
+        rows = list(range(k0, k0 + step))
+        A = _identity_rows(fmt, rows, K)
+        y32, _ = run_gpu(q, prep, A, q.DT_F32, kernel_hint=hint)
+        assert np.array_equal(y32, want[:, rows].T), f"fp32 dequant mismatch rows {k0}.."
+        y16, _ = run_gpu(q, prep, A, out16_dtype(q, fmt), kernel_hint=hint)
+        kind = out16_kind(fmt)
+        want16 = codecs.f16_bits(want[:, rows].T) if kind == "f16" else codecs.bf16_bits(want[:, rows].T)
+        assert np.array_equal(y16, want16)
+
+
+CONFIGS = [
+    # workload name, shape index, (M, N, K), G, sampled rows (None = all)
+    ("int4_tiny", 0, (1, 256, 512), 128, None),
+    ("int4_decode", 0, (1, 4096, 4096), 128, None),
+    ("int4_decode", 1, (16, 4096, 4096), 128, None),
+    ("int4_decode", 2, (1, 11008, 4096), 128, None),
+    ("int4_decode", 3, (16, 11008, 4096), 128, None),
+    ("int4_prefill", 0, (4096, 4096, 4096), 32, 96),
+    ("int4_prefill", 0, (4096, 4096, 4096), 64, 96),
+    ("int4_prefill", 0, (4096, 4096, 4096), 128, 96),
+    ("int4_prefill", 0, (4096, 4096, 4096), 256, 96),
+    ("fp8", 0, (1, 10240, 5120), None, None),
+    ("fp8", 1, (16, 10240, 5120), None, None),
+    ("fp8", 2, (8192, 10240, 5120), None, 64),
+    ("fp8", 3, (32768, 3200, 5120), None, 64),
+    ("fp8", 4, (16384, 12800, 5120), None, 64),
+    ("fp4", 0, (1, 8192, 8192), None, None),
+    ("fp4", 1, (128, 8192, 8192), None, None),
+    ("fp4", 2, (8192, 8192, 8192), None, 64),
+]
+
+
+@pytest.mark.parametrize("name,si,shape,G,nrows", CONFIGS,
+                         ids=[f"{c[0]}-{c[2][0]}x{c[2][1]}x{c[2][2]}-G{c[3]}" for c in CONFIGS])
+def test_workload_parity(q, name, si, shape, G, nrows):
+    M, N, K = shape
+    fmt = synthetic.WORKLOADS[name]["fmt"]
+    wi = synthetic.WORKLOAD_INDEX[name]
+    say(f"case workload {name} M={M} N={N} K={K} G={G}")
+    prep = Prepared(q, fmt, N, K, G or 0, (wi, si))
+    A = _act(fmt, M, K, (wi, si))
+    rows = None
+    if nrows:
+        g = np.random.default_rng([wi, si, 2])
+        rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, nrows, replace=False)]))
+    st, _ = check_against_oracle(q, prep, A, rows)
+    say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f} max_abs={st['max_abs']:.3e}")
+
+
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int4", 256), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 33, 127, 128, 129])
+def test_m_sweep_ragged(q, fmt, G, M):
+    N, K = 272, 768          # N: 17 column blocks (ragged against 128-wide tiles); K: 6 k blocks
+    say(f"case m-sweep fmt={fmt} G={G} M={M}")
+    prep = Prepared(q, fmt, N, K, G or 0, (50, N, K))
+    A = _act(fmt, M, K, (50, M))
+    check_against_oracle(q, prep, A)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+@pytest.mark.parametrize("hint,split", [(1, 1), (1, 2), (1, 3), (1, 7), (2, 1), (2, 2), (2, 5)])
+def test_split_k_and_kernel_hints(q, fmt, hint, split):
+    M, N, K = 16, 256, 1792    # 14 k blocks
+    say(f"case hints fmt={fmt} kernel={hint} split={split}")
+    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (51, N, K))
+    A = _act(fmt, M, K, (51, M))
+    check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+@pytest.mark.parametrize("M", [16, 256])
+def test_deterministic_and_counters_reset(q, fmt, M):
+    N, K = 512, 4096
+    say(f"case determinism fmt={fmt} M={M}")
+    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (52, N, K))
+    A = _act(fmt, M, K, (52, M))
+    outs = []
+    ws = None
+    for _ in range(3):
+        y, ws = run_gpu(q, prep, A, q.DT_F32, workspace=ws)
+        outs.append(y)
+        if ws is not None:
+            p = q.problem(M, N, K, fmt, group_size=128 if fmt == "int4" else None)
+            assert q.workspace_bytes(p) > 0
+            head = ws[:256].cpu().numpy()
+            assert not head.any(), "split-K tickets must return to zero"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+def test_minimum_shape_and_zero_weights(q, fmt):
+    import torch as T
+    N, K = 16, 128
+    say(f"case minimum fmt={fmt}")
+    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (53, N, K))
+    for M in (1, 16, 17):
+        check_against_oracle(q, prep, _act(fmt, M, K, (53, M)))
+    # all-zero packed weights give exact zeros
+    prep.w.zero_()
+    if prep.s is not None:
+        prep.s.zero_()
+    y, _ = run_gpu(q, prep, _act(fmt, 5, K, (53, 5)), q.DT_F32)
+    assert not y.any()
+
+
+def test_int4_closed_form_equal_nibbles_unit_scales(q):
+    import torch as T
+    N, K, M = 64, 1024, 8
+    say("case closed-form int4")
+    p = q.problem(M, N, K, "int4")
+    A16 = _act("int4", M, K, (54, 0))
+    rowsum = A16.to(T.float64).sum(dim=1).numpy()
+    for c in (0, 5, 8, 15):
+        codes = np.full((N, K // 2), c | (c << 4), np.uint8)
+        scales = np.full((K // 128, N), 0x3C00, np.uint16)        # 1.0
+        wpk, spk = q.pack(p, codes, scales)
+        out = T.empty((M, N), dtype=T.float32, device="cuda")
+        q.run(p, A16.cuda(), T.from_numpy(wpk).cuda(), T.from_numpy(spk).cuda(), None, out,
+              q.alloc_workspace(p))
+        T.cuda.synchronize()
+        y = out.cpu().numpy().astype(np.float64)
+        want = np.repeat(((c - 8) * rowsum)[:, None], N, axis=1)
+        if c == 8:
+            assert not y.any()
+        else:
+            tolerance.check_e1_e2(y, want)

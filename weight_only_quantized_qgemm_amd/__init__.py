@@ -1,0 +1,189 @@
+"""Python binding of the qgemm C ABI (include/qgemm.h): argument marshalling only.
+
+Every step of the GEMM runs in the HIP library ``libqgemm.so`` built next to this file;
+torch serves only for device memory and the current stream.  Importing this package
+fails loudly when the library has not been built.
+
+Quick use::
+
+    import weight_only_quantized_qgemm_amd as q
+    p = q.problem(M, N, K, "int4", group_size=128)
+    codes, scales, alpha = q.quantize(p, w_nk)          # host, numpy
+    wpk, spk = q.pack(p, codes, scales)                  # host, numpy
+    ... upload with torch, then q.run(p, A, wpk_dev, spk_dev, alpha_dev, out, ws)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m weight_only_quantized_qgemm_amd._build` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ----------------------------------------------------------------------------- enums
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(6)
+DT_F16, DT_BF16, DT_F32, DT_INT4, DT_FP8_E4M3, DT_FP4_E2M1 = range(6)
+SCALE_GROUP_F16, SCALE_TENSOR_F32, SCALE_BLOCK16_E4M3 = range(3)
+KERNEL_AUTO, KERNEL_DECODE, KERNEL_PREFILL = range(3)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
+                ("kernel_hint", ctypes.c_int32), ("split_k_hint", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(Problem) == 56
+
+_P = ctypes.POINTER(Problem)
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_lib.qgemm_quantize.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_float)]
+_lib.qgemm_pack.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp, ctypes.POINTER(_sz)]
+_lib.qgemm_workspace_bytes.argtypes = [_P, ctypes.POINTER(_sz)]
+_lib.qgemm_run.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.qgemm_status_string.argtypes = [ctypes.c_int]
+_lib.qgemm_status_string.restype = ctypes.c_char_p
+_lib.qgemm_last_error.argtypes = []
+_lib.qgemm_last_error.restype = ctypes.c_char_p
+_lib.qgemm_version.restype = ctypes.c_int32
+for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+lib = _lib
+
+
+class QgemmError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{_lib.qgemm_status_string(status).decode()}: {detail}")
+
+
+def _check(status):
+    if status != OK:
+        raise QgemmError(status, _lib.qgemm_last_error().decode())
+
+
+# ----------------------------------------------------------------------------- problems
+_FORMATS = {
+    "int4": (DT_F16, DT_INT4, SCALE_GROUP_F16, DT_F16),
+    "fp8": (DT_BF16, DT_FP8_E4M3, SCALE_TENSOR_F32, DT_BF16),
+    "fp4": (DT_BF16, DT_FP4_E2M1, SCALE_BLOCK16_E4M3, DT_BF16),
+}
+
+
+def problem(M, N, K, fmt, group_size=None, out_dtype=None, kernel_hint=KERNEL_AUTO, split_k_hint=0):
+    """Problem descriptor for one of the formats 'int4', 'fp8', 'fp4'."""
+    a, w, sl, o = _FORMATS[fmt]
+    if group_size is None:
+        group_size = {"int4": 128, "fp8": 0, "fp4": 16}[fmt]
+    if out_dtype is not None:
+        o = out_dtype
+    return Problem(M, N, K, a, w, o, group_size, sl, kernel_hint, split_k_hint, 0)
+
+
+def fmt_of(p):
+    return {DT_INT4: "int4", DT_FP8_E4M3: "fp8", DT_FP4_E2M1: "fp4"}[p.w_dtype]
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()          # torch tensor
+
+
+# ----------------------------------------------------------------------------- host calls
+def quantize(p, w_nk):
+    """fp32 [N, K] weights -> (canonical codes uint8, canonical scales or None, alpha)."""
+    w = np.ascontiguousarray(w_nk, dtype=np.float32)
+    N, K = int(p.N), int(p.K)
+    assert w.shape == (N, K)
+    f = fmt_of(p)
+    codes = np.empty((N, K // 2) if f != "fp8" else (N, K), np.uint8)
+    scales = None
+    if f == "int4":
+        scales = np.empty((K // p.group_size, N), np.uint16)
+    elif f == "fp4":
+        scales = np.empty((N, K // 16), np.uint8)
+    alpha = ctypes.c_float(0.0)
+    _check(_lib.qgemm_quantize(ctypes.byref(p), w.ctypes.data, codes.ctypes.data,
+                               None if scales is None else scales.ctypes.data, ctypes.byref(alpha)))
+    return codes, scales, float(alpha.value)
+
+
+def packed_sizes(p):
+    wb, sb = _sz(0), _sz(0)
+    _check(_lib.qgemm_pack(ctypes.byref(p), None, None, None, ctypes.byref(wb), None, ctypes.byref(sb)))
+    return wb.value, sb.value
+
+
+def pack(p, codes, scales):
+    """Canonical codes / scales (host) -> packed device-layout bytes (host numpy uint8)."""
+    wsz, ssz = packed_sizes(p)
+    codes = np.ascontiguousarray(codes)
+    wpk = np.empty(wsz, np.uint8)
+    spk = np.empty(max(ssz, 0), np.uint8)
+    if scales is not None:
+        scales = np.ascontiguousarray(scales)
+    wb, sb = _sz(wsz), _sz(ssz)
+    _check(_lib.qgemm_pack(ctypes.byref(p), codes.ctypes.data,
+                           None if scales is None else scales.ctypes.data,
+                           wpk.ctypes.data, ctypes.byref(wb),
+                           spk.ctypes.data if ssz else None, ctypes.byref(sb)))
+    return wpk, (spk if ssz else None)
+
+
+def workspace_bytes(p):
+    n = _sz(0)
+    _check(_lib.qgemm_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+# ----------------------------------------------------------------------------- device calls
+def alloc_workspace(p, device="cuda"):
+    """A zero-filled workspace of the size qgemm_workspace_bytes reports (or None)."""
+    import torch
+    n = workspace_bytes(p)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def run(p, A, w_packed, s_packed, alpha, out, workspace=None, stream=None):
+    """Enqueue out = A . dequant(W) (* alpha) on `stream` (default: torch's current stream)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.qgemm_run(ctypes.byref(p), _ptr(A), _ptr(w_packed), _ptr(s_packed), _ptr(alpha),
+                          _ptr(out), _ptr(workspace), ws_bytes, stream))
+
+
+def run_raw(p, A, w_packed, s_packed, alpha, out, workspace, workspace_bytes_, stream):
+    """qgemm_run on raw integer addresses; returns the status (no exception)."""
+    return _lib.qgemm_run(ctypes.byref(p), A, w_packed, s_packed, alpha, out, workspace,
+                          workspace_bytes_, stream)
+
+
+def last_error():
+    return _lib.qgemm_last_error().decode()
+
+
+def status_string(st):
+    return _lib.qgemm_status_string(st).decode()
+
+
+def version():
+    return int(_lib.qgemm_version())

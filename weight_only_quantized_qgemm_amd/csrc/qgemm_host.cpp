@@ -1,0 +1,444 @@
+// Host side of the library: status text, validation, launch planning, the offline
+// quantizer and the offline packer.  Nothing in this file touches the GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qgemm_internal.h"
+
+namespace qgemm {
+
+static_assert(sizeof(qgemm_problem_t) == 56, "qgemm_problem_t layout is part of the ABI");
+
+static thread_local std::string t_last_error;
+
+qgemm_status_t fail(qgemm_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return st;
+}
+
+void clear_error() { t_last_error.clear(); }
+
+static const char* dtype_name(int d) {
+  switch (d) {
+    case QGEMM_DT_F16: return "F16";
+    case QGEMM_DT_BF16: return "BF16";
+    case QGEMM_DT_F32: return "F32";
+    case QGEMM_DT_INT4: return "INT4";
+    case QGEMM_DT_FP8_E4M3: return "FP8_E4M3";
+    case QGEMM_DT_FP4_E2M1: return "FP4_E2M1";
+    default: return "?";
+  }
+}
+
+Format format_of(const qgemm_problem_t* p) {
+  return p->w_dtype == QGEMM_DT_INT4 ? FMT_INT4 : p->w_dtype == QGEMM_DT_FP8_E4M3 ? FMT_FP8 : FMT_FP4;
+}
+
+// Each of M, N, K is limited to 2^24; the kernels address A, W, out and the workspace with
+// 64-bit offsets, and grids are checked against the 2^31 - 1 workgroup limit when planned.
+static const int64_t kMaxDim = int64_t(1) << 24;
+
+qgemm_status_t validate_problem(const qgemm_problem_t* p) {
+  if (!p) return fail(QGEMM_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->reserved != 0) return fail(QGEMM_ERR_INVALID_ARGUMENT, "problem.reserved must be 0, got %d", p->reserved);
+  for (int d : {p->a_dtype, p->w_dtype, p->out_dtype})
+    if (d < QGEMM_DT_F16 || d > QGEMM_DT_FP4_E2M1)
+      return fail(QGEMM_ERR_INVALID_ARGUMENT, "dtype value %d is not a qgemm_dtype_t", d);
+  if (p->scale_layout < QGEMM_SCALE_GROUP_F16 || p->scale_layout > QGEMM_SCALE_BLOCK16_E4M3)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "scale_layout %d is not a qgemm_scale_layout_t", p->scale_layout);
+  if (p->M < 1 || p->M > kMaxDim)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "M must be in [1, %lld], got %lld", (long long)kMaxDim, (long long)p->M);
+  if (p->N < 16 || p->N % 16 || p->N > kMaxDim)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "N must be a positive multiple of 16 (<= %lld), got %lld",
+                (long long)kMaxDim, (long long)p->N);
+  if (p->K < 128 || p->K % 128 || p->K > kMaxDim)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "K must be a positive multiple of 128 (<= %lld), got %lld",
+                (long long)kMaxDim, (long long)p->K);
+
+  const int a = p->a_dtype, w = p->w_dtype, o = p->out_dtype, sl = p->scale_layout, g = p->group_size;
+  if (w == QGEMM_DT_INT4) {
+    if (a != QGEMM_DT_F16 || sl != QGEMM_SCALE_GROUP_F16 || (o != QGEMM_DT_F16 && o != QGEMM_DT_F32))
+      return fail(QGEMM_ERR_UNSUPPORTED, "INT4 weights need a_dtype F16, scale_layout GROUP_F16 and out_dtype F16 or F32; "
+                  "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
+    if (g != 32 && g != 64 && g != 128 && g != 256)
+      return fail(QGEMM_ERR_UNSUPPORTED, "INT4 group_size must be 32, 64, 128 or 256, got %d", g);
+    if (p->K % g) return fail(QGEMM_ERR_INVALID_ARGUMENT, "K (%lld) must be a multiple of group_size (%d)", (long long)p->K, g);
+  } else if (w == QGEMM_DT_FP8_E4M3) {
+    if (a != QGEMM_DT_BF16 || sl != QGEMM_SCALE_TENSOR_F32 || (o != QGEMM_DT_BF16 && o != QGEMM_DT_F32))
+      return fail(QGEMM_ERR_UNSUPPORTED, "FP8_E4M3 weights need a_dtype BF16, scale_layout TENSOR_F32 and out_dtype BF16 or F32; "
+                  "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
+    if (g != 0) return fail(QGEMM_ERR_INVALID_ARGUMENT, "FP8_E4M3 takes group_size 0 (per-tensor scale), got %d", g);
+  } else if (w == QGEMM_DT_FP4_E2M1) {
+    if (a != QGEMM_DT_BF16 || sl != QGEMM_SCALE_BLOCK16_E4M3 || (o != QGEMM_DT_BF16 && o != QGEMM_DT_F32))
+      return fail(QGEMM_ERR_UNSUPPORTED, "FP4_E2M1 weights need a_dtype BF16, scale_layout BLOCK16_E4M3 and out_dtype BF16 or F32; "
+                  "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
+    if (g != 16) return fail(QGEMM_ERR_INVALID_ARGUMENT, "FP4_E2M1 takes group_size 16 (one e4m3 scale per 16 K), got %d", g);
+  } else {
+    return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, FP8_E4M3, FP4_E2M1)", dtype_name(w));
+  }
+
+  if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint must be 0, 1 or 2, got %d", p->kernel_hint);
+  if (p->kernel_hint == QGEMM_KERNEL_DECODE && p->M > 16)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint DECODE needs M <= 16, got M=%lld", (long long)p->M);
+  if (p->split_k_hint < 0 || p->split_k_hint > 64)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint must be in [0, 64], got %d", p->split_k_hint);
+  if (p->split_k_hint > p->K / 128)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d exceeds the %lld 128-wide K blocks",
+                p->split_k_hint, (long long)(p->K / 128));
+  return QGEMM_OK;
+}
+
+// ----------------------------------------------------------------------------- planning
+static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// The chip has 256 compute units; grids are sized against that.
+static const int kCUs = 256;
+
+static void finish_split(Plan* pl, int kblocks, int requested) {
+  int s = requested > 0 ? requested : pl->splits;
+  if (s < 1) s = 1;
+  if (s > kblocks) s = kblocks;
+  pl->kb_per_split = ceil_div(kblocks, s);
+  pl->splits = ceil_div(kblocks, pl->kb_per_split);   // no empty split
+}
+
+qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
+  std::memset(pl, 0, sizeof(*pl));
+  pl->fmt = format_of(p);
+  const int kblocks = (int)(p->K / 128);
+  const int nblocks = (int)(p->N / 16);
+  bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
+  if (decode) {
+    pl->kind = KIND_DECODE;
+    // Column blocks per workgroup: more columns per workgroup means fewer re-reads of A
+    // (all of A is read by every workgroup of a K slice); keep >= ~2 workgroups per CU.
+    pl->cb = 1;
+    if (p->M > 1) {
+      pl->cb = 4;
+      while (pl->cb > 1 && nblocks % pl->cb) pl->cb /= 2;
+    }
+    const int groups = ceil_div(nblocks, pl->cb);
+    // K splits so that the grid fills the chip at least twice.
+    int s = 1;
+    while (groups * s < 2 * kCUs && s * 2 <= kblocks / 2) s *= 2;
+    pl->splits = s;
+    finish_split(pl, kblocks, p->split_k_hint);
+    pl->grid_x = (unsigned)groups;
+    pl->grid_y = (unsigned)pl->splits;
+    pl->tiles = groups;
+    pl->tile_elems = pl->cb * 256;
+  } else {
+    pl->kind = KIND_PREFILL;
+    pl->bm = 128;
+    pl->bn = 128;
+    const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
+    int s = 1;
+    while ((int64_t)mt * nt * s < kCUs && s * 2 <= kblocks / 4) s *= 2;
+    pl->splits = s;
+    finish_split(pl, kblocks, p->split_k_hint);
+    if (mt * nt > 0x7fffffffLL) return fail(QGEMM_ERR_UNSUPPORTED, "too many output tiles (%lld)", (long long)(mt * nt));
+    pl->grid_x = (unsigned)(mt * nt);
+    pl->grid_y = (unsigned)pl->splits;
+    pl->tiles = (int)(mt * nt);
+    pl->tile_elems = pl->bm * pl->bn;
+  }
+  if ((int64_t)pl->grid_x * pl->grid_y > 0x7fffffffLL)
+    return fail(QGEMM_ERR_UNSUPPORTED, "problem needs %lld workgroups, more than one launch allows",
+                (long long)pl->grid_x * pl->grid_y);
+  if (pl->splits > 1) {
+    pl->counters_bytes = ((size_t)pl->tiles * 4 + 255) / 256 * 256;
+    pl->ws_bytes = pl->counters_bytes + (size_t)pl->tiles * pl->splits * pl->tile_elems * 4;
+  }
+  return QGEMM_OK;
+}
+
+// ----------------------------------------------------------------------------- rounding
+// Round-to-nearest-even of a double onto a binary format with `mant` explicit mantissa
+// bits and smallest normal exponent `emin` (no overflow handling; callers clamp).
+static double round_format(double x, int mant, int emin) {
+  if (x == 0.0 || !std::isfinite(x)) return x;
+  int e2;
+  std::frexp(x, &e2);             // |x| = f * 2^e2, f in [0.5, 1)
+  int e = e2 - 1;
+  if (e < emin) e = emin;
+  double q = std::ldexp(1.0, e - mant);
+  return std::nearbyint(x / q) * q;   // default rounding mode is to-nearest-even
+}
+
+static uint16_t f16_bits_of(double v) {   // v already an fp16 value (finite)
+  if (v == 0.0) return std::signbit(v) ? 0x8000 : 0;
+  uint16_t s = std::signbit(v) ? 0x8000 : 0;
+  double a = std::fabs(v);
+  int e2;
+  double f = std::frexp(a, &e2);        // a = f 2^e2
+  int e = e2 - 1;                        // a = (2f) 2^e
+  if (e < -14) {                         // subnormal: a = m 2^-24
+    return (uint16_t)(s | (uint16_t)std::llround(a * 16777216.0));
+  }
+  int m = (int)std::llround((2.0 * f - 1.0) * 1024.0);
+  return (uint16_t)(s | ((e + 15) << 10) | m);
+}
+
+static uint8_t e4m3_code_of(double v) {   // v already an e4m3 value, |v| <= 448
+  if (v == 0.0) return 0;
+  uint8_t s = std::signbit(v) ? 0x80 : 0;
+  double a = std::fabs(v);
+  if (a < std::ldexp(1.0, -6)) return (uint8_t)(s | (uint8_t)std::llround(a * 512.0));
+  int e2;
+  double f = std::frexp(a, &e2);
+  int e = e2 - 1;
+  int m = (int)std::llround((2.0 * f - 1.0) * 8.0);
+  return (uint8_t)(s | ((e + 7) << 3) | m);
+}
+
+static double e4m3_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v = e == 0 ? std::ldexp(m / 8.0, -6) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+static uint8_t e2m1_code_of(double v) {   // v already an e2m1 value, |v| <= 6
+  static const double mags[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double a = std::fabs(v);
+  int idx = 0;
+  for (int i = 0; i < 8; ++i)
+    if (mags[i] == a) idx = i;
+  uint8_t s = (std::signbit(v) && a != 0.0) ? 8 : 0;
+  return (uint8_t)(s | idx);
+}
+
+static double clampd(double x, double lo, double hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace qgemm
+
+using namespace qgemm;
+
+// ============================================================================= C ABI
+extern "C" {
+
+const char* qgemm_status_string(qgemm_status_t st) {
+  switch (st) {
+    case QGEMM_OK: return "QGEMM_OK";
+    case QGEMM_ERR_INVALID_ARGUMENT: return "QGEMM_ERR_INVALID_ARGUMENT";
+    case QGEMM_ERR_UNSUPPORTED: return "QGEMM_ERR_UNSUPPORTED";
+    case QGEMM_ERR_MISALIGNED: return "QGEMM_ERR_MISALIGNED";
+    case QGEMM_ERR_WORKSPACE_TOO_SMALL: return "QGEMM_ERR_WORKSPACE_TOO_SMALL";
+    case QGEMM_ERR_HIP: return "QGEMM_ERR_HIP";
+    default: return "QGEMM_ERR_UNKNOWN_STATUS";
+  }
+}
+
+const char* qgemm_last_error(void) { return t_last_error.c_str(); }
+
+int32_t qgemm_version(void) { return 100; }
+
+qgemm_status_t qgemm_workspace_bytes(const qgemm_problem_t* p, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(QGEMM_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  qgemm_status_t st = validate_problem(p);
+  if (st != QGEMM_OK) return st;
+  Plan pl;
+  st = make_plan(p, &pl);
+  if (st != QGEMM_OK) return st;
+  *bytes = pl.ws_bytes;
+  return QGEMM_OK;
+}
+
+qgemm_status_t qgemm_quantize(const qgemm_problem_t* p, const float* w_nk, void* codes_canonical,
+                              void* scales_canonical, float* alpha_out) {
+  clear_error();
+  qgemm_status_t st = validate_problem(p);
+  if (st != QGEMM_OK) return st;
+  if (!w_nk || !codes_canonical) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk and codes_canonical must not be NULL");
+  const Format fmt = format_of(p);
+  if (fmt != FMT_FP8 && !scales_canonical)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical must not be NULL for INT4 / FP4");
+  if (fmt != FMT_INT4 && !alpha_out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha_out must not be NULL for FP8 / FP4");
+  const int64_t N = p->N, K = p->K;
+  uint8_t* codes = static_cast<uint8_t*>(codes_canonical);
+
+  if (fmt == FMT_INT4) {
+    const int G = p->group_size;
+    uint16_t* sc = static_cast<uint16_t*>(scales_canonical);   // [K/G][N]
+    std::vector<uint8_t> q(K);
+    for (int64_t n = 0; n < N; ++n) {
+      const float* row = w_nk + n * K;
+      for (int64_t g = 0; g < K / G; ++g) {
+        double amax = 0.0;
+        for (int i = 0; i < G; ++i) {
+          const double v = std::fabs((double)row[g * G + i]);
+          if (!std::isfinite(v))
+            return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk[%lld] is not finite", (long long)(n * K + g * G + i));
+          amax = v > amax ? v : amax;
+        }
+        double s = round_format(amax / 7.0, 10, -14);
+        if (!(s <= 65504.0))
+          return fail(QGEMM_ERR_INVALID_ARGUMENT, "column %lld group %lld: absmax %g is not finite or its scale overflows fp16",
+                      (long long)n, (long long)g, amax);
+        sc[g * N + n] = f16_bits_of(s);
+        for (int i = 0; i < G; ++i) {
+          double v = s == 0.0 ? 0.0 : clampd(std::nearbyint((double)row[g * G + i] / s), -8.0, 7.0);
+          q[g * G + i] = (uint8_t)((int)v + 8);
+        }
+      }
+      for (int64_t j = 0; j < K / 2; ++j) codes[n * (K / 2) + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+    }
+    if (alpha_out) *alpha_out = 1.0f;
+    return QGEMM_OK;
+  }
+
+  double amax = 0.0;
+  for (int64_t i = 0; i < N * K; ++i) {
+    const double v = std::fabs((double)w_nk[i]);
+    if (!std::isfinite(v)) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk[%lld] is not finite", (long long)i);
+    amax = v > amax ? v : amax;
+  }
+
+  if (fmt == FMT_FP8) {
+    const float alpha = (float)(amax / 448.0);
+    *alpha_out = alpha;
+    for (int64_t i = 0; i < N * K; ++i) {
+      if (alpha == 0.0f) { codes[i] = 0; continue; }
+      double x = clampd((double)w_nk[i] / (double)alpha, -448.0, 448.0);
+      codes[i] = e4m3_code_of(round_format(x, 3, -6));
+    }
+    return QGEMM_OK;
+  }
+
+  // FP4
+  const float alpha = (float)(amax / (6.0 * 448.0));
+  *alpha_out = alpha;
+  uint8_t* sf = static_cast<uint8_t*>(scales_canonical);   // [N][K/16]
+  std::vector<uint8_t> q(K);
+  for (int64_t n = 0; n < N; ++n) {
+    const float* row = w_nk + n * K;
+    for (int64_t b = 0; b < K / 16; ++b) {
+      uint8_t scode = 0;
+      if (alpha != 0.0f) {
+        double bmax = 0.0;
+        for (int i = 0; i < 16; ++i) bmax = std::fmax(bmax, std::fabs((double)row[b * 16 + i]));
+        double t = bmax / (6.0 * (double)alpha);
+        if (t > 448.0) t = 448.0;
+        scode = e4m3_code_of(round_format(t, 3, -6));
+      }
+      sf[n * (K / 16) + b] = scode;
+      const double den = e4m3_value(scode) * (double)alpha;
+      for (int i = 0; i < 16; ++i) {
+        if (den == 0.0) { q[b * 16 + i] = 0; continue; }
+        double x = clampd((double)row[b * 16 + i] / den, -6.0, 6.0);
+        q[b * 16 + i] = e2m1_code_of(round_format(x, 1, 0));
+      }
+    }
+    for (int64_t j = 0; j < K / 2; ++j) codes[n * (K / 2) + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+  }
+  return QGEMM_OK;
+}
+
+qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, const void* scales_canonical,
+                          void* w_packed, size_t* w_packed_bytes, void* s_packed, size_t* s_packed_bytes) {
+  clear_error();
+  qgemm_status_t st = validate_problem(p);
+  if (st != QGEMM_OK) return st;
+  if (!w_packed_bytes || !s_packed_bytes)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed_bytes and s_packed_bytes must not be NULL");
+  const Format fmt = format_of(p);
+  const int64_t N = p->N, K = p->K, NB = N / 16;
+  const size_t need_w = fmt == FMT_FP8 ? (size_t)(N * K) : (size_t)(N * K / 2);
+  size_t need_s = 0;
+  if (fmt == FMT_INT4) need_s = (size_t)(N * (K / p->group_size)) * 2;
+  if (fmt == FMT_FP4) need_s = (size_t)(N * (K / 16));
+  const size_t cap_w = *w_packed_bytes, cap_s = *s_packed_bytes;
+  *w_packed_bytes = need_w;
+  *s_packed_bytes = need_s;
+  if (!w_packed && !s_packed) return QGEMM_OK;     // size query
+  if (w_packed) {
+    if (!w_canonical) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_canonical is NULL");
+    if (cap_w < need_w) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed capacity %zu < %zu bytes", cap_w, need_w);
+  }
+  if (s_packed && need_s) {
+    if (!scales_canonical) return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical is NULL");
+    if (cap_s < need_s) return fail(QGEMM_ERR_INVALID_ARGUMENT, "s_packed capacity %zu < %zu bytes", cap_s, need_s);
+  }
+
+  if (w_packed) {
+    const uint8_t* src = static_cast<const uint8_t*>(w_canonical);
+    uint8_t* dst = static_cast<uint8_t*>(w_packed);
+    if (fmt == FMT_FP8) {
+      // 1 KiB block = 16 columns x 64 k; lane l: column l & 15, k = 32t + 8(l >> 4) + j.
+      const int64_t KB = K / 64;
+      for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t kb = 0; kb < KB; ++kb) {
+          uint8_t* blk = dst + (nb * KB + kb) * 1024;
+          for (int lane = 0; lane < 64; ++lane) {
+            const uint8_t* col = src + (nb * 16 + (lane & 15)) * K + kb * 64 + 8 * (lane >> 4);
+            for (int t = 0; t < 2; ++t) std::memcpy(blk + 16 * lane + 8 * t, col + 32 * t, 8);
+          }
+        }
+    } else {
+      // 1 KiB block = 16 columns x 128 k; lane l owns 4 dwords, dword t holds the 8 nibbles
+      // of column l & 15 at k = 32t + 8(l >> 4) + J[slot].
+      static const int J_INT4[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+      static const int J_FP4[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+      const int* J = fmt == FMT_INT4 ? J_INT4 : J_FP4;
+      const int64_t KB = K / 128;
+      for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t kb = 0; kb < KB; ++kb) {
+          uint8_t* blk = dst + (nb * KB + kb) * 1024;
+          for (int lane = 0; lane < 64; ++lane) {
+            const uint8_t* col = src + (nb * 16 + (lane & 15)) * (K / 2);
+            for (int t = 0; t < 4; ++t) {
+              uint32_t word = 0;
+              const int64_t k0 = kb * 128 + 32 * t + 8 * (lane >> 4);
+              for (int slot = 0; slot < 8; ++slot) {
+                const int64_t k = k0 + J[slot];
+                const uint32_t nib = (col[k >> 1] >> (4 * (k & 1))) & 0xF;
+                word |= nib << (4 * slot);
+              }
+              std::memcpy(blk + 16 * lane + 4 * t, &word, 4);
+            }
+          }
+        }
+    }
+  }
+
+  if (s_packed && need_s) {
+    if (fmt == FMT_INT4) {
+      const int G = p->group_size;
+      const int span = G > 128 ? G : 128;
+      const int T = G < 128 ? 128 / G : 1;
+      const int64_t KS = K / span, NG = K / G;
+      const uint16_t* src = static_cast<const uint16_t*>(scales_canonical);   // [K/G][N]
+      uint16_t* dst = static_cast<uint16_t*>(s_packed);
+      for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t ks = 0; ks < KS; ++ks)
+          for (int c = 0; c < 16; ++c)
+            for (int t = 0; t < T; ++t) {
+              const int64_t g = ks * (span / G) + t;
+              if (g < NG) dst[((nb * KS + ks) * 16 + c) * T + t] = src[g * N + nb * 16 + c];
+            }
+    } else {
+      const int64_t KB = K / 128;
+      const uint8_t* src = static_cast<const uint8_t*>(scales_canonical);     // [N][K/16]
+      uint8_t* dst = static_cast<uint8_t*>(s_packed);
+      for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t kb = 0; kb < KB; ++kb)
+          for (int c = 0; c < 16; ++c)
+            for (int h = 0; h < 2; ++h)
+              for (int t = 0; t < 4; ++t)
+                dst[((nb * KB + kb) * 16 + c) * 8 + 4 * h + t] = src[(nb * 16 + c) * (K / 16) + 8 * kb + 2 * t + h];
+    }
+  }
+  return QGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/qgemm.h"
+
+namespace qgemm {
+
+enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
+enum Kind : int { KIND_DECODE = 1, KIND_PREFILL = 2 };
+
+// Records a detail message for qgemm_last_error() and returns `st`.
+qgemm_status_t fail(qgemm_status_t st, const char* fmt, ...);
+void clear_error();
+
+// Full validation of the descriptor (shapes, dtype combination, hints).
+qgemm_status_t validate_problem(const qgemm_problem_t* p);
+Format format_of(const qgemm_problem_t* p);
+
+// Launch plan, a pure function of the problem (never of out_dtype or of pointers).
+struct Plan {
+  Kind kind;
+  Format fmt;
+  // decode: column blocks (16 columns each) per workgroup, k-blocks unrolled per wave step
+  int cb;
+  // prefill: workgroup tile
+  int bm, bn;
+  // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
+  int splits;
+  int kb_per_split;
+  // grid
+  unsigned grid_x, grid_y;
+  int tiles;              // output tiles that own a split-K counter
+  int tile_elems;         // fp32 elements of one partial tile
+  size_t counters_bytes;  // workspace prefix holding one 32-bit ticket per tile
+  size_t ws_bytes;        // total workspace (0 when splits == 1)
+};
+
+qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* plan);
+
+}  // namespace qgemm

@@ -1,0 +1,476 @@
+// gfx950 (CDNA4) kernels of the weight-only quantized GEMM and the qgemm_run entry point.
+//
+//   out[M, N] = A[M, K] . dequant(W)[K, N]   (times alpha for FP8 / FP4)
+//
+// Both kernels feed v_mfma_f32_16x16x32_{f16,bf16}.  Operand fragment of that MFMA, per
+// 64-lane wavefront: lane l supplies row (A) or column (B) l & 15 and the eight
+// consecutive K values 8 (l >> 4) .. 8 (l >> 4) + 7 of the 32-wide K step; the 16x16 fp32
+// result sits in lane l as rows 4 (l >> 4) .. +3 of column l & 15.  The packed weight
+// layout puts exactly one such B fragment per K step in each lane's 16-byte chunk, so a
+// wavefront turns one coalesced 1 KiB load into MFMA operands with register-only
+// unpacking: the dequantize-in-registers pattern of Low Bit Triton Kernels (GPU MODE
+// lecture 034, core pattern), without the shared-memory re-layout that the Bitblas
+// lecture 033 (layout section) measures as the dominant cost when fragments mismatch.
+//
+// Dequantization (value semantics of each format):
+//   INT4: the nibble (stored value + 8) is OR-ed into the mantissa of an fp16 constant
+//         (0x6400 = 1024 for a low nibble, 0x5400 = 64 for a nibble at bit 4), the
+//         constant plus 8 is subtracted (exact), and the result is multiplied by the fp16
+//         group scale: RNE_fp16((nibble - 8) * s), the 16-bit tile of the gemlite snippet.
+//   FP8 : v_cvt_scalef32_pk_bf16_fp8 with scale 1.0 (OCP e4m3, exact in bf16); the
+//         per-tensor alpha multiplies the fp32 accumulator in the epilogue (FlashInfer
+//         PR #7495 analysis, introduction).
+//   FP4 : v_cvt_scalef32_pk_f32_fp4 with scale 1.0, times the e4m3 block scale in fp32
+//         (exact), then RNE to bf16 (exact).  The scale operand of the scalef32 converts
+//         only honours its exponent, so it cannot carry an e4m3 block scale.
+//
+// Split-K (when the output tiles alone cannot fill 256 compute units): each K slice writes
+// an fp32 partial tile to the workspace, then takes a ticket; the workgroup that draws the
+// last ticket sums all partials in slice order (bitwise deterministic, whichever slice
+// arrives last) and resets the ticket.  No workgroup ever waits for another, so nothing
+// assumes co-residency (FlashInfer PR #7495 analysis, section 3(d), describes the deadlock
+// that assumption caused and the slice-ordered sum that keeps results bitwise identical).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "qgemm_internal.h"
+
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct KArgs {
+  const uint16_t* A;          // [M][K] 16-bit
+  const uint8_t* W;           // packed weights
+  const void* S;              // packed scales (INT4: fp16, FP4: e4m3 bytes)
+  const float* alpha;         // FP8 / FP4: device scalar
+  void* out;                  // [M][N]
+  unsigned* counters;         // split-K tickets, one per tile
+  float* partials;            // split-K partial tiles
+  int M, N, K;
+  int out_dtype;
+  int group_size;
+  int splits, kb_per_split;
+  int tiles_n;                // prefill: output tiles along N
+};
+
+// ----------------------------------------------------------------------------- dequant
+__device__ __forceinline__ u32x4 dq_int4(unsigned w, unsigned s2) {
+  const unsigned hi = w >> 8;
+  const unsigned p0 = (w & 0x000F000Fu) | 0x64006400u;    // k slots j0, j1: 1024 + nibble
+  const unsigned p1 = (w & 0x00F000F0u) | 0x54005400u;    // j2, j3: 64 + nibble
+  const unsigned p2 = (hi & 0x000F000Fu) | 0x64006400u;   // j4, j5
+  const unsigned p3 = (hi & 0x00F000F0u) | 0x54005400u;   // j6, j7
+  const f16x2 s = __builtin_bit_cast(f16x2, s2);
+  const f16x2 big = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 small = {(_Float16)72.0f, (_Float16)72.0f};
+  const f16x2 h0 = (__builtin_bit_cast(f16x2, p0) - big) * s;
+  const f16x2 h1 = (__builtin_bit_cast(f16x2, p1) - small) * s;
+  const f16x2 h2 = (__builtin_bit_cast(f16x2, p2) - big) * s;
+  const f16x2 h3 = (__builtin_bit_cast(f16x2, p3) - small) * s;
+  return u32x4{__builtin_bit_cast(unsigned, h0), __builtin_bit_cast(unsigned, h1),
+               __builtin_bit_cast(unsigned, h2), __builtin_bit_cast(unsigned, h3)};
+}
+
+__device__ __forceinline__ u32x4 dq_fp8(unsigned lo, unsigned hi) {
+  return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+__device__ __forceinline__ unsigned pk_bf16(f32x2 f, float s) {
+  bf16x2 r;
+  r[0] = (__bf16)(f[0] * s);
+  r[1] = (__bf16)(f[1] * s);
+  return __builtin_bit_cast(unsigned, r);
+}
+
+__device__ __forceinline__ u32x4 dq_fp4(unsigned w, float s) {
+  return u32x4{pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), s),
+               pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), s),
+               pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), s),
+               pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), s)};
+}
+
+// Four e4m3 block-scale bytes -> fp32 (exact through the verified e4m3 -> bf16 convert).
+__device__ __forceinline__ void fp4_scales(unsigned sw, float (&s)[4]) {
+  const unsigned a = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(sw, 1.0f, false));
+  const unsigned b = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(sw, 1.0f, true));
+  s[0] = __builtin_bit_cast(float, a << 16);
+  s[1] = __builtin_bit_cast(float, a & 0xFFFF0000u);
+  s[2] = __builtin_bit_cast(float, b << 16);
+  s[3] = __builtin_bit_cast(float, b & 0xFFFF0000u);
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (FMT == qgemm::FMT_INT4)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Weights + scales of one (column block, 128-wide k block) as seen by one lane.
+template <int FMT>
+struct WFrag {
+  u32x4 w[FMT == qgemm::FMT_FP8 ? 2 : 1];
+  unsigned s[4];    // INT4: fp16 scale pair per K step; FP4: 4 scale bytes (one dword)
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int lane, WFrag<FMT>& f) {
+  const int KB = a.K >> 7;
+  if constexpr (FMT == qgemm::FMT_FP8) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * (KB * 2) + 2 * kb) * 1024) + lane;
+    f.w[0] = __builtin_nontemporal_load(p);
+    f.w[1] = __builtin_nontemporal_load(p + 64);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * KB + kb) * 1024) + lane;
+    f.w[0] = __builtin_nontemporal_load(p);
+  }
+  if constexpr (FMT == qgemm::FMT_INT4) {
+    const uint16_t* S = static_cast<const uint16_t*>(a.S);
+    const int c = lane & 15;
+    const int G = a.group_size;
+    if (G <= 128) {
+      const int T = 128 / G;
+      const size_t base = ((size_t)nb * KB + kb) * 16 * T + (size_t)c * T;
+      unsigned v[4];
+      if (T == 4) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(S + base);
+        v[0] = x[0] & 0xFFFFu; v[1] = x[0] >> 16; v[2] = x[1] & 0xFFFFu; v[3] = x[1] >> 16;
+      } else if (T == 2) {
+        const unsigned x = *reinterpret_cast<const unsigned*>(S + base);
+        v[0] = v[1] = x & 0xFFFFu;
+        v[2] = v[3] = x >> 16;
+      } else {
+        v[0] = v[1] = v[2] = v[3] = S[base];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f.s[t] = v[t] | (v[t] << 16);
+    } else {   // G == 256: one scale per two k blocks
+      const unsigned x = S[((size_t)nb * (KB >> 1) + (kb >> 1)) * 16 + c];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) f.s[t] = x | (x << 16);
+    }
+  } else if constexpr (FMT == qgemm::FMT_FP4) {
+    const uint8_t* S = static_cast<const uint8_t*>(a.S);
+    f.s[0] = *reinterpret_cast<const unsigned*>(S + (((size_t)nb * KB + kb) * 16 + (lane & 15)) * 8 + 4 * (lane >> 5));
+  }
+}
+
+// The B operand (dequantized weights) of K step t.
+template <int FMT>
+__device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (&fs)[4]) {
+  if constexpr (FMT == qgemm::FMT_INT4) {
+    return dq_int4(f.w[0][t], f.s[t]);
+  } else if constexpr (FMT == qgemm::FMT_FP8) {
+    return dq_fp8(f.w[t >> 1][2 * (t & 1)], f.w[t >> 1][2 * (t & 1) + 1]);
+  } else {
+    return dq_fp4(f.w[0][t], fs[t]);
+  }
+}
+
+// ----------------------------------------------------------------------------- epilogue
+__device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v) {
+  const size_t i = (size_t)m * a.N + n;
+  if (a.out_dtype == QGEMM_DT_F32) {
+    static_cast<float*>(a.out)[i] = v;
+  } else if (a.out_dtype == QGEMM_DT_F16) {
+    static_cast<_Float16*>(a.out)[i] = (_Float16)v;
+  } else {
+    static_cast<__bf16*>(a.out)[i] = (__bf16)v;
+  }
+}
+
+// Split-K hand-off.  Every thread of the workgroup calls this with its NF fragments
+// (`active` false for threads that hold none).  Returns true in the workgroup that must
+// write the output; then `v` holds the slice-ordered sum of all partials.
+template <int NF>
+__device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  float* base = a.partials + (size_t)tile * a.splits * tile_elems;
+  if (active) {
+    f32x4* mine = reinterpret_cast<f32x4*>(base + (size_t)split * tile_elems);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) mine[f * 256 + tid] = v[f];
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned ticket = atomicAdd(a.counters + tile, 1u);
+    s_last = ticket == (unsigned)(a.splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return false;
+  __threadfence();
+  if (active) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) v[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.splits; ++s) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(base + (size_t)s * tile_elems);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) v[f] += p[f * 256 + tid];
+    }
+  }
+  if (tid == 0) atomicExch(a.counters + tile, 0u);
+  return true;
+}
+
+// ============================================================================= decode
+// M <= 16.  Workgroup = 4 wavefronts; it owns CB column blocks (16 columns each) and one
+// K slice; wavefront w takes the slice's k blocks w, w + 4, ... and accumulates a 16 x 16
+// MFMA tile per column block.  The four wavefront tiles are summed through LDS in wave
+// order, then split-K or the epilogue follows.
+template <int FMT, int CB>
+__global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int group = blockIdx.x, split = blockIdx.y;
+  const int KB = a.K >> 7, NB = a.N >> 4;
+  const int kb_begin = split * a.kb_per_split;
+  const int kb_end = min(KB, kb_begin + a.kb_per_split);
+  const int nb0 = group * CB;
+  const int row = lane & 15;
+  const bool row_ok = row < a.M;
+
+  f32x4 acc[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int U = 2;   // k blocks in flight per wavefront
+  for (int kb_base = kb_begin + wave; kb_base < kb_end; kb_base += 4 * U) {
+    u32x4 afr[U][4];
+    WFrag<FMT> wf[U][CB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kb_base + 4 * u;
+      if (kb < kb_end) {
+        const u32x4* ap = reinterpret_cast<const u32x4*>(a.A + (size_t)row * a.K + (size_t)kb * 128 + 8 * (lane >> 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) afr[u][t] = row_ok ? ap[4 * t] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          if (nb0 + c < NB) load_wfrag<FMT>(a, nb0 + c, kb, lane, wf[u][c]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kb_base + 4 * u;
+      if (kb < kb_end) {
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+          if (nb0 + c < NB) {
+            float fs[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[c] = mfma<FMT>(afr[u][t], bfrag<FMT>(wf[u][c], t, fs), acc[c]);
+          }
+        }
+      }
+    }
+  }
+
+  __shared__ f32x4 red[4][CB][64];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) red[wave][c][lane] = acc[c];
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const bool active = tid < CB * 64;
+  const int c = tid >> 6, ln = tid & 63;
+  f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (active) v[0] = ((red[0][c][ln] + red[1][c][ln]) + red[2][c][ln]) + red[3][c][ln];
+  if (a.splits > 1) {
+    if (!splitk_finish<1>(a, group, split, CB * 256, active, v)) return;
+  }
+  if (!active || nb0 + c >= NB) return;
+  const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
+  const int n = (nb0 + c) * 16 + (ln & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * (ln >> 4) + r;
+    if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[0][r] : v[0][r] * alpha);
+  }
+}
+
+// ============================================================================= prefill
+// Workgroup tile 128 x 128, 4 wavefronts in 2 x 2, each 64 x 64 (4 x 4 MFMA tiles).
+// Per 128-wide k block: the A tile is staged through LDS (rows padded by 16 bytes against
+// bank conflicts); each wavefront loads its own packed weight fragments straight into
+// registers and dequantizes them once per K step, reusing them across its 4 row tiles.
+constexpr int PF_BM = 128, PF_BN = 128, PF_LDA = 128 + 8;
+
+template <int FMT>
+__global__ __launch_bounds__(256) void qgemm_prefill(KArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[PF_BM * PF_LDA];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+  const int m0 = tm * PF_BM, n0 = tn * PF_BN;
+  const int KB = a.K >> 7, NB = a.N >> 4;
+  const int kb_begin = split * a.kb_per_split;
+  const int kb_end = min(KB, kb_begin + a.kb_per_split);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    // global -> registers: A tile 128 rows x 128 k = 2048 chunks of 16 bytes, 8 per thread
+    u32x4 areg[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;
+      const int r = q >> 4, c8 = q & 15;
+      const int m = m0 + r;
+      areg[i] = m < a.M ? *reinterpret_cast<const u32x4*>(a.A + (size_t)m * a.K + (size_t)kb * 128 + 8 * c8)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    WFrag<FMT> wf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = (n0 >> 4) + 4 * wn + j;
+      if (nb < NB) load_wfrag<FMT>(a, nb, kb, lane, wf[j]);
+    }
+    __syncthreads();   // previous k block's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;
+      const int r = q >> 4, c8 = q & 15;
+      *reinterpret_cast<u32x4*>(As + r * PF_LDA + 8 * c8) = areg[i];
+    }
+    __syncthreads();
+    float fs[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fs[j][t] = 0.f;
+      if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[j].s[0], fs[j]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = bfrag<FMT>(wf[j], t, fs[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(As + (64 * wm + 16 * i + (lane & 15)) * PF_LDA + 32 * t + 8 * (lane >> 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<FMT>(af, b[j], acc[i][j]);
+      }
+    }
+  }
+
+  f32x4 v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * i + j] = acc[i][j];
+  if (a.splits > 1) {
+    if (!splitk_finish<16>(a, tile, split, PF_BM * PF_BN, true, v)) return;
+  }
+  const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = (n0 >> 4) + 4 * wn + j;
+      if (nb >= NB) continue;
+      const int n = nb * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
+        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[4 * i + j][r] : v[4 * i + j][r] * alpha);
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------- launch
+template <int FMT>
+hipError_t launch(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
+  const dim3 grid(pl.grid_x, pl.grid_y), block(256);
+  if (pl.kind == qgemm::KIND_PREFILL) {
+    hipLaunchKernelGGL(qgemm_prefill<FMT>, grid, block, 0, stream, a);
+  } else if (pl.cb == 4) {
+    hipLaunchKernelGGL((qgemm_decode<FMT, 4>), grid, block, 0, stream, a);
+  } else if (pl.cb == 2) {
+    hipLaunchKernelGGL((qgemm_decode<FMT, 2>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((qgemm_decode<FMT, 1>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, const void* w_packed,
+                                    const void* s_packed, const float* alpha, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  using namespace qgemm;
+  clear_error();
+  qgemm_status_t st = validate_problem(p);
+  if (st != QGEMM_OK) return st;
+  const Format fmt = format_of(p);
+  if (!A) return fail(QGEMM_ERR_INVALID_ARGUMENT, "A is NULL");
+  if (!w_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed is NULL");
+  if (!out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (fmt != FMT_FP8 && !s_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "s_packed is NULL (needed for INT4 and FP4)");
+  if (fmt != FMT_INT4 && !alpha) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha is NULL (needed for FP8 and FP4)");
+  if (!aligned(A, 16)) return fail(QGEMM_ERR_MISALIGNED, "A must be 16-byte aligned");
+  if (!aligned(w_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "w_packed must be 16-byte aligned");
+  if (s_packed && fmt != FMT_FP8 && !aligned(s_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "s_packed must be 16-byte aligned");
+  if (alpha && fmt != FMT_INT4 && !aligned(alpha, 4)) return fail(QGEMM_ERR_MISALIGNED, "alpha must be 4-byte aligned");
+  if (!aligned(out, 16)) return fail(QGEMM_ERR_MISALIGNED, "out must be 16-byte aligned");
+
+  Plan pl;
+  st = make_plan(p, &pl);
+  if (st != QGEMM_OK) return st;
+  if (pl.ws_bytes) {
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+      return fail(QGEMM_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given%s", pl.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 256)) return fail(QGEMM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  }
+
+  KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.A = static_cast<const uint16_t*>(A);
+  a.W = static_cast<const uint8_t*>(w_packed);
+  a.S = s_packed;
+  a.alpha = alpha;
+  a.out = out;
+  if (pl.ws_bytes) {
+    a.counters = static_cast<unsigned*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counters_bytes);
+  }
+  a.M = (int)p->M;
+  a.N = (int)p->N;
+  a.K = (int)p->K;
+  a.out_dtype = p->out_dtype;
+  a.group_size = p->group_size;
+  a.splits = pl.splits;
+  a.kb_per_split = pl.kb_per_split;
+  a.tiles_n = (int)((p->N + pl.bn - 1) / (pl.bn ? pl.bn : 1));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fmt == FMT_INT4 ? launch<FMT_INT4>(pl, a, s)
+               : fmt == FMT_FP8  ? launch<FMT_FP8>(pl, a, s)
+                                 : launch<FMT_FP4>(pl, a, s);
+  if (e != hipSuccess) return fail(QGEMM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return QGEMM_OK;
+}
