@@ -1,0 +1,267 @@
+"""Benchmark of the weight-only quantized GEMM on one MI355X.
+
+A step is one pass of the decode workload the headline metric is quoted on: W4A16 with
+fp16 activations, int4 weights in groups of 128 along K with fp16 scales, and the four
+GEMMs M in {1, 16} x (N, K) in {(4096, 4096), (11008, 4096)}.  Every launch reads a
+different copy of the packed weights (rotating copies, > 1 GB between two reads of the
+same copy), so the weight stream comes from HBM, not from the 256 MB last-level cache.
+The K timed steps are one HIP-graph replay; `value` is the effective weight bandwidth
+(packed weight + scale bytes / time) over them.
+
+Also reported: a `roofline` object for the decode kernel, `secondary` numbers (per-shape
+decode timings and the M = 4096 prefill TFLOP/s over the group-size sweep), and the CPU
+oracle timed on the host as `cpu_baseline`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2516.6  # dense fp16/bf16 MFMA, published (no sparsity)
+METRIC = "effective weight GB/s at M=1/16 and TFLOP/s at M=4096, % of MI355X roofline"
+
+DECODE_SHAPES = [(1, 4096, 4096), (16, 4096, 4096), (1, 11008, 4096), (16, 11008, 4096)]
+PREFILL_G = [32, 64, 128, 256]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def weight_bytes(fmt, N, K, G):
+    if fmt == "int4":
+        return N * K // 2 + (K // G) * N * 2
+    if fmt == "fp8":
+        return N * K
+    return N * K // 2 + N * K // 16
+
+
+class Gemm:
+    """One GEMM with rotating device copies of its packed weights."""
+
+    def __init__(self, q, torch, fmt, M, N, K, G, key, min_rotate_bytes):
+        import synthetic
+        self.fmt, self.M, self.N, self.K, self.G = fmt, M, N, K, G
+        self.p = q.problem(M, N, K, fmt, group_size=G if fmt == "int4" else None)
+        pq = q.problem(1, N, K, fmt, group_size=G if fmt == "int4" else None)
+        w = synthetic.weights(N, K, {"int4": 0.02, "fp8": 0.05, "fp4": 0.02}[fmt], key)
+        codes, scales, alpha = q.quantize(pq, w)            # the library's own quantizer
+        wpk, spk = q.pack(pq, codes, scales)
+        self.wbytes = weight_bytes(fmt, N, K, G)
+        assert self.wbytes == wpk.size + (0 if spk is None else spk.size)
+        ncopies = max(2, -(-min_rotate_bytes // self.wbytes))
+        w0 = torch.from_numpy(wpk).cuda()
+        s0 = None if spk is None else torch.from_numpy(spk).cuda()
+        self.w = [w0] + [w0.clone() for _ in range(ncopies - 1)]
+        self.s = [s0] + [None if s0 is None else s0.clone() for _ in range(ncopies - 1)]
+        self.alpha = torch.tensor([alpha], dtype=torch.float32, device="cuda")
+        self.A = synthetic.activations(M, K, "f16" if fmt == "int4" else "bf16", key).cuda()
+        odt = torch.float16 if fmt == "int4" else torch.bfloat16
+        self.out = torch.empty((M, N), dtype=odt, device="cuda")
+        self.ws = q.alloc_workspace(self.p)
+        self.i = 0
+        self.q = q
+
+    def launch(self):
+        c = self.i % len(self.w)
+        self.i += 1
+        self.q.run(self.p, self.A, self.w[c], self.s[c], None if self.fmt == "int4" else self.alpha,
+                   self.out, self.ws)
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+
+def graph_of(torch, fn, n):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                          # one eager call on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps=1):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps        # ms
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (dequant in fp32 + fp64 matmul) on the decode step, timed on the host."""
+    import synthetic
+    from oracle import quant, reference
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wi = synthetic.WORKLOAD_INDEX["int4_decode"]
+    prepared = []
+    for si, (M, N, K) in enumerate(DECODE_SHAPES):
+        w = synthetic.weights(N, K, 0.02, (wi, si))
+        codes, sbits = quant.quantize_int4(w, 128)
+        a = synthetic.activations(M, K, "f16", (wi, si)).float().numpy()
+        prepared.append((codes, sbits, a, weight_bytes("int4", N, K, 128)))
+    t0 = time.perf_counter()
+    done_bytes, steps = 0, 0
+    while True:
+        for codes, sbits, a, nb in prepared:
+            wdq = reference.dequant_int4(codes, sbits, 128)
+            reference.gemm_fp64(a, wdq)
+            done_bytes += nb
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 20:
+            break
+    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full decode steps (4 GEMMs each: fp32 dequant + fp64 matmul), "
+                      f"{el:.1f} s, host cores available {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--all", action="store_true", help="also time the FP8 and FP4 workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rotate-mb", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMM shards by "
+              "columns with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weight_only_quantized_qgemm_amd as q
+    import synthetic
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.init()
+    rot = args.rotate_mb << 20
+
+    wi = synthetic.WORKLOAD_INDEX["int4_decode"]
+    log("bench: preparing decode workload")
+    gemms = [Gemm(q, torch, "int4", M, N, K, 128, (wi, si), rot // 2) for si, (M, N, K) in enumerate(DECODE_SHAPES)]
+
+    def step():
+        for g in gemms:
+            g.launch()
+
+    step_bytes = sum(g.wbytes for g in gemms)
+    # warmup: eager steps, then a captured graph of exactly `steps` steps
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: capturing {args.steps} steps")
+    graph = graph_of(torch, step, args.steps)
+    graph.replay()                        # untimed warm replay
+    torch.cuda.synchronize()
+
+    log("bench: timed region")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes * args.steps / wall / 1e9
+    launches = 4 * args.steps
+    avg_launch_us = ev_ms * 1e3 / launches
+    avg_bytes = step_bytes / 4
+    achieved = avg_bytes / (avg_launch_us * 1e-6) / 1e9
+    del graph
+
+    # per-shape breakdown (graphs of one GEMM repeated; not part of the timed steps)
+    secondary = []
+    for g in gemms:
+        n = 64
+        gg = graph_of(torch, g.launch, n)
+        ms = time_graph(torch, gg, 3)
+        us = ms * 1e3 / n
+        secondary.append({"gemm": f"int4 M={g.M} N={g.N} K={g.K} G=128", "us_per_launch": round(us, 3),
+                          "weight_GBps": round(g.wbytes / (us * 1e-6) / 1e9, 1),
+                          "frac_hbm": round(g.wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        del gg
+    del gemms
+    torch.cuda.empty_cache()
+
+    # prefill M = 4096 over the group-size sweep (TFLOP/s)
+    wi2 = synthetic.WORKLOAD_INDEX["int4_prefill"]
+    for G in PREFILL_G:
+        g = Gemm(q, torch, "int4", 4096, 4096, 4096, G, (wi2, 0), 64 << 20)
+        gg = graph_of(torch, g.launch, 20)
+        ms = time_graph(torch, gg, 3) / 20
+        tf = g.flops / (ms * 1e-3) / 1e12
+        secondary.append({"gemm": f"int4 M=4096 N=4096 K=4096 G={G}", "us_per_launch": round(ms * 1e3, 2),
+                          "TFLOPs": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+        del gg, g
+        torch.cuda.empty_cache()
+
+    if args.all:
+        for name in ("fp8", "fp4"):
+            wk = synthetic.WORKLOADS[name]
+            wix = synthetic.WORKLOAD_INDEX[name]
+            for si, (M, N, K) in enumerate(wk["shapes"]):
+                big = M >= 128
+                g = Gemm(q, torch, name, M, N, K, 0, (wix, si), (64 << 20) if big else rot)
+                n = 10 if big else 64
+                gg = graph_of(torch, g.launch, n)
+                ms = time_graph(torch, gg, 3) / n
+                tf = g.flops / (ms * 1e-3) / 1e12
+                gbs = g.wbytes / (ms * 1e-3) / 1e9
+                secondary.append({"gemm": f"{name} M={M} N={N} K={K}", "us_per_launch": round(ms * 1e3, 2),
+                                  "TFLOPs": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                  "weight_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+                del gg, g
+                torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "W4A16 decode: fp16 A ~N(0,1); int4 W ~N(0,0.02), group 128, fp16 scales; "
+                               "M in {1,16} x (N,K) in {(4096,4096),(11008,4096)}; rotating weight copies",
+                   "gemms_per_step": 4, "weight_bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "qgemm_decode (int4)", "avg_launch_us": round(avg_launch_us, 3),
+                     "algorithmic_bytes_per_launch": avg_bytes},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

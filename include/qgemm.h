@@ -80,8 +80,11 @@ typedef enum qgemm_scale_layout {
  *   M >= 1 (any value); N % 16 == 0; K % 128 == 0; for INT4 also K % group_size == 0.
  *   group_size: INT4 only, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
- *   slices (1..64) the chosen kernel uses.  Both only change the reduction order of the
- *   fp32 accumulation, never the packed layout.
+ *   slices (1..64) the chosen kernel uses; tile_hint: 0 = automatic, else for the decode
+ *   kernel the number of 16-column blocks per workgroup (1, 2 or 4); the prefill kernel
+ *   accepts only 0.  Hints only change the work split and the reduction order of the fp32
+ *   accumulation, never the packed layout; the automatic choice depends only on M, N, K
+ *   and the formats (never on out_dtype or pointers).
  */
 typedef struct qgemm_problem {
   int64_t M, N, K;
@@ -90,7 +93,7 @@ typedef struct qgemm_problem {
   int32_t scale_layout;
   int32_t kernel_hint;
   int32_t split_k_hint;
-  int32_t reserved;          /* must be 0 */
+  int32_t tile_hint;
 } qgemm_problem_t;
 
 /*

@@ -52,12 +52,13 @@ class Prepared:
         self.alpha_t = torch.tensor([self.alpha], dtype=torch.float32, device="cuda")
 
 
-def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=None):
+def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=None, tile_hint=0):
     """Run through the C ABI; returns (out as numpy float64 or 16-bit bits, the workspace)."""
     import torch
     M, K = A16.shape
     p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt == "int4" else None,
-                  out_dtype=out_dtype, kernel_hint=kernel_hint, split_k_hint=split_k_hint)
+                  out_dtype=out_dtype, kernel_hint=kernel_hint, split_k_hint=split_k_hint,
+                  tile_hint=tile_hint)
     tdt = {q.DT_F32: torch.float32, q.DT_F16: torch.float16, q.DT_BF16: torch.bfloat16}[out_dtype]
     out = torch.full((M, prep.N), float("nan"), dtype=tdt, device="cuda")
     A = A16.cuda()
@@ -87,14 +88,14 @@ def out16_values(bits, fmt):
     return codecs.f16_from_bits(bits) if fmt == "int4" else codecs.bf16_from_bits(bits)
 
 
-def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0):
+def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0, tile_hint=0):
     """E1/E2 on the fp32 output, E2 on the 16-bit output, E3 between them."""
     M = A16.shape[0]
     rows = np.arange(M) if rows is None else np.asarray(rows)
-    y32, ws = run_gpu(q, prep, A16, q.DT_F32, kernel_hint, split_k_hint)
+    y32, ws = run_gpu(q, prep, A16, q.DT_F32, kernel_hint, split_k_hint, tile_hint=tile_hint)
     r = ref_rows(prep, A16, rows)
     st = tolerance.check_e1_e2(y32[rows], r)
-    y16, _ = run_gpu(q, prep, A16, out16_dtype(q, prep.fmt), kernel_hint, split_k_hint, ws)
+    y16, _ = run_gpu(q, prep, A16, out16_dtype(q, prep.fmt), kernel_hint, split_k_hint, ws, tile_hint)
     tolerance.check_e3(y16, y32.astype(np.float32), out16_kind(prep.fmt))
     tolerance.check_e2(out16_values(y16[rows], prep.fmt), r)
     return st, y32

@@ -115,13 +115,15 @@ def test_m_sweep_ragged(q, fmt, G, M):
 
 
 @pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
-@pytest.mark.parametrize("hint,split", [(1, 1), (1, 2), (1, 3), (1, 7), (2, 1), (2, 2), (2, 5)])
-def test_split_k_and_kernel_hints(q, fmt, hint, split):
-    M, N, K = 16, 256, 1792    # 14 k blocks
-    say(f"case hints fmt={fmt} kernel={hint} split={split}")
+@pytest.mark.parametrize("M,hint,split,tile", [(16, 1, 2, 0), (16, 1, 3, 1), (16, 1, 7, 2), (16, 1, 14, 4),
+                                               (4, 1, 1, 4), (4, 1, 5, 1), (16, 2, 1, 0), (16, 2, 2, 0),
+                                               (16, 2, 5, 0)])
+def test_split_k_and_kernel_hints(q, fmt, M, hint, split, tile):
+    N, K = 256, 1792    # 14 k blocks
+    say(f"case hints fmt={fmt} M={M} kernel={hint} split={split} tile={tile}")
     prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (51, N, K))
     A = _act(fmt, M, K, (51, M))
-    check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split)
+    check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, tile_hint=tile)
 
 
 @pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
@@ -164,7 +166,7 @@ def test_int4_closed_form_equal_nibbles_unit_scales(q):
     import torch as T
     N, K, M = 64, 1024, 8
     say("case closed-form int4")
-    p = q.problem(M, N, K, "int4")
+    p = q.problem(M, N, K, "int4", out_dtype=q.DT_F32)
     A16 = _act("int4", M, K, (54, 0))
     rowsum = A16.to(T.float64).sum(dim=1).numpy()
     for c in (0, 5, 8, 15):

@@ -16,6 +16,10 @@ import ctypes
 import os
 
 import numpy as np
+# torch first: it loads its HIP runtime (soname libamdhip64.so.7), and the library below then
+# binds to that same runtime instance, so torch's pointers and streams are valid in it.  Loading
+# the library first would bring in a second runtime that cannot share the device with torch's.
+import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqgemm.so")
@@ -37,7 +41,7 @@ class Problem(ctypes.Structure):
                 ("a_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
                 ("kernel_hint", ctypes.c_int32), ("split_k_hint", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("tile_hint", ctypes.c_int32)]
 
 
 assert ctypes.sizeof(Problem) == 56
@@ -80,14 +84,15 @@ _FORMATS = {
 }
 
 
-def problem(M, N, K, fmt, group_size=None, out_dtype=None, kernel_hint=KERNEL_AUTO, split_k_hint=0):
+def problem(M, N, K, fmt, group_size=None, out_dtype=None, kernel_hint=KERNEL_AUTO, split_k_hint=0,
+            tile_hint=0):
     """Problem descriptor for one of the formats 'int4', 'fp8', 'fp4'."""
     a, w, sl, o = _FORMATS[fmt]
     if group_size is None:
         group_size = {"int4": 128, "fp8": 0, "fp4": 16}[fmt]
     if out_dtype is not None:
         o = out_dtype
-    return Problem(M, N, K, a, w, o, group_size, sl, kernel_hint, split_k_hint, 0)
+    return Problem(M, N, K, a, w, o, group_size, sl, kernel_hint, split_k_hint, tile_hint)
 
 
 def fmt_of(p):

@@ -49,7 +49,6 @@ static const int64_t kMaxDim = int64_t(1) << 24;
 
 qgemm_status_t validate_problem(const qgemm_problem_t* p) {
   if (!p) return fail(QGEMM_ERR_INVALID_ARGUMENT, "problem is NULL");
-  if (p->reserved != 0) return fail(QGEMM_ERR_INVALID_ARGUMENT, "problem.reserved must be 0, got %d", p->reserved);
   for (int d : {p->a_dtype, p->w_dtype, p->out_dtype})
     if (d < QGEMM_DT_F16 || d > QGEMM_DT_FP4_E2M1)
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "dtype value %d is not a qgemm_dtype_t", d);
@@ -95,6 +94,11 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
   if (p->split_k_hint > p->K / 128)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d exceeds the %lld 128-wide K blocks",
                 p->split_k_hint, (long long)(p->K / 128));
+  const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
+  if (decode && p->tile_hint != 0 && p->tile_hint != 1 && p->tile_hint != 2 && p->tile_hint != 4)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the decode kernel must be 0, 1, 2 or 4, got %d", p->tile_hint);
+  if (!decode && p->tile_hint != 0)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the prefill kernel must be 0, got %d", p->tile_hint);
   return QGEMM_OK;
 }
 
@@ -117,22 +121,25 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
   pl->fmt = format_of(p);
   const int kblocks = (int)(p->K / 128);
   const int nblocks = (int)(p->N / 16);
-  bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
+  const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
   if (decode) {
     pl->kind = KIND_DECODE;
-    // Column blocks per workgroup: more columns per workgroup means fewer re-reads of A
-    // (all of A is read by every workgroup of a K slice); keep >= ~2 workgroups per CU.
-    pl->cb = 1;
-    if (p->M > 1) {
-      pl->cb = 4;
-      while (pl->cb > 1 && nblocks % pl->cb) pl->cb /= 2;
-    }
+    // Column blocks per workgroup.  Every workgroup reads its K slice of A, so wider
+    // workgroups cut A re-reads when M > 1; at M = 1, A is a few KiB and one block (the
+    // most workgroups) is best.
+    pl->cb = p->tile_hint ? p->tile_hint : (p->M == 1 ? 1 : 4);
     const int groups = ceil_div(nblocks, pl->cb);
-    // K splits so that the grid fills the chip at least twice.
+    // Split K until the grid covers every compute unit, keeping >= 4 k blocks per slice
+    // (one per wavefront).
     int s = 1;
-    while (groups * s < 2 * kCUs && s * 2 <= kblocks / 2) s *= 2;
+    while (groups * s < kCUs && kblocks / (s * 2) >= 4) s *= 2;
     pl->splits = s;
     finish_split(pl, kblocks, p->split_k_hint);
+    // k blocks per wavefront run: up to 8 weight blocks in flight per wavefront, and
+    // enough runs that all four wavefronts of the workgroup get work.
+    pl->kpw = 1;
+    for (int k = 8; k >= 1; k /= 2)
+      if (pl->cb * k <= 8 && 4 * k <= pl->kb_per_split) { pl->kpw = k; break; }
     pl->grid_x = (unsigned)groups;
     pl->grid_y = (unsigned)pl->splits;
     pl->tiles = groups;

@@ -23,8 +23,8 @@ Format format_of(const qgemm_problem_t* p);
 struct Plan {
   Kind kind;
   Format fmt;
-  // decode: column blocks (16 columns each) per workgroup, k-blocks unrolled per wave step
-  int cb;
+  // decode: column blocks (16 columns each) per workgroup, k blocks per wavefront run
+  int cb, kpw;
   // prefill: workgroup tile
   int bm, bn;
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers

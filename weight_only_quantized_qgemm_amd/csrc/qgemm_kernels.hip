@@ -58,7 +58,6 @@ struct KArgs {
   float* partials;            // split-K partial tiles
   int M, N, K;
   int out_dtype;
-  int group_size;
   int splits, kb_per_split;
   int tiles_n;                // prefill: output tiles along N
 };
@@ -127,7 +126,9 @@ struct WFrag {
   unsigned s[4];    // INT4: fp16 scale pair per K step; FP4: 4 scale bytes (one dword)
 };
 
-template <int FMT>
+// G is the INT4 group size (a template parameter, so the scale load has no branches:
+// a branch around a load ends in a wait for every outstanding load); 0 for FP8 / FP4.
+template <int FMT, int G>
 __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int lane, WFrag<FMT>& f) {
   const int KB = a.K >> 7;
   if constexpr (FMT == qgemm::FMT_FP8) {
@@ -141,15 +142,14 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
   if constexpr (FMT == qgemm::FMT_INT4) {
     const uint16_t* S = static_cast<const uint16_t*>(a.S);
     const int c = lane & 15;
-    const int G = a.group_size;
-    if (G <= 128) {
-      const int T = 128 / G;
+    if constexpr (G <= 128) {
+      constexpr int T = 128 / G;
       const size_t base = ((size_t)nb * KB + kb) * 16 * T + (size_t)c * T;
       unsigned v[4];
-      if (T == 4) {
+      if constexpr (T == 4) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(S + base);
         v[0] = x[0] & 0xFFFFu; v[1] = x[0] >> 16; v[2] = x[1] & 0xFFFFu; v[3] = x[1] >> 16;
-      } else if (T == 2) {
+      } else if constexpr (T == 2) {
         const unsigned x = *reinterpret_cast<const unsigned*>(S + base);
         v[0] = v[1] = x & 0xFFFFu;
         v[2] = v[3] = x >> 16;
@@ -196,86 +196,107 @@ __device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v)
 // Split-K hand-off.  Every thread of the workgroup calls this with its NF fragments
 // (`active` false for threads that hold none).  Returns true in the workgroup that must
 // write the output; then `v` holds the slice-ordered sum of all partials.
+//
+// Visibility across XCDs without L2 maintenance: partials are written with device-scope
+// stores (write-through past the XCD-private L2), every thread waits for its stores to
+// be acknowledged before the barrier that precedes the ticket, and the last workgroup
+// reads the partials back with device-scope loads.  A device-scope fence would instead
+// write back and invalidate the whole XCD L2 in every workgroup.
+__device__ __forceinline__ void store_dev(float* p, f32x4 v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) __hip_atomic_store(p + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_dev(const float* p) {
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
 template <int NF>
 __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
   __shared__ int s_last;
   const int tid = threadIdx.x;
   float* base = a.partials + (size_t)tile * a.splits * tile_elems;
   if (active) {
-    f32x4* mine = reinterpret_cast<f32x4*>(base + (size_t)split * tile_elems);
+    float* mine = base + (size_t)split * tile_elems;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) mine[f * 256 + tid] = v[f];
+    for (int f = 0; f < NF; ++f) store_dev(mine + 4 * (f * 256 + tid), v[f]);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores are complete
   __syncthreads();
   if (tid == 0) {
-    const unsigned ticket = atomicAdd(a.counters + tile, 1u);
+    const unsigned ticket = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = ticket == (unsigned)(a.splits - 1);
   }
   __syncthreads();
   if (!s_last) return false;
-  __threadfence();
   if (active) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) v[f] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < a.splits; ++s) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(base + (size_t)s * tile_elems);
+      const float* p = base + (size_t)s * tile_elems;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) v[f] += p[f * 256 + tid];
+      for (int f = 0; f < NF; ++f) v[f] += load_dev(p + 4 * (f * 256 + tid));
     }
   }
-  if (tid == 0) atomicExch(a.counters + tile, 0u);
+  if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
 // ============================================================================= decode
 // M <= 16.  Workgroup = 4 wavefronts; it owns CB column blocks (16 columns each) and one
-// K slice; wavefront w takes the slice's k blocks w, w + 4, ... and accumulates a 16 x 16
-// MFMA tile per column block.  The four wavefront tiles are summed through LDS in wave
-// order, then split-K or the epilogue follows.
-template <int FMT, int CB>
+// K slice.  Wavefront w streams contiguous runs of KPW k blocks (run r starts at k block
+// begin + (4 r + w) KPW).  Per run, the A fragments are loaded first, then every weight and
+// scale load of the run, and only then is anything consumed: loads complete in issue order,
+// so waiting for A never waits for the weight stream.  Rows of A at or beyond M are read
+// from row M - 1 instead of being masked: MFMA output row m depends on A row m only, and
+// rows >= M are never stored.  All control flow is wavefront-uniform (scalar branches);
+// loads past the end of the slice are clamped to its last k block and their results unused.
+// Each wavefront accumulates one 16 x 16 MFMA tile per column block; the four tiles are
+// summed through LDS in wave order, then split-K or the epilogue follows.
+template <int FMT, int G, int CB, int KPW>
 __global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = blockIdx.x, split = blockIdx.y;
   const int KB = a.K >> 7, NB = a.N >> 4;
   const int kb_begin = split * a.kb_per_split;
   const int kb_end = min(KB, kb_begin + a.kb_per_split);
   const int nb0 = group * CB;
-  const int row = lane & 15;
-  const bool row_ok = row < a.M;
+  const int row = min(lane & 15, a.M - 1);
+  const uint16_t* arow = a.A + (size_t)row * a.K + 8 * (lane >> 4);
 
   f32x4 acc[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int U = 2;   // k blocks in flight per wavefront
-  for (int kb_base = kb_begin + wave; kb_base < kb_end; kb_base += 4 * U) {
-    u32x4 afr[U][4];
-    WFrag<FMT> wf[U][CB];
+  for (int run = kb_begin + wave * KPW; run < kb_end; run += 4 * KPW) {
+    u32x4 afr[KPW][4];
+    WFrag<FMT> wf[KPW][CB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = kb_base + 4 * u;
-      if (kb < kb_end) {
-        const u32x4* ap = reinterpret_cast<const u32x4*>(a.A + (size_t)row * a.K + (size_t)kb * 128 + 8 * (lane >> 4));
+    for (int u = 0; u < KPW; ++u) {
+      const int kb = min(run + u, kb_end - 1);
+      const u32x4* ap = reinterpret_cast<const u32x4*>(arow + (size_t)kb * 128);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) afr[u][t] = row_ok ? ap[4 * t] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-          if (nb0 + c < NB) load_wfrag<FMT>(a, nb0 + c, kb, lane, wf[u][c]);
-      }
+      for (int t = 0; t < 4; ++t) afr[u][t] = ap[4 * t];
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = kb_base + 4 * u;
-      if (kb < kb_end) {
+    for (int u = 0; u < KPW; ++u) {
+      const int kb = min(run + u, kb_end - 1);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) load_wfrag<FMT, G>(a, min(nb0 + c, NB - 1), kb, lane, wf[u][c]);
+    }
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) {
+      if (run + u < kb_end) {
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-          if (nb0 + c < NB) {
-            float fs[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
+          float fs[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[c] = mfma<FMT>(afr[u][t], bfrag<FMT>(wf[u][c], t, fs), acc[c]);
-          }
+          for (int t = 0; t < 4; ++t) acc[c] = mfma<FMT>(afr[u][t], bfrag<FMT>(wf[u][c], t, fs), acc[c]);
         }
       }
     }
@@ -285,7 +306,6 @@ __global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
 #pragma unroll
   for (int c = 0; c < CB; ++c) red[wave][c][lane] = acc[c];
   __syncthreads();
-  const int tid = threadIdx.x;
   const bool active = tid < CB * 64;
   const int c = tid >> 6, ln = tid & 63;
   f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -310,10 +330,11 @@ __global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
 // registers and dequantizes them once per K step, reusing them across its 4 row tiles.
 constexpr int PF_BM = 128, PF_BN = 128, PF_LDA = 128 + 8;
 
-template <int FMT>
+template <int FMT, int G>
 __global__ __launch_bounds__(256) void qgemm_prefill(KArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[PF_BM * PF_LDA];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
@@ -343,7 +364,7 @@ __global__ __launch_bounds__(256) void qgemm_prefill(KArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int nb = (n0 >> 4) + 4 * wn + j;
-      if (nb < NB) load_wfrag<FMT>(a, nb, kb, lane, wf[j]);
+      if (nb < NB) load_wfrag<FMT, G>(a, nb, kb, lane, wf[j]);
     }
     __syncthreads();   // previous k block's LDS reads are done
 #pragma unroll
@@ -399,19 +420,46 @@ __global__ __launch_bounds__(256) void qgemm_prefill(KArgs a) {
 }
 
 // ----------------------------------------------------------------------------- launch
-template <int FMT>
+template <int FMT, int G, int CB, int KPW>
+void launch_decode(const dim3& grid, const KArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW>), grid, dim3(256), 0, stream, a);
+}
+
+template <int FMT, int G>
 hipError_t launch(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
-  const dim3 grid(pl.grid_x, pl.grid_y), block(256);
+  const dim3 grid(pl.grid_x, pl.grid_y);
   if (pl.kind == qgemm::KIND_PREFILL) {
-    hipLaunchKernelGGL(qgemm_prefill<FMT>, grid, block, 0, stream, a);
-  } else if (pl.cb == 4) {
-    hipLaunchKernelGGL((qgemm_decode<FMT, 4>), grid, block, 0, stream, a);
-  } else if (pl.cb == 2) {
-    hipLaunchKernelGGL((qgemm_decode<FMT, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G>), grid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((qgemm_decode<FMT, 1>), grid, block, 0, stream, a);
+    switch (pl.cb * 16 + pl.kpw) {
+      case 16 + 8: launch_decode<FMT, G, 1, 8>(grid, a, stream); break;
+      case 16 + 4: launch_decode<FMT, G, 1, 4>(grid, a, stream); break;
+      case 16 + 2: launch_decode<FMT, G, 1, 2>(grid, a, stream); break;
+      case 16 + 1: launch_decode<FMT, G, 1, 1>(grid, a, stream); break;
+      case 32 + 4: launch_decode<FMT, G, 2, 4>(grid, a, stream); break;
+      case 32 + 2: launch_decode<FMT, G, 2, 2>(grid, a, stream); break;
+      case 32 + 1: launch_decode<FMT, G, 2, 1>(grid, a, stream); break;
+      case 64 + 2: launch_decode<FMT, G, 4, 2>(grid, a, stream); break;
+      case 64 + 1: launch_decode<FMT, G, 4, 1>(grid, a, stream); break;
+      default: return hipErrorInvalidConfiguration;
+    }
   }
   return hipGetLastError();
+}
+
+hipError_t launch_any(const qgemm::Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  switch (pl.fmt) {
+    case qgemm::FMT_INT4:
+      switch (group_size) {
+        case 32: return launch<qgemm::FMT_INT4, 32>(pl, a, stream);
+        case 64: return launch<qgemm::FMT_INT4, 64>(pl, a, stream);
+        case 128: return launch<qgemm::FMT_INT4, 128>(pl, a, stream);
+        case 256: return launch<qgemm::FMT_INT4, 256>(pl, a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    case qgemm::FMT_FP8: return launch<qgemm::FMT_FP8, 0>(pl, a, stream);
+    default: return launch<qgemm::FMT_FP4, 0>(pl, a, stream);
+  }
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -462,15 +510,12 @@ extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, con
   a.N = (int)p->N;
   a.K = (int)p->K;
   a.out_dtype = p->out_dtype;
-  a.group_size = p->group_size;
   a.splits = pl.splits;
   a.kb_per_split = pl.kb_per_split;
   a.tiles_n = (int)((p->N + pl.bn - 1) / (pl.bn ? pl.bn : 1));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fmt == FMT_INT4 ? launch<FMT_INT4>(pl, a, s)
-               : fmt == FMT_FP8  ? launch<FMT_FP8>(pl, a, s)
-                                 : launch<FMT_FP4>(pl, a, s);
+  const hipError_t e = launch_any(pl, p->group_size, a, s);
   if (e != hipSuccess) return fail(QGEMM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return QGEMM_OK;
 }
