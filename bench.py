@@ -108,6 +108,26 @@ def time_graph(torch, g, reps=1):
     return e0.elapsed_time(e1) / reps        # ms
 
 
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter summary, if it still applies.
+
+    The summary records the kernel source hash it was measured with; a changed kernel makes
+    the figure stale, and then None is reported.
+    """
+    import hashlib
+    src = os.path.join(ROOT, "weight_only_quantized_qgemm_amd", "csrc", "qgemm_kernels.hip")
+    prof = os.path.join(ROOT, "profiles", "qgemm_decode_int4_traffic.txt")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        text = open(prof).read()
+    except OSError:
+        return None
+    rec_sha = text.split("Kernel source sha256[:16]:", 1)[1].split()[0] if "Kernel source sha256[:16]:" in text else ""
+    if rec_sha != sha or "traffic_bytes_per_launch =" not in text:
+        return None
+    return int(text.split("traffic_bytes_per_launch =", 1)[1].split()[0])
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (dequant in fp32 + fp64 matmul) on the decode step, timed on the host."""
     import synthetic
@@ -148,6 +168,10 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the FP8 and FP4 workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-mb", type=int, default=1024)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="for rocprofv3 --pmc: run each decode GEMM 20 times eagerly, print nothing else")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="for rocprofv3 --pmc: copy a MIB-sized device buffer 5 times (known traffic)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the GEMM shards by "
@@ -163,6 +187,16 @@ def main():
     torch.cuda.init()
     rot = args.rotate_mb << 20
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": 5}))
+        return
+
     wi = synthetic.WORKLOAD_INDEX["int4_decode"]
     log("bench: preparing decode workload")
     gemms = [Gemm(q, torch, "int4", M, N, K, 128, (wi, si), rot // 2) for si, (M, N, K) in enumerate(DECODE_SHAPES)]
@@ -170,6 +204,15 @@ def main():
     def step():
         for g in gemms:
             g.launch()
+
+    if args.counter_pass:
+        for g in gemms:
+            for _ in range(20):
+                g.launch()
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": [f"int4 M={g.M} N={g.N} K={g.K}" for g in gemms],
+                          "launches_each": 20, "weight_bytes": [g.wbytes for g in gemms]}))
+        return
 
     step_bytes = sum(g.wbytes for g in gemms)
     # warmup: eager steps, then a captured graph of exactly `steps` steps
@@ -254,7 +297,7 @@ def main():
                                "M in {1,16} x (N,K) in {(4096,4096),(11008,4096)}; rotating weight copies",
                    "gemms_per_step": 4, "weight_bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "qgemm_decode (int4)", "avg_launch_us": round(avg_launch_us, 3),
                      "algorithmic_bytes_per_launch": avg_bytes},
         "cpu_baseline": cpu,

@@ -146,8 +146,8 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->tile_elems = pl->cb * 256;
   } else {
     pl->kind = KIND_PREFILL;
-    pl->bm = 128;
-    pl->bn = 128;
+    pl->bm = kPrefillBM;
+    pl->bn = kPrefillBN;
     const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
     int s = 1;
     while ((int64_t)mt * nt * s < kCUs && s * 2 <= kblocks / 4) s *= 2;

@@ -8,6 +8,17 @@
 
 namespace qgemm {
 
+// Prefill kernel shape: a WGM x WGN grid of wavefronts, each owning TM x TN MFMA tiles
+// of 16 x 16 (overridable at build time for tile sweeps).
+#ifndef QGEMM_PF_WGM
+#define QGEMM_PF_WGM 2
+#define QGEMM_PF_WGN 2
+#define QGEMM_PF_TM 4
+#define QGEMM_PF_TN 4
+#endif
+constexpr int kPrefillBM = 16 * QGEMM_PF_WGM * QGEMM_PF_TM;
+constexpr int kPrefillBN = 16 * QGEMM_PF_WGN * QGEMM_PF_TN;
+
 enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
 enum Kind : int { KIND_DECODE = 1, KIND_PREFILL = 2 };
 

@@ -214,7 +214,7 @@ __device__ __forceinline__ f32x4 load_dev(const float* p) {
   return v;
 }
 
-template <int NF>
+template <int NF, int NT = 256>
 __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -222,7 +222,7 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
   if (active) {
     float* mine = base + (size_t)split * tile_elems;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) store_dev(mine + 4 * (f * 256 + tid), v[f]);
+    for (int f = 0; f < NF; ++f) store_dev(mine + 4 * (f * NT + tid), v[f]);
   }
   __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores are complete
   __syncthreads();
@@ -238,7 +238,7 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
     for (int s = 0; s < a.splits; ++s) {
       const float* p = base + (size_t)s * tile_elems;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) v[f] += load_dev(p + 4 * (f * 256 + tid));
+      for (int f = 0; f < NF; ++f) v[f] += load_dev(p + 4 * (f * NT + tid));
     }
   }
   if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -324,99 +324,128 @@ __global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
 }
 
 // ============================================================================= prefill
-// Workgroup tile 128 x 128, 4 wavefronts in 2 x 2, each 64 x 64 (4 x 4 MFMA tiles).
-// Per 128-wide k block: the A tile is staged through LDS (rows padded by 16 bytes against
-// bank conflicts); each wavefront loads its own packed weight fragments straight into
-// registers and dequantizes them once per K step, reusing them across its 4 row tiles.
-constexpr int PF_BM = 128, PF_BN = 128, PF_LDA = 128 + 8;
+// Workgroup = WGM x WGN wavefronts; each wavefront owns TM x TN MFMA tiles (16 x 16), so
+// the workgroup tile is (16 WGM TM) x (16 WGN TN); one 128-wide k block per step.  A is
+// staged through LDS in two buffers (rows padded by 16 bytes against bank conflicts) so
+// one barrier per k block suffices; each wavefront loads its own packed weight fragments
+// straight into registers and dequantizes each once per K step, reusing it for its TM row
+// tiles.  The next k block's A tile and weight fragments are loaded while the current one
+// is computed.  Rows at or beyond M and column blocks at or beyond N/16 are loaded from
+// the last valid row / block (never stored), so the loop has no masking.
+constexpr int PF_LDA = 128 + 8;
 
-template <int FMT, int G>
-__global__ __launch_bounds__(256) void qgemm_prefill(KArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[PF_BM * PF_LDA];
+template <int FMT, int G, int WGM, int WGN, int TM, int TN>
+__global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
+  constexpr int NT = 64 * WGM * WGN;                 // threads
+  constexpr int BM = 16 * WGM * TM, BN = 16 * WGN * TN;
+  constexpr int STAGE = BM * PF_LDA;                 // halves per LDS buffer
+  constexpr int CH = BM * 16 / NT;                   // 16-byte A chunks per thread per k block
+  static_assert(CH * NT == BM * 16, "A tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
-  const int m0 = tm * PF_BM, n0 = tn * PF_BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int KB = a.K >> 7, NB = a.N >> 4;
   const int kb_begin = split * a.kb_per_split;
   const int kb_end = min(KB, kb_begin + a.kb_per_split);
 
-  f32x4 acc[4][4];
+  const uint16_t* arow[CH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < CH; ++i) {
+    const int q = tid + NT * i;
+    const int m = min(m0 + (q >> 4), a.M - 1);
+    arow[i] = a.A + (size_t)m * a.K + 8 * (q & 15);
+  }
+  int nbw[TN];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < TN; ++j) nbw[j] = min((n0 >> 4) + TN * wn + j, NB - 1);
 
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 stage[CH];
+  WFrag<FMT> wf[TN], wnext[TN];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) stage[i] = *reinterpret_cast<const u32x4*>(arow[i] + (size_t)kb_begin * 128);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) load_wfrag<FMT, G>(a, nbw[j], kb_begin, lane, wf[j]);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int q = tid + NT * i;
+    *reinterpret_cast<u32x4*>(As + (q >> 4) * PF_LDA + 8 * (q & 15)) = stage[i];
+  }
+  __syncthreads();
+
+  int cur = 0;
   for (int kb = kb_begin; kb < kb_end; ++kb) {
-    // global -> registers: A tile 128 rows x 128 k = 2048 chunks of 16 bytes, 8 per thread
-    u32x4 areg[8];
+    const bool more = kb + 1 < kb_end;
+    if (more) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i;
-      const int r = q >> 4, c8 = q & 15;
-      const int m = m0 + r;
-      areg[i] = m < a.M ? *reinterpret_cast<const u32x4*>(a.A + (size_t)m * a.K + (size_t)kb * 128 + 8 * c8)
-                        : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < CH; ++i) stage[i] = *reinterpret_cast<const u32x4*>(arow[i] + (size_t)(kb + 1) * 128);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) load_wfrag<FMT, G>(a, nbw[j], kb + 1, lane, wnext[j]);
     }
-    WFrag<FMT> wf[4];
+    const uint16_t* Ab = As + cur * STAGE + (16 * TM * wm + (lane & 15)) * PF_LDA + 8 * (lane >> 4);
+    float fs[TN][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = (n0 >> 4) + 4 * wn + j;
-      if (nb < NB) load_wfrag<FMT, G>(a, nb, kb, lane, wf[j]);
-    }
-    __syncthreads();   // previous k block's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i;
-      const int r = q >> 4, c8 = q & 15;
-      *reinterpret_cast<u32x4*>(As + r * PF_LDA + 8 * c8) = areg[i];
-    }
-    __syncthreads();
-    float fs[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) fs[j][t] = 0.f;
       if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[j].s[0], fs[j]);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      u32x4 b[4];
+      u32x4 b[TN];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = bfrag<FMT>(wf[j], t, fs[j]);
+      for (int j = 0; j < TN; ++j) b[j] = bfrag<FMT>(wf[j], t, fs[j]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(As + (64 * wm + 16 * i + (lane & 15)) * PF_LDA + 32 * t + 8 * (lane >> 4));
+      for (int i = 0; i < TM; ++i) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(Ab + 16 * i * PF_LDA + 32 * t);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<FMT>(af, b[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma<FMT>(af, b[j], acc[i][j]);
       }
     }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int q = tid + NT * i;
+        *reinterpret_cast<u32x4*>(As + (cur ^ 1) * STAGE + (q >> 4) * PF_LDA + 8 * (q & 15)) = stage[i];
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) wf[j] = wnext[j];
+    }
+    __syncthreads();
+    cur ^= 1;
   }
 
-  f32x4 v[16];
+  f32x4 v[TM * TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * i + j] = acc[i][j];
+    for (int j = 0; j < TN; ++j) v[TN * i + j] = acc[i][j];
   if (a.splits > 1) {
-    if (!splitk_finish<16>(a, tile, split, PF_BM * PF_BN, true, v)) return;
+    if (!splitk_finish<TM * TN, NT>(a, tile, split, BM * BN, true, v)) return;
   }
   const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < TN; ++j) {
+    const int nb = (n0 >> 4) + TN * wn + j;
+    if (nb >= NB) continue;
+    const int n = nb * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = (n0 >> 4) + 4 * wn + j;
-      if (nb >= NB) continue;
-      const int n = nb * 16 + (lane & 15);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[4 * i + j][r] : v[4 * i + j][r] * alpha);
+        const int m = m0 + 16 * TM * wm + 16 * i + 4 * (lane >> 4) + r;
+        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[TN * i + j][r] : v[TN * i + j][r] * alpha);
       }
-    }
+  }
 }
 
 // ----------------------------------------------------------------------------- launch
@@ -429,7 +458,7 @@ template <int FMT, int G>
 hipError_t launch(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
   const dim3 grid(pl.grid_x, pl.grid_y);
   if (pl.kind == qgemm::KIND_PREFILL) {
-    hipLaunchKernelGGL((qgemm_prefill<FMT, G>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G, QGEMM_PF_WGM, QGEMM_PF_WGN, QGEMM_PF_TM, QGEMM_PF_TN>), grid, dim3(64 * QGEMM_PF_WGM * QGEMM_PF_WGN), 0, stream, a);
   } else {
     switch (pl.cb * 16 + pl.kpw) {
       case 16 + 8: launch_decode<FMT, G, 1, 8>(grid, a, stream); break;
