@@ -124,22 +124,35 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
   const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
   if (decode) {
     pl->kind = KIND_DECODE;
-    // Column blocks per workgroup.  Every workgroup reads its K slice of A, so wider
-    // workgroups cut A re-reads when M > 1; at M = 1, A is a few KiB and one block (the
-    // most workgroups) is best.
-    pl->cb = p->tile_hint ? p->tile_hint : (p->M == 1 ? 1 : 4);
+    // A is staged in LDS (at most 32 KiB per workgroup) when M is small: the MFMA fragment
+    // loads would otherwise fetch each A value many times.  With larger M the rows are
+    // distinct and fragments are loaded directly.
+    pl->astage = p->M <= 4;
+    // Column blocks per workgroup: wider workgroups cut A re-reads when M > 1.
+    pl->cb = p->tile_hint ? p->tile_hint : (p->M == 1 ? 1 : (p->M <= 4 ? 2 : 4));
     const int groups = ceil_div(nblocks, pl->cb);
-    // Split K until the grid covers every compute unit, keeping >= 4 k blocks per slice
-    // (one per wavefront).
+    // K is split only when needed to bound the staged A slice, or when the output alone
+    // gives fewer than 128 workgroups (a split-K hand-off costs three dependent memory
+    // round trips); every wavefront keeps at least one k block.
+    const int max_kb = pl->astage ? (int)((32 * 1024) / (2 * 128 * p->M)) : kblocks;
     int s = 1;
-    while (groups * s < kCUs && kblocks / (s * 2) >= 4) s *= 2;
+    while (ceil_div(kblocks, s) > max_kb) ++s;
+    while (groups * s < kCUs / 2 && kblocks / (s * 2) >= kDecodeWaves) s *= 2;
     pl->splits = s;
     finish_split(pl, kblocks, p->split_k_hint);
-    // k blocks per wavefront run: up to 8 weight blocks in flight per wavefront, and
-    // enough runs that all four wavefronts of the workgroup get work.
+    if (pl->kb_per_split > max_kb)
+      return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d leaves %d k blocks per slice; the decode kernel "
+                  "stages at most %d at M=%lld", p->split_k_hint, pl->kb_per_split, max_kb, (long long)p->M);
+    // Each wavefront owns ceil(kb_per_split / waves) consecutive k blocks, streamed in runs
+    // of KPW (at most 8 weight blocks in flight per wavefront).
+    const int share = ceil_div(pl->kb_per_split, kDecodeWaves);
+    const int cap = 8 / pl->cb;
     pl->kpw = 1;
-    for (int k = 8; k >= 1; k /= 2)
-      if (pl->cb * k <= 8 && 4 * k <= pl->kb_per_split) { pl->kpw = k; break; }
+    if (share <= cap && (share == 8 || share == 5 || share == 4 || share == 2 || share == 1) && (pl->cb == 1 || share != 5))
+      pl->kpw = share;
+    else
+      for (int k = cap; k >= 1; k /= 2)
+        if (k <= share) { pl->kpw = k; break; }
     pl->grid_x = (unsigned)groups;
     pl->grid_y = (unsigned)pl->splits;
     pl->tiles = groups;

@@ -16,6 +16,11 @@ namespace qgemm {
 #define QGEMM_PF_TM 4
 #define QGEMM_PF_TN 4
 #endif
+// Decode kernel: wavefronts per workgroup.
+#ifndef QGEMM_DEC_NW
+#define QGEMM_DEC_NW 8
+#endif
+constexpr int kDecodeWaves = QGEMM_DEC_NW;
 constexpr int kPrefillBM = 16 * QGEMM_PF_WGM * QGEMM_PF_TM;
 constexpr int kPrefillBN = 16 * QGEMM_PF_WGN * QGEMM_PF_TN;
 
@@ -36,6 +41,7 @@ struct Plan {
   Format fmt;
   // decode: column blocks (16 columns each) per workgroup, k blocks per wavefront run
   int cb, kpw;
+  bool astage;            // decode: stage the A slice in LDS (small M)
   // prefill: workgroup tile
   int bm, bn;
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers

@@ -63,12 +63,20 @@ struct KArgs {
 };
 
 // ----------------------------------------------------------------------------- dequant
+// (a & m) | o in one VALU op.  The compiler splits it into AND + OR because the two
+// constants cannot both be instruction operands; as VGPR operands they can.
+__device__ __forceinline__ unsigned and_or(unsigned a, unsigned m, unsigned o) {
+  unsigned r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
 __device__ __forceinline__ u32x4 dq_int4(unsigned w, unsigned s2) {
   const unsigned hi = w >> 8;
-  const unsigned p0 = (w & 0x000F000Fu) | 0x64006400u;    // k slots j0, j1: 1024 + nibble
-  const unsigned p1 = (w & 0x00F000F0u) | 0x54005400u;    // j2, j3: 64 + nibble
-  const unsigned p2 = (hi & 0x000F000Fu) | 0x64006400u;   // j4, j5
-  const unsigned p3 = (hi & 0x00F000F0u) | 0x54005400u;   // j6, j7
+  const unsigned p0 = and_or(w, 0x000F000Fu, 0x64006400u);    // k slots j0, j1: 1024 + nibble
+  const unsigned p1 = and_or(w, 0x00F000F0u, 0x54005400u);    // j2, j3: 64 + nibble
+  const unsigned p2 = and_or(hi, 0x000F000Fu, 0x64006400u);   // j4, j5
+  const unsigned p3 = and_or(hi, 0x00F000F0u, 0x54005400u);   // j6, j7
   const f16x2 s = __builtin_bit_cast(f16x2, s2);
   const f16x2 big = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 small = {(_Float16)72.0f, (_Float16)72.0f};
@@ -119,11 +127,14 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Weights + scales of one (column block, 128-wide k block) as seen by one lane.
+// Weights + scales of one (column block, 128-wide k block) as seen by one lane.  Scales
+// are kept as loaded (raw bits) and expanded only where they are used, so that nothing
+// consumes a load before the MFMA loop does (a consumer forces a wait for every load
+// issued before it).
 template <int FMT>
 struct WFrag {
   u32x4 w[FMT == qgemm::FMT_FP8 ? 2 : 1];
-  unsigned s[4];    // INT4: fp16 scale pair per K step; FP4: 4 scale bytes (one dword)
+  unsigned s[2];    // INT4: 1, 2 or 4 fp16 scales (G = 128|256, 64, 32); FP4: 4 e4m3 bytes
 };
 
 // G is the INT4 group size (a template parameter, so the scale load has no branches:
@@ -145,23 +156,17 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
     if constexpr (G <= 128) {
       constexpr int T = 128 / G;
       const size_t base = ((size_t)nb * KB + kb) * 16 * T + (size_t)c * T;
-      unsigned v[4];
       if constexpr (T == 4) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(S + base);
-        v[0] = x[0] & 0xFFFFu; v[1] = x[0] >> 16; v[2] = x[1] & 0xFFFFu; v[3] = x[1] >> 16;
+        f.s[0] = x[0];
+        f.s[1] = x[1];
       } else if constexpr (T == 2) {
-        const unsigned x = *reinterpret_cast<const unsigned*>(S + base);
-        v[0] = v[1] = x & 0xFFFFu;
-        v[2] = v[3] = x >> 16;
+        f.s[0] = *reinterpret_cast<const unsigned*>(S + base);
       } else {
-        v[0] = v[1] = v[2] = v[3] = S[base];
+        f.s[0] = S[base];
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) f.s[t] = v[t] | (v[t] << 16);
     } else {   // G == 256: one scale per two k blocks
-      const unsigned x = S[((size_t)nb * (KB >> 1) + (kb >> 1)) * 16 + c];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) f.s[t] = x | (x << 16);
+      f.s[0] = S[((size_t)nb * (KB >> 1) + (kb >> 1)) * 16 + c];
     }
   } else if constexpr (FMT == qgemm::FMT_FP4) {
     const uint8_t* S = static_cast<const uint8_t*>(a.S);
@@ -169,11 +174,21 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
   }
 }
 
+// fp16 scale of K step t, duplicated into both halves (INT4).
+template <int G>
+__device__ __forceinline__ unsigned int4_scale_pair(const unsigned (&s)[2], int t) {
+  unsigned h;
+  if constexpr (G == 32) h = (t & 1) ? (s[t >> 1] >> 16) : (s[t >> 1] & 0xFFFFu);
+  else if constexpr (G == 64) h = (t >> 1) ? (s[0] >> 16) : (s[0] & 0xFFFFu);
+  else h = s[0] & 0xFFFFu;
+  return h | (h << 16);
+}
+
 // The B operand (dequantized weights) of K step t.
-template <int FMT>
+template <int FMT, int G>
 __device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (&fs)[4]) {
   if constexpr (FMT == qgemm::FMT_INT4) {
-    return dq_int4(f.w[0][t], f.s[t]);
+    return dq_int4(f.w[0][t], int4_scale_pair<G>(f.s, t));
   } else if constexpr (FMT == qgemm::FMT_FP8) {
     return dq_fp8(f.w[t >> 1][2 * (t & 1)], f.w[t >> 1][2 * (t & 1) + 1]);
   } else {
@@ -246,18 +261,30 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
 }
 
 // ============================================================================= decode
-// M <= 16.  Workgroup = 4 wavefronts; it owns CB column blocks (16 columns each) and one
-// K slice.  Wavefront w streams contiguous runs of KPW k blocks (run r starts at k block
-// begin + (4 r + w) KPW).  Per run, the A fragments are loaded first, then every weight and
-// scale load of the run, and only then is anything consumed: loads complete in issue order,
-// so waiting for A never waits for the weight stream.  Rows of A at or beyond M are read
-// from row M - 1 instead of being masked: MFMA output row m depends on A row m only, and
-// rows >= M are never stored.  All control flow is wavefront-uniform (scalar branches);
-// loads past the end of the slice are clamped to its last k block and their results unused.
-// Each wavefront accumulates one 16 x 16 MFMA tile per column block; the four tiles are
-// summed through LDS in wave order, then split-K or the epilogue follows.
-template <int FMT, int G, int CB, int KPW>
-__global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
+// M <= 16.  Workgroup = NW wavefronts; it owns CB column blocks (16 columns each) and one
+// K slice (normally all of K: a split-K hand-off costs three dependent memory round trips,
+// more than a whole small GEMM).  Wavefront w owns a contiguous share of the slice's k
+// blocks, streamed in runs of up to KPW blocks: all weight and scale loads of a run are
+// issued before any is consumed, and the k blocks are then consumed in load order, so each
+// waits only for its own data.
+// A fragments: with ASTAGE (small M) every thread first loads distinct 16-byte chunks of the
+// A slice (M rows, at most 32 KiB) into LDS, because a wave's fragment loads would otherwise
+// fetch each A value 16 times; otherwise (rows all distinct) each wavefront loads its
+// fragments from global memory before the run's weights.  Rows at or beyond M read row
+// M - 1 (MFMA output row m depends on A row m only; rows >= M are never stored).
+// Control flow is wavefront-uniform and loads are clamped rather than predicated (the
+// compiler waits for every outstanding load at the end of a branch that contains one).
+// Each wavefront keeps two accumulators per column block (even / odd K steps) to halve the
+// MFMA dependency chain; the NW wavefront tiles are summed through LDS in wave order.
+constexpr int DEC_A_CHUNKS = 2048;                  // 32 KiB of staged A per workgroup
+constexpr bool DEC_ACC2 = true;                     // two accumulators per column block
+
+template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE>
+__global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int SCH = ASTAGE ? DEC_A_CHUNKS / NT : 1;   // staging chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t a_lds[ASTAGE ? DEC_A_CHUNKS * 8 + 16 * 8 : 8];
+  __shared__ f32x4 red[NW][CB][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = blockIdx.x, split = blockIdx.y;
@@ -265,53 +292,115 @@ __global__ __launch_bounds__(256) void qgemm_decode(KArgs a) {
   const int kb_begin = split * a.kb_per_split;
   const int kb_end = min(KB, kb_begin + a.kb_per_split);
   const int nb0 = group * CB;
+  const int kslice = (kb_end - kb_begin) * 128;     // halves per A row in this slice
+  const int lda = kslice + 8;                        // LDS row stride (halves)
+  // this wavefront's contiguous share of the slice
+  const int share = (kb_end - kb_begin + NW - 1) / NW;
+  const int w_begin = min(kb_end, kb_begin + wave * share);
+  const int w_end = min(kb_end, w_begin + share);
   const int row = min(lane & 15, a.M - 1);
-  const uint16_t* arow = a.A + (size_t)row * a.K + 8 * (lane >> 4);
 
-  f32x4 acc[CB];
+  int soff[SCH];
+  u32x4 stage[SCH];
+  if constexpr (ASTAGE) {
+    const int cpr = kslice >> 3;                     // 16-byte chunks per row
+    const int chunks = a.M * cpr;                    // <= DEC_A_CHUNKS by the launch plan
+    const float inv_cpr = 1.0f / (float)cpr;
 #pragma unroll
-  for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < SCH; ++i) {                  // no branch around a load: surplus threads re-load the last chunk
+      const int q = tid + NT * i;
+      const int qq = min(q, chunks - 1);
+      const int r = (int)(((float)qq + 0.5f) * inv_cpr);
+      const int c8 = qq - r * cpr;
+      stage[i] = *reinterpret_cast<const u32x4*>(a.A + (size_t)r * a.K + (size_t)kb_begin * 128 + 8 * c8);
+      soff[i] = q < chunks ? r * lda + 8 * c8 : -1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-  for (int run = kb_begin + wave * KPW; run < kb_end; run += 4 * KPW) {
-    u32x4 afr[KPW][4];
-    WFrag<FMT> wf[KPW][CB];
+  f32x4 acc[CB][2];
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      const int kb = min(run + u, kb_end - 1);
-      const u32x4* ap = reinterpret_cast<const u32x4*>(arow + (size_t)kb * 128);
+  for (int c = 0; c < CB; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* arow_g = a.A + (size_t)row * a.K + 8 * (lane >> 4);
+  const uint16_t* arow_l = a_lds + row * lda + 8 * (lane >> 4);
+  const int last = max(w_end - 1, w_begin);          // clamp target (valid even for an empty share)
+  const int kb_cap = min(last, KB - 1);
+
+  // one run: loads first (A fragments, then weights and scales), then the k blocks in
+  // load order, each waiting only for its own data
+  auto run_loads = [&](int run, u32x4 (&afr)[ASTAGE ? 1 : KPW][4], WFrag<FMT> (&wf)[KPW][CB]) {
+    if constexpr (!ASTAGE) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) afr[u][t] = ap[4 * t];
+      for (int u = 0; u < KPW; ++u) {
+        const u32x4* ap = reinterpret_cast<const u32x4*>(arow_g + (size_t)min(run + u, kb_cap) * 128);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) afr[u][t] = ap[4 * t];
+      }
     }
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      const int kb = min(run + u, kb_end - 1);
+    for (int u = 0; u < KPW; ++u)
 #pragma unroll
-      for (int c = 0; c < CB; ++c) load_wfrag<FMT, G>(a, min(nb0 + c, NB - 1), kb, lane, wf[u][c]);
-    }
+      for (int c = 0; c < CB; ++c) load_wfrag<FMT, G>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run_compute = [&](int run, const u32x4 (&afr)[ASTAGE ? 1 : KPW][4], const WFrag<FMT> (&wf)[KPW][CB]) {
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
-      if (run + u < kb_end) {
+      if (run + u < w_end) {
+        u32x4 al[4];
+        if constexpr (ASTAGE) {
+          const uint16_t* ap = arow_l + (run + u - kb_begin) * 128;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const u32x4*>(ap + 32 * t);
+        }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
           float fs[4] = {0.f, 0.f, 0.f, 0.f};
           if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[c] = mfma<FMT>(afr[u][t], bfrag<FMT>(wf[u][c], t, fs), acc[c]);
+          for (int t = 0; t < 4; ++t) {
+            const u32x4 av = ASTAGE ? al[t] : afr[ASTAGE ? 0 : u][t];
+            acc[c][DEC_ACC2 ? (t & 1) : 0] = mfma<FMT>(av, bfrag<FMT, G>(wf[u][c], t, fs), acc[c][DEC_ACC2 ? (t & 1) : 0]);
+          }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  {   // first run: every wavefront, with or without k blocks, also stages A and syncs
+    u32x4 afr[ASTAGE ? 1 : KPW][4];
+    WFrag<FMT> wf[KPW][CB];
+    run_loads(w_begin, afr, wf);
+    if constexpr (ASTAGE) {
+#pragma unroll
+      for (int i = 0; i < SCH; ++i)
+        if (soff[i] >= 0) *reinterpret_cast<u32x4*>(a_lds + soff[i]) = stage[i];
+      __syncthreads();
+    }
+    if (w_begin < w_end) run_compute(w_begin, afr, wf);
+  }
+  for (int run = w_begin + KPW; run < w_end; run += KPW) {
+    u32x4 afr[ASTAGE ? 1 : KPW][4];
+    WFrag<FMT> wf[KPW][CB];
+    run_loads(run, afr, wf);
+    run_compute(run, afr, wf);
   }
 
-  __shared__ f32x4 red[4][CB][64];
 #pragma unroll
-  for (int c = 0; c < CB; ++c) red[wave][c][lane] = acc[c];
+  for (int c = 0; c < CB; ++c) red[wave][c][lane] = DEC_ACC2 ? acc[c][0] + acc[c][1] : acc[c][0];
   __syncthreads();
   const bool active = tid < CB * 64;
   const int c = tid >> 6, ln = tid & 63;
   f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (active) v[0] = ((red[0][c][ln] + red[1][c][ln]) + red[2][c][ln]) + red[3][c][ln];
+  if (active) {
+    v[0] = red[0][c][ln];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v[0] += red[w][c][ln];
+  }
   if (a.splits > 1) {
-    if (!splitk_finish<1>(a, group, split, CB * 256, active, v)) return;
+    if (!splitk_finish<1, NT>(a, group, split, CB * 256, active, v)) return;
   }
   if (!active || nb0 + c >= NB) return;
   const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
@@ -403,7 +492,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     for (int t = 0; t < 4; ++t) {
       u32x4 b[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = bfrag<FMT>(wf[j], t, fs[j]);
+      for (int j = 0; j < TN; ++j) b[j] = bfrag<FMT, G>(wf[j], t, fs[j]);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const u32x4 af = *reinterpret_cast<const u32x4*>(Ab + 16 * i * PF_LDA + 32 * t);
@@ -450,26 +539,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 
 // ----------------------------------------------------------------------------- launch
 template <int FMT, int G, int CB, int KPW>
-void launch_decode(const dim3& grid, const KArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW>), grid, dim3(256), 0, stream, a);
+void launch_decode(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
+  const dim3 grid(pl.grid_x, pl.grid_y);
+  if (pl.astage)
+    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, true>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, false>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
 }
 
 template <int FMT, int G>
 hipError_t launch(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
-  const dim3 grid(pl.grid_x, pl.grid_y);
   if (pl.kind == qgemm::KIND_PREFILL) {
-    hipLaunchKernelGGL((qgemm_prefill<FMT, G, QGEMM_PF_WGM, QGEMM_PF_WGN, QGEMM_PF_TM, QGEMM_PF_TN>), grid, dim3(64 * QGEMM_PF_WGM * QGEMM_PF_WGN), 0, stream, a);
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G, QGEMM_PF_WGM, QGEMM_PF_WGN, QGEMM_PF_TM, QGEMM_PF_TN>),
+                       dim3(pl.grid_x, pl.grid_y), dim3(64 * QGEMM_PF_WGM * QGEMM_PF_WGN), 0, stream, a);
   } else {
     switch (pl.cb * 16 + pl.kpw) {
-      case 16 + 8: launch_decode<FMT, G, 1, 8>(grid, a, stream); break;
-      case 16 + 4: launch_decode<FMT, G, 1, 4>(grid, a, stream); break;
-      case 16 + 2: launch_decode<FMT, G, 1, 2>(grid, a, stream); break;
-      case 16 + 1: launch_decode<FMT, G, 1, 1>(grid, a, stream); break;
-      case 32 + 4: launch_decode<FMT, G, 2, 4>(grid, a, stream); break;
-      case 32 + 2: launch_decode<FMT, G, 2, 2>(grid, a, stream); break;
-      case 32 + 1: launch_decode<FMT, G, 2, 1>(grid, a, stream); break;
-      case 64 + 2: launch_decode<FMT, G, 4, 2>(grid, a, stream); break;
-      case 64 + 1: launch_decode<FMT, G, 4, 1>(grid, a, stream); break;
+      case 16 + 8: launch_decode<FMT, G, 1, 8>(pl, a, stream); break;
+      case 16 + 5: launch_decode<FMT, G, 1, 5>(pl, a, stream); break;
+      case 16 + 4: launch_decode<FMT, G, 1, 4>(pl, a, stream); break;
+      case 16 + 2: launch_decode<FMT, G, 1, 2>(pl, a, stream); break;
+      case 16 + 1: launch_decode<FMT, G, 1, 1>(pl, a, stream); break;
+      case 32 + 4: launch_decode<FMT, G, 2, 4>(pl, a, stream); break;
+      case 32 + 2: launch_decode<FMT, G, 2, 2>(pl, a, stream); break;
+      case 32 + 1: launch_decode<FMT, G, 2, 1>(pl, a, stream); break;
+      case 64 + 2: launch_decode<FMT, G, 4, 2>(pl, a, stream); break;
+      case 64 + 1: launch_decode<FMT, G, 4, 1>(pl, a, stream); break;
       default: return hipErrorInvalidConfiguration;
     }
   }
