@@ -126,6 +126,18 @@ def test_split_k_and_kernel_hints(q, fmt, M, hint, split, tile):
     check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, tile_hint=tile)
 
 
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("tile,split", [(128, 1), (128, 3), (256, 1), (256, 3)])
+def test_prefill_tile_shapes(q, fmt, G, tile, split):
+    # Both prefill workgroup shapes on every format: 600 rows are ragged against 128- and
+    # 256-row tiles, 784 columns (49 column blocks) against 256-column tiles; 8 k blocks.
+    M, N, K = 600, 784, 1024
+    say(f"case prefill-tile fmt={fmt} G={G} tile={tile} split={split}")
+    prep = Prepared(q, fmt, N, K, G or 0, (53, N, K))
+    A = _act(fmt, M, K, (53, M))
+    check_against_oracle(q, prep, A, kernel_hint=2, split_k_hint=split, tile_hint=tile)
+
+
 @pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
 @pytest.mark.parametrize("M", [16, 256])
 def test_deterministic_and_counters_reset(q, fmt, M):

@@ -97,8 +97,9 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
   const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
   if (decode && p->tile_hint != 0 && p->tile_hint != 1 && p->tile_hint != 2 && p->tile_hint != 4)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the decode kernel must be 0, 1, 2 or 4, got %d", p->tile_hint);
-  if (!decode && p->tile_hint != 0)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the prefill kernel must be 0, got %d", p->tile_hint);
+  if (!decode && p->tile_hint != 0 && p->tile_hint != pf_bm(kPfMedium) && p->tile_hint != pf_bm(kPfLarge))
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the prefill kernel must be 0, %d or %d, got %d",
+                pf_bm(kPfMedium), pf_bm(kPfLarge), p->tile_hint);
   return QGEMM_OK;
 }
 
@@ -159,8 +160,15 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->tile_elems = pl->cb * 256;
   } else {
     pl->kind = KIND_PREFILL;
-    pl->bm = kPrefillBM;
-    pl->bn = kPrefillBN;
+    // The large tile once M fills at least two of its row tiles.
+    const bool large = p->tile_hint ? p->tile_hint == pf_bm(kPfLarge) : p->M >= 2 * pf_bm(kPfLarge);
+    const PfShape sh = large ? kPfLarge : kPfMedium;
+    pl->bm = pf_bm(sh);
+    pl->bn = pf_bn(sh);
+    // the A tile is addressed with 32-bit byte offsets
+    if ((int64_t)pl->bm * p->K * 2 > 0x7fffffffLL)
+      return fail(QGEMM_ERR_UNSUPPORTED, "the prefill kernel needs %d * K * 2 < 2^31 (K = %lld)", pl->bm,
+                  (long long)p->K);
     const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
     int s = 1;
     while ((int64_t)mt * nt * s < kCUs && s * 2 <= kblocks / 4) s *= 2;

@@ -8,21 +8,24 @@
 
 namespace qgemm {
 
-// Prefill kernel shape: a WGM x WGN grid of wavefronts, each owning TM x TN MFMA tiles
-// of 16 x 16 (overridable at build time for tile sweeps).
-#ifndef QGEMM_PF_WGM
-#define QGEMM_PF_WGM 2
-#define QGEMM_PF_WGN 2
-#define QGEMM_PF_TM 4
-#define QGEMM_PF_TN 4
+// Prefill workgroup shapes: one row of eight wavefronts (two per SIMD), each owning
+// TM x TN MFMA tiles of 16 x 16.  The large shape amortises every dequantized weight
+// fragment over 16 row tiles; the medium one halves the rows for small M.
+// RU: row tiles per LDS read unit (A fragments are read one unit ahead of their MFMAs).
+struct PfShape { int wgm, wgn, tm, tn, ru; };
+#ifndef QGEMM_PF_LARGE
+#define QGEMM_PF_LARGE 1, 8, 16, 2, 4
+#define QGEMM_PF_MEDIUM 1, 8, 8, 2, 8
 #endif
+constexpr PfShape kPfLarge{QGEMM_PF_LARGE};    // 256 x 256 output tile
+constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 256 output tile
+constexpr int pf_bm(PfShape s) { return 16 * s.wgm * s.tm; }
+constexpr int pf_bn(PfShape s) { return 16 * s.wgn * s.tn; }
 // Decode kernel: wavefronts per workgroup.
 #ifndef QGEMM_DEC_NW
 #define QGEMM_DEC_NW 8
 #endif
 constexpr int kDecodeWaves = QGEMM_DEC_NW;
-constexpr int kPrefillBM = 16 * QGEMM_PF_WGM * QGEMM_PF_TM;
-constexpr int kPrefillBN = 16 * QGEMM_PF_WGN * QGEMM_PF_TN;
 
 enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
 enum Kind : int { KIND_DECODE = 1, KIND_PREFILL = 2 };
@@ -42,7 +45,7 @@ struct Plan {
   // decode: column blocks (16 columns each) per workgroup, k blocks per wavefront run
   int cb, kpw;
   bool astage;            // decode: stage the A slice in LDS (small M)
-  // prefill: workgroup tile
+  // prefill: workgroup tile (bm == pf_bm(kPfLarge) selects the large shape)
   int bm, bn;
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
   int splits;

@@ -139,16 +139,24 @@ struct WFrag {
 
 // G is the INT4 group size (a template parameter, so the scale load has no branches:
 // a branch around a load ends in a wait for every outstanding load); 0 for FP8 / FP4.
-template <int FMT, int G>
+// STREAM marks weights read once (decode: non-temporal loads keep them out of the way in
+// the caches); prefill re-reads each weight fragment once per row tile and caches it.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 wload(const u32x4* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int FMT, int G, bool STREAM = true>
 __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int lane, WFrag<FMT>& f) {
   const int KB = a.K >> 7;
   if constexpr (FMT == qgemm::FMT_FP8) {
     const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * (KB * 2) + 2 * kb) * 1024) + lane;
-    f.w[0] = __builtin_nontemporal_load(p);
-    f.w[1] = __builtin_nontemporal_load(p + 64);
+    f.w[0] = wload<STREAM>(p);
+    f.w[1] = wload<STREAM>(p + 64);
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * KB + kb) * 1024) + lane;
-    f.w[0] = __builtin_nontemporal_load(p);
+    f.w[0] = wload<STREAM>(p);
   }
   if constexpr (FMT == qgemm::FMT_INT4) {
     const uint16_t* S = static_cast<const uint16_t*>(a.S);
@@ -414,25 +422,45 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
 
 // ============================================================================= prefill
 // Workgroup = WGM x WGN wavefronts; each wavefront owns TM x TN MFMA tiles (16 x 16), so
-// the workgroup tile is (16 WGM TM) x (16 WGN TN); one 128-wide k block per step.  A is
-// staged through LDS in two buffers (rows padded by 16 bytes against bank conflicts) so
-// one barrier per k block suffices; each wavefront loads its own packed weight fragments
-// straight into registers and dequantizes each once per K step, reusing it for its TM row
-// tiles.  The next k block's A tile and weight fragments are loaded while the current one
-// is computed.  Rows at or beyond M and column blocks at or beyond N/16 are loaded from
-// the last valid row / block (never stored), so the loop has no masking.
-constexpr int PF_LDA = 128 + 8;
+// the workgroup tile is (16 WGM TM) x (16 WGN TN); one 128-wide k block per step.
+//
+// A goes from HBM straight into LDS (buffer loads with the LDS-destination bit: no VGPR
+// staging), double-buffered in two separate arrays so that the compiler can tell the
+// buffer being read from the one being filled.  A DMA load writes its 64 lanes' 16 bytes
+// contiguously, so LDS rows cannot be padded; instead the 16-byte chunk c of tile row r
+// is stored at chunk position c ^ (r & 15).  The MFMA A-fragment read (lane l: row l & 15,
+// chunk 4t + l / 16) then touches 16 distinct positions per 16 lanes: no bank conflicts.
+// The buffer resource covers the tile's valid rows only and the row sits in the range-
+// checked per-lane offset (the k block in the scalar offset never leaves its row), so rows
+// at or beyond M read as zero (and are never stored).
+//
+// Each wavefront loads its own packed weight fragments into registers (one k block
+// ahead) and dequantizes each once per K step, reusing it for its TM row tiles; the
+// dequantization of K step t + 1 is issued with the MFMAs of step t.  A fragments are
+// read from LDS in units of RU row tiles, one unit ahead of the MFMAs that consume it.
+// One barrier per k block: step k issues the A and weight loads of block k + 1, computes
+// block k, waits for its own loads and meets the other wavefronts at the barrier.  The
+// loop is unrolled by two so buffers and register sets alternate without copies; every
+// load is unconditional (the last step re-loads its own block, never used) and
+// sched_barrier pins the phase order (a load under a branch, or a consumer scheduled
+// early, would make the wavefront wait for all outstanding loads).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN>
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU>
 __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
-  constexpr int NT = 64 * WGM * WGN;                 // threads
+  constexpr int NW = WGM * WGN;                      // wavefronts
+  constexpr int NT = 64 * NW;                        // threads
   constexpr int BM = 16 * WGM * TM, BN = 16 * WGN * TN;
-  constexpr int STAGE = BM * PF_LDA;                 // halves per LDS buffer
-  constexpr int CH = BM * 16 / NT;                   // 16-byte A chunks per thread per k block
-  static_assert(CH * NT == BM * 16, "A tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int ROWB = 256;                          // bytes of one A row per k block
+  constexpr int NDMA = BM / (4 * NW);                // 1 KiB DMA loads per wavefront per k block
+  constexpr int TU = TM / RU;                        // read units per K step
+  constexpr int NU = 4 * TU;                         // read units per k block
+  static_assert(NDMA * 4 * NW == BM && (4 * NW) % 16 == 0, "A tile must split into whole 4-row DMA loads");
+  static_assert(TU * RU == TM, "RU must divide TM");
+  __shared__ __attribute__((aligned(1024))) unsigned char As0[BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char As1[BM * ROWB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
@@ -441,16 +469,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   const int kb_begin = split * a.kb_per_split;
   const int kb_end = min(KB, kb_begin + a.kb_per_split);
 
-  const uint16_t* arow[CH];
+  // DMA load i of this wavefront fills LDS bytes [(NW i + wave) KiB, +1 KiB): tile rows
+  // 4 (NW i + wave) + lane / 16, chunk position lane & 15.  Since 4 NW is a multiple of 16,
+  // the row's low four bits, and so the swizzled source chunk, do not depend on i.
+  const int drow = 4 * wave + (lane >> 4);
+  const int dchunk = (lane & 15) ^ (drow & 15);
+  const int rows = min(a.M - m0, BM);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.A + (size_t)m0 * a.K), (short)0, rows * a.K * 2, 0x00020000);
+  const int dvoff = drow * a.K * 2 + 16 * dchunk;
+  const int dstride = 4 * NW * a.K * 2;              // bytes between a wavefront's DMA loads
+  auto load_a = [&](int kb, unsigned char* As) {
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int q = tid + NT * i;
-    const int m = min(m0 + (q >> 4), a.M - 1);
-    arow[i] = a.A + (size_t)m * a.K + 8 * (q & 15);
-  }
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(As + (NW * i + wave) * 1024), 16,
+                                               dvoff + i * dstride, kb * ROWB, 0, 0);
+  };
+
+  // A-fragment read offsets, one per K step: row 16 TM wm + 16 i + (l & 15), chunk 4t + l / 16.
+  int aoff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    aoff[t] = (16 * TM * wm + (lane & 15)) * ROWB + 16 * ((4 * t + (lane >> 4)) ^ (lane & 15));
+
   int nbw[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) nbw[j] = min((n0 >> 4) + TN * wn + j, NB - 1);
+  auto load_w = [&](int kb, WFrag<FMT> (&wf)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) load_wfrag<FMT, G, false>(a, nbw[j], kb, lane, wf[j]);
+  };
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -458,29 +506,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 stage[CH];
-  WFrag<FMT> wf[TN], wnext[TN];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) stage[i] = *reinterpret_cast<const u32x4*>(arow[i] + (size_t)kb_begin * 128);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) load_wfrag<FMT, G>(a, nbw[j], kb_begin, lane, wf[j]);
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int q = tid + NT * i;
-    *reinterpret_cast<u32x4*>(As + (q >> 4) * PF_LDA + 8 * (q & 15)) = stage[i];
-  }
-  __syncthreads();
-
-  int cur = 0;
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const bool more = kb + 1 < kb_end;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) stage[i] = *reinterpret_cast<const u32x4*>(arow[i] + (size_t)(kb + 1) * 128);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) load_wfrag<FMT, G>(a, nbw[j], kb + 1, lane, wnext[j]);
-    }
-    const uint16_t* Ab = As + cur * STAGE + (16 * TM * wm + (lane & 15)) * PF_LDA + 8 * (lane >> 4);
+  auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN]) {
     float fs[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -488,29 +514,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
       for (int t = 0; t < 4; ++t) fs[j][t] = 0.f;
       if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[j].s[0], fs[j]);
     }
+    u32x4 af[2][RU];
+    auto read_unit = [&](int u, u32x4 (&dst)[RU]) {
+      const int t = u / TU, i0 = (u % TU) * RU;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 b[TN];
+      for (int r = 0; r < RU; ++r) dst[r] = *reinterpret_cast<const u32x4*>(As + aoff[t] + (i0 + r) * 16 * ROWB);
+    };
+    u32x4 b[2][TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = bfrag<FMT, G>(wf[j], t, fs[j]);
+    for (int j = 0; j < TN; ++j) b[0][j] = bfrag<FMT, G>(wf[j], 0, fs[j]);
+    read_unit(0, af[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(Ab + 16 * i * PF_LDA + 32 * t);
+    for (int u = 0; u < NU; ++u) {
+      const int t = u / TU, i0 = (u % TU) * RU;
+      if (u + 1 < NU) read_unit(u + 1, af[(u + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);   // the next unit's reads go out before this unit's MFMAs
+      if (i0 + RU == TM && t < 3) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma<FMT>(af, b[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) b[(t + 1) & 1][j] = bfrag<FMT, G>(wf[j], t + 1, fs[j]);
       }
-    }
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int q = tid + NT * i;
-        *reinterpret_cast<u32x4*>(As + (cur ^ 1) * STAGE + (q >> 4) * PF_LDA + 8 * (q & 15)) = stage[i];
-      }
+      for (int r = 0; r < RU; ++r)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) wf[j] = wnext[j];
+        for (int j = 0; j < TN; ++j) acc[i0 + r][j] = mfma<FMT>(af[u & 1][r], b[t & 1][j], acc[i0 + r][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  WFrag<FMT> w0[TN], w1[TN];
+  load_a(kb_begin, As0);
+  load_w(kb_begin, w0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
+    // even step: block kb from As0 / w0; loads of block kb + 1 into As1 / w1
+    const int k1 = min(kb + 1, kb_end - 1);
+    load_a(k1, As1);
+    load_w(k1, w1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As0, w0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur ^= 1;
+    if (kb + 1 >= kb_end) break;
+    // odd step: block kb + 1 from As1 / w1; loads of block kb + 2 into As0 / w0
+    const int k2 = min(kb + 2, kb_end - 1);
+    load_a(k2, As0);
+    load_w(k2, w0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As1, w1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   f32x4 v[TM * TN];
@@ -547,11 +602,21 @@ void launch_decode(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, false>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
 }
 
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU>
+void launch_prefill(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU>), dim3(pl.grid_x, pl.grid_y), dim3(64 * WGM * WGN),
+                     0, stream, a);
+}
+
 template <int FMT, int G>
 hipError_t launch(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
   if (pl.kind == qgemm::KIND_PREFILL) {
-    hipLaunchKernelGGL((qgemm_prefill<FMT, G, QGEMM_PF_WGM, QGEMM_PF_WGN, QGEMM_PF_TM, QGEMM_PF_TN>),
-                       dim3(pl.grid_x, pl.grid_y), dim3(64 * QGEMM_PF_WGM * QGEMM_PF_WGN), 0, stream, a);
+    if (pl.bm == qgemm::pf_bm(qgemm::kPfLarge))
+      launch_prefill<FMT, G, qgemm::kPfLarge.wgm, qgemm::kPfLarge.wgn, qgemm::kPfLarge.tm, qgemm::kPfLarge.tn,
+                     qgemm::kPfLarge.ru>(pl, a, stream);
+    else
+      launch_prefill<FMT, G, qgemm::kPfMedium.wgm, qgemm::kPfMedium.wgn, qgemm::kPfMedium.tm, qgemm::kPfMedium.tn,
+                     qgemm::kPfMedium.ru>(pl, a, stream);
   } else {
     switch (pl.cb * 16 + pl.kpw) {
       case 16 + 8: launch_decode<FMT, G, 1, 8>(pl, a, stream); break;
