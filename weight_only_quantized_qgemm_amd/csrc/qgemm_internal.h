@@ -11,11 +11,11 @@ namespace qgemm {
 // Prefill workgroup shapes: one row of eight wavefronts (two per SIMD), each owning
 // TM x TN MFMA tiles of 16 x 16.  The large shape amortises every dequantized weight
 // fragment over 16 row tiles; the medium one halves the rows for small M.
-// RU: row tiles per LDS read unit (A fragments are read one unit ahead of their MFMAs).
-struct PfShape { int wgm, wgn, tm, tn, ru; };
+// RU: row tiles per LDS read unit; LA: units read ahead of the MFMAs that consume them.
+struct PfShape { int wgm, wgn, tm, tn, ru, la; };
 #ifndef QGEMM_PF_LARGE
-#define QGEMM_PF_LARGE 1, 8, 16, 2, 4
-#define QGEMM_PF_MEDIUM 1, 8, 8, 2, 8
+#define QGEMM_PF_LARGE 1, 8, 16, 2, 4, 1
+#define QGEMM_PF_MEDIUM 1, 8, 8, 2, 8, 1
 #endif
 constexpr PfShape kPfLarge{QGEMM_PF_LARGE};    // 256 x 256 output tile
 constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 256 output tile

@@ -437,16 +437,39 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
 // Each wavefront loads its own packed weight fragments into registers (one k block
 // ahead) and dequantizes each once per K step, reusing it for its TM row tiles; the
 // dequantization of K step t + 1 is issued with the MFMAs of step t.  A fragments are
-// read from LDS in units of RU row tiles, one unit ahead of the MFMAs that consume it.
-// One barrier per k block: step k issues the A and weight loads of block k + 1, computes
-// block k, waits for its own loads and meets the other wavefronts at the barrier.  The
+// read from LDS in units of RU row tiles, LA units ahead of the MFMAs that consume them.
+// One barrier per k block: step k issues the weight loads of block k + 1, computes block k
+// while spreading the A DMA loads of block k + 1 over its first read units, waits for its
+// own loads and meets the other wavefronts at the barrier.  The
 // loop is unrolled by two so buffers and register sets alternate without copies; every
 // load is unconditional (the last step re-loads its own block, never used) and
 // sched_barrier pins the phase order (a load under a branch, or a consumer scheduled
 // early, would make the wavefront wait for all outstanding loads).
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU>
+// Output tile of workgroup b.  Workgroups are dispatched to the eight XCDs (each with its
+// own L2) round-robin by id, so the id is first mapped to a position such that each XCD
+// owns one contiguous range of positions; positions then walk the tile grid in bands of
+// GM tile rows, column by column, so that the tiles an XCD runs at the same time share
+// few A row blocks and weight column blocks.
+#ifndef QGEMM_PF_GM
+#define QGEMM_PF_GM 4
+#endif
+#ifndef QGEMM_PF_DS
+#define QGEMM_PF_DS 1
+#endif
+__device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& tm, int& tn) {
+  const int x = b & 7, slot = b >> 3, q = tiles >> 3, r = tiles & 7;
+  const int L = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+  const int tiles_m = tiles / tiles_n;
+  const int band = L / (QGEMM_PF_GM * tiles_n), first = band * QGEMM_PF_GM;
+  const int gm = min(QGEMM_PF_GM, tiles_m - first);
+  const int in = L - band * QGEMM_PF_GM * tiles_n;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA>
 __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   constexpr int NW = WGM * WGN;                      // wavefronts
   constexpr int NT = 64 * NW;                        // threads
@@ -457,13 +480,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   constexpr int NU = 4 * TU;                         // read units per k block
   static_assert(NDMA * 4 * NW == BM && (4 * NW) % 16 == 0, "A tile must split into whole 4-row DMA loads");
   static_assert(TU * RU == TM, "RU must divide TM");
+  constexpr int DS = QGEMM_PF_DS;                    // read units between two DMA issues
+  static_assert(DS * (NDMA - 1) < NU, "the DMA loads must all be issued within one k block");
   __shared__ __attribute__((aligned(1024))) unsigned char As0[BM * ROWB];
   __shared__ __attribute__((aligned(1024))) unsigned char As1[BM * ROWB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int tile = blockIdx.x, split = blockIdx.y;
-  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+  int tm, tn;
+  pf_tile_of(tile, gridDim.x, a.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int KB = a.K >> 7, NB = a.N >> 4;
   const int kb_begin = split * a.kb_per_split;
@@ -479,11 +505,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
       const_cast<uint16_t*>(a.A + (size_t)m0 * a.K), (short)0, rows * a.K * 2, 0x00020000);
   const int dvoff = drow * a.K * 2 + 16 * dchunk;
   const int dstride = 4 * NW * a.K * 2;              // bytes between a wavefront's DMA loads
-  auto load_a = [&](int kb, unsigned char* As) {
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(As + (NW * i + wave) * 1024), 16,
-                                               dvoff + i * dstride, kb * ROWB, 0, 0);
+  auto load_a = [&](int kb, unsigned char* As, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(As + (NW * i + wave) * 1024), 16,
+                                             dvoff + i * dstride, kb * ROWB, 0, 0);
   };
 
   // A-fragment read offsets, one per K step: row 16 TM wm + 16 i + (l & 15), chunk 4t + l / 16.
@@ -506,7 +530,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN]) {
+  // Computes one k block from As / wf while issuing the DMA loads of the next one (into
+  // Ad), DS read units apart: issued all at once they would fill the memory pipeline's
+  // queue and stall the wavefront's MFMAs behind it.
+  auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN], int kb_next, unsigned char* Ad) {
     float fs[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -514,7 +541,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
       for (int t = 0; t < 4; ++t) fs[j][t] = 0.f;
       if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[j].s[0], fs[j]);
     }
-    u32x4 af[2][RU];
+    u32x4 af[LA + 1][RU];
     auto read_unit = [&](int u, u32x4 (&dst)[RU]) {
       const int t = u / TU, i0 = (u % TU) * RU;
 #pragma unroll
@@ -523,13 +550,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     u32x4 b[2][TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[0][j] = bfrag<FMT, G>(wf[j], 0, fs[j]);
-    read_unit(0, af[0]);
+#pragma unroll
+    for (int u = 0; u < LA && u < NU; ++u) read_unit(u, af[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int t = u / TU, i0 = (u % TU) * RU;
-      if (u + 1 < NU) read_unit(u + 1, af[(u + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);   // the next unit's reads go out before this unit's MFMAs
+      if (u + LA < NU) read_unit(u + LA, af[(u + LA) % (LA + 1)]);
+      if (u % DS == 0 && u / DS < NDMA) load_a(kb_next, Ad, u / DS);
+      __builtin_amdgcn_sched_barrier(0);   // later units' reads go out before this unit's MFMAs
       if (i0 + RU == TM && t < 3) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) b[(t + 1) & 1][j] = bfrag<FMT, G>(wf[j], t + 1, fs[j]);
@@ -537,13 +566,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
       for (int r = 0; r < RU; ++r)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i0 + r][j] = mfma<FMT>(af[u & 1][r], b[t & 1][j], acc[i0 + r][j]);
+        for (int j = 0; j < TN; ++j) acc[i0 + r][j] = mfma<FMT>(af[u % (LA + 1)][r], b[t & 1][j], acc[i0 + r][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   WFrag<FMT> w0[TN], w1[TN];
-  load_a(kb_begin, As0);
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) load_a(kb_begin, As0, i);
   load_w(kb_begin, w0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -551,19 +581,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   for (int kb = kb_begin; kb < kb_end; kb += 2) {
     // even step: block kb from As0 / w0; loads of block kb + 1 into As1 / w1
     const int k1 = min(kb + 1, kb_end - 1);
-    load_a(k1, As1);
     load_w(k1, w1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(As0, w0);
+    compute(As0, w0, k1, As1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kb + 1 >= kb_end) break;
     // odd step: block kb + 1 from As1 / w1; loads of block kb + 2 into As0 / w0
     const int k2 = min(kb + 2, kb_end - 1);
-    load_a(k2, As0);
     load_w(k2, w0);
     __builtin_amdgcn_sched_barrier(0);
-    compute(As1, w1);
+    compute(As1, w1, k2, As0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -602,10 +630,10 @@ void launch_decode(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, false>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
 }
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU>
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA>
 void launch_prefill(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU>), dim3(pl.grid_x, pl.grid_y), dim3(64 * WGM * WGN),
-                     0, stream, a);
+  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA>), dim3(pl.grid_x, pl.grid_y),
+                     dim3(64 * WGM * WGN), 0, stream, a);
 }
 
 template <int FMT, int G>
@@ -613,10 +641,10 @@ hipError_t launch(const qgemm::Plan& pl, const KArgs& a, hipStream_t stream) {
   if (pl.kind == qgemm::KIND_PREFILL) {
     if (pl.bm == qgemm::pf_bm(qgemm::kPfLarge))
       launch_prefill<FMT, G, qgemm::kPfLarge.wgm, qgemm::kPfLarge.wgn, qgemm::kPfLarge.tm, qgemm::kPfLarge.tn,
-                     qgemm::kPfLarge.ru>(pl, a, stream);
+                     qgemm::kPfLarge.ru, qgemm::kPfLarge.la>(pl, a, stream);
     else
       launch_prefill<FMT, G, qgemm::kPfMedium.wgm, qgemm::kPfMedium.wgn, qgemm::kPfMedium.tm, qgemm::kPfMedium.tn,
-                     qgemm::kPfMedium.ru>(pl, a, stream);
+                     qgemm::kPfMedium.ru, qgemm::kPfMedium.la>(pl, a, stream);
   } else {
     switch (pl.cb * 16 + pl.kpw) {
       case 16 + 8: launch_decode<FMT, G, 1, 8>(pl, a, stream); break;
