@@ -108,21 +108,34 @@ def time_graph(torch, g, reps=1):
     return e0.elapsed_time(e1) / reps        # ms
 
 
+KERNEL_SOURCES = {"decode": ["qgemm_device.h", "qgemm_decode.hip"],
+                  "prefill": ["qgemm_device.h", "qgemm_prefill.hip"]}
+
+
+def kernel_sha(kind):
+    """sha256[:16] over the sources that make up one kernel (recorded in the profiles)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "weight_only_quantized_qgemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic():
     """HBM bytes per decode launch from the committed counter summary, if it still applies.
 
     The summary records the kernel source hash it was measured with; a changed kernel makes
     the figure stale, and then None is reported.
     """
-    import hashlib
-    src = os.path.join(ROOT, "weight_only_quantized_qgemm_amd", "csrc", "qgemm_kernels.hip")
     prof = os.path.join(ROOT, "profiles", "qgemm_decode_int4_traffic.txt")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = kernel_sha("decode")
         text = open(prof).read()
     except OSError:
         return None
-    rec_sha = text.split("Kernel source sha256[:16]:", 1)[1].split()[0] if "Kernel source sha256[:16]:" in text else ""
+    tag = "Decode kernel sources sha256[:16]:"
+    rec_sha = text.split(tag, 1)[1].split()[0] if tag in text else ""
     if rec_sha != sha or "traffic_bytes_per_launch =" not in text:
         return None
     return int(text.split("traffic_bytes_per_launch =", 1)[1].split()[0])
@@ -168,8 +181,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the FP8 and FP4 workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-mb", type=int, default=1024)
-    ap.add_argument("--counter-pass", action="store_true",
-                    help="for rocprofv3 --pmc: run each decode GEMM 20 times eagerly, print nothing else")
+    ap.add_argument("--counter-pass", nargs="?", const="decode", choices=("decode", "prefill"),
+                    help="for rocprofv3 --pmc: run each decode GEMM 20 times (or each prefill workload "
+                         "3 times) eagerly, print nothing else")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="for rocprofv3 --pmc: copy a MIB-sized device buffer 5 times (known traffic)")
     args = ap.parse_args()
@@ -195,6 +209,21 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": 5}))
+        return
+
+    if args.counter_pass == "prefill":
+        done = []
+        for name, si, G in (("int4_prefill", 0, 128), ("fp8", 2, 0), ("fp4", 2, 0)):
+            wk = synthetic.WORKLOADS[name]
+            M, N, K = wk["shapes"][si]
+            g = Gemm(q, torch, wk["fmt"], M, N, K, G, (synthetic.WORKLOAD_INDEX[name], si), 64 << 20)
+            for _ in range(3):
+                g.launch()
+            torch.cuda.synchronize()
+            done.append(f"{wk['fmt']} M={M} N={N} K={K}")
+            del g
+            torch.cuda.empty_cache()
+        print(json.dumps({"counter_pass": done, "launches_each": 3}))
         return
 
     wi = synthetic.WORKLOAD_INDEX["int4_decode"]

@@ -1,15 +1,20 @@
-"""Builds the HIP library (libqgemm.so) in-tree for gfx950 with hipcc."""
+"""Builds the HIP library (libqgemm.so) in-tree for gfx950 with hipcc.
+
+Each source compiles to its own object (in parallel), then hipcc links the shared library.
+"""
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = ["qgemm_host.cpp", "qgemm_kernels.hip"]
+SOURCES = ["qgemm_host.cpp", "qgemm_run.hip", "qgemm_decode.hip", "qgemm_prefill.hip"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -17,20 +22,34 @@ HIPCC_FLAGS = [
 ]
 
 
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the gfx-only target feature; that warning is noise
+    lines = [l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    return res.returncode, lines
+
+
 def build(verbose=False):
     """Compile every source into libqgemm.so next to this file; returns its path."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = (res.stdout + res.stderr)
-    # the host pass does not know the gfx-only target feature; that warning is noise
-    lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
-    if verbose and lines:
-        print("\n".join(lines))
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="qgemm_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        cmds = [[hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+            results = list(ex.map(_run, cmds))
+        msgs = []
+        for s, (rc, lines) in zip(SOURCES, results):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {s}:\n" + "\n".join(lines))
+            msgs += lines
+        tmp = LIB + ".tmp"
+        rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(lines))
+        msgs += lines
+    if verbose and msgs:
+        print("\n".join(msgs))
     os.replace(tmp, LIB)
     return LIB
 

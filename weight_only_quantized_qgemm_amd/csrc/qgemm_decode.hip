@@ -1,0 +1,213 @@
+// The decode kernel (M <= 16) of the weight-only quantized GEMM on gfx950.
+#include "qgemm_device.h"
+
+namespace qgemm {
+namespace dev {
+namespace {
+
+// ============================================================================= decode
+// M <= 16.  Workgroup = NW wavefronts; it owns CB column blocks (16 columns each) and one
+// K slice (normally all of K: a split-K hand-off costs three dependent memory round trips,
+// more than a whole small GEMM).  Wavefront w owns a contiguous share of the slice's k
+// blocks, streamed in runs of up to KPW blocks: all weight and scale loads of a run are
+// issued before any is consumed, and the k blocks are then consumed in load order, so each
+// waits only for its own data.
+// A fragments: with ASTAGE (small M) every thread first loads distinct 16-byte chunks of the
+// A slice (M rows, at most 32 KiB) into LDS, because a wave's fragment loads would otherwise
+// fetch each A value 16 times; otherwise (rows all distinct) each wavefront loads its
+// fragments from global memory before the run's weights.  Rows at or beyond M read row
+// M - 1 (MFMA output row m depends on A row m only; rows >= M are never stored).
+// Control flow is wavefront-uniform and loads are clamped rather than predicated (the
+// compiler waits for every outstanding load at the end of a branch that contains one).
+// Each wavefront keeps two accumulators per column block (even / odd K steps) to halve the
+// MFMA dependency chain; the NW wavefront tiles are summed through LDS in wave order.
+constexpr int DEC_A_CHUNKS = 2048;                  // 32 KiB of staged A per workgroup
+constexpr bool DEC_ACC2 = true;                     // two accumulators per column block
+
+template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE>
+__global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int SCH = ASTAGE ? DEC_A_CHUNKS / NT : 1;   // staging chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t a_lds[ASTAGE ? DEC_A_CHUNKS * 8 + 16 * 8 : 8];
+  __shared__ f32x4 red[NW][CB][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = blockIdx.x, split = blockIdx.y;
+  const int KB = a.K >> 7, NB = a.N >> 4;
+  const int kb_begin = split * a.kb_per_split;
+  const int kb_end = min(KB, kb_begin + a.kb_per_split);
+  const int nb0 = group * CB;
+  const int kslice = (kb_end - kb_begin) * 128;     // halves per A row in this slice
+  const int lda = kslice + 8;                        // LDS row stride (halves)
+  // this wavefront's contiguous share of the slice
+  const int share = (kb_end - kb_begin + NW - 1) / NW;
+  const int w_begin = min(kb_end, kb_begin + wave * share);
+  const int w_end = min(kb_end, w_begin + share);
+  const int row = min(lane & 15, a.M - 1);
+
+  int soff[SCH];
+  u32x4 stage[SCH];
+  if constexpr (ASTAGE) {
+    const int cpr = kslice >> 3;                     // 16-byte chunks per row
+    const int chunks = a.M * cpr;                    // <= DEC_A_CHUNKS by the launch plan
+    const float inv_cpr = 1.0f / (float)cpr;
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {                  // no branch around a load: surplus threads re-load the last chunk
+      const int q = tid + NT * i;
+      const int qq = min(q, chunks - 1);
+      const int r = (int)(((float)qq + 0.5f) * inv_cpr);
+      const int c8 = qq - r * cpr;
+      stage[i] = *reinterpret_cast<const u32x4*>(a.A + (size_t)r * a.K + (size_t)kb_begin * 128 + 8 * c8);
+      soff[i] = q < chunks ? r * lda + 8 * c8 : -1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  f32x4 acc[CB][2];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* arow_g = a.A + (size_t)row * a.K + 8 * (lane >> 4);
+  const uint16_t* arow_l = a_lds + row * lda + 8 * (lane >> 4);
+  const int last = max(w_end - 1, w_begin);          // clamp target (valid even for an empty share)
+  const int kb_cap = min(last, KB - 1);
+
+  // one run: loads first (A fragments, then weights and scales), then the k blocks in
+  // load order, each waiting only for its own data
+  auto run_loads = [&](int run, u32x4 (&afr)[ASTAGE ? 1 : KPW][4], WFrag<FMT> (&wf)[KPW][CB]) {
+    if constexpr (!ASTAGE) {
+#pragma unroll
+      for (int u = 0; u < KPW; ++u) {
+        const u32x4* ap = reinterpret_cast<const u32x4*>(arow_g + (size_t)min(run + u, kb_cap) * 128);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) afr[u][t] = ap[4 * t];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KPW; ++u)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) load_wfrag<FMT, G>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run_compute = [&](int run, const u32x4 (&afr)[ASTAGE ? 1 : KPW][4], const WFrag<FMT> (&wf)[KPW][CB]) {
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) {
+      if (run + u < w_end) {
+        u32x4 al[4];
+        if constexpr (ASTAGE) {
+          const uint16_t* ap = arow_l + (run + u - kb_begin) * 128;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const u32x4*>(ap + 32 * t);
+        }
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+          float fs[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const u32x4 av = ASTAGE ? al[t] : afr[ASTAGE ? 0 : u][t];
+            acc[c][DEC_ACC2 ? (t & 1) : 0] = mfma<FMT>(av, bfrag<FMT, G>(wf[u][c], t, fs), acc[c][DEC_ACC2 ? (t & 1) : 0]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  {   // first run: every wavefront, with or without k blocks, also stages A and syncs
+    u32x4 afr[ASTAGE ? 1 : KPW][4];
+    WFrag<FMT> wf[KPW][CB];
+    run_loads(w_begin, afr, wf);
+    if constexpr (ASTAGE) {
+#pragma unroll
+      for (int i = 0; i < SCH; ++i)
+        if (soff[i] >= 0) *reinterpret_cast<u32x4*>(a_lds + soff[i]) = stage[i];
+      __syncthreads();
+    }
+    if (w_begin < w_end) run_compute(w_begin, afr, wf);
+  }
+  for (int run = w_begin + KPW; run < w_end; run += KPW) {
+    u32x4 afr[ASTAGE ? 1 : KPW][4];
+    WFrag<FMT> wf[KPW][CB];
+    run_loads(run, afr, wf);
+    run_compute(run, afr, wf);
+  }
+
+#pragma unroll
+  for (int c = 0; c < CB; ++c) red[wave][c][lane] = DEC_ACC2 ? acc[c][0] + acc[c][1] : acc[c][0];
+  __syncthreads();
+  const bool active = tid < CB * 64;
+  const int c = tid >> 6, ln = tid & 63;
+  f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (active) {
+    v[0] = red[0][c][ln];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v[0] += red[w][c][ln];
+  }
+  if (a.splits > 1) {
+    if (!splitk_finish<1, NT>(a, group, split, CB * 256, active, v)) return;
+  }
+  if (!active || nb0 + c >= NB) return;
+  const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
+  const int n = (nb0 + c) * 16 + (ln & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * (ln >> 4) + r;
+    if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[0][r] : v[0][r] * alpha);
+  }
+}
+
+template <int FMT, int G, int CB, int KPW>
+void launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {
+  const dim3 grid(pl.grid_x, pl.grid_y);
+  if (pl.astage)
+    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, true>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, false>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
+}
+
+template <int FMT, int G>
+struct DecodeLauncher {
+  static hipError_t run(const Plan& pl, const KArgs& a, hipStream_t stream) {
+    switch (pl.cb * 16 + pl.kpw) {
+      case 16 + 8: launch_cb<FMT, G, 1, 8>(pl, a, stream); break;
+      case 16 + 5: launch_cb<FMT, G, 1, 5>(pl, a, stream); break;
+      case 16 + 4: launch_cb<FMT, G, 1, 4>(pl, a, stream); break;
+      case 16 + 2: launch_cb<FMT, G, 1, 2>(pl, a, stream); break;
+      case 16 + 1: launch_cb<FMT, G, 1, 1>(pl, a, stream); break;
+      case 32 + 4: launch_cb<FMT, G, 2, 4>(pl, a, stream); break;
+      case 32 + 2: launch_cb<FMT, G, 2, 2>(pl, a, stream); break;
+      case 32 + 1: launch_cb<FMT, G, 2, 1>(pl, a, stream); break;
+      case 64 + 2: launch_cb<FMT, G, 4, 2>(pl, a, stream); break;
+      case 64 + 1: launch_cb<FMT, G, 4, 1>(pl, a, stream); break;
+      default: return hipErrorInvalidConfiguration;
+    }
+    return hipGetLastError();
+  }
+};
+
+// Instances for every group size the format has (INT4: 32, 64, 128, 256; FP8 / FP4: none).
+template <template <int, int> class L>
+hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  switch (pl.fmt) {
+    case FMT_INT4:
+      switch (group_size) {
+        case 32: return L<FMT_INT4, 32>::run(pl, a, stream);
+        case 64: return L<FMT_INT4, 64>::run(pl, a, stream);
+        case 128: return L<FMT_INT4, 128>::run(pl, a, stream);
+        case 256: return L<FMT_INT4, 256>::run(pl, a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);
+    default: return L<FMT_FP4, 0>::run(pl, a, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  return by_format<DecodeLauncher>(pl, group_size, a, stream);
+}
+
+}  // namespace dev
+}  // namespace qgemm

@@ -1,0 +1,280 @@
+// Device-side building blocks shared by the decode and prefill kernels of the weight-only
+// quantized GEMM on gfx950 (CDNA4), and the launchers each kernel source defines.
+//
+//   out[M, N] = A[M, K] . dequant(W)[K, N]   (times alpha for FP8 / FP4)
+//
+// Both kernels feed v_mfma_f32_16x16x32_{f16,bf16}.  Operand fragment of that MFMA, per
+// 64-lane wavefront: lane l supplies row (A) or column (B) l & 15 and the eight
+// consecutive K values 8 (l >> 4) .. 8 (l >> 4) + 7 of the 32-wide K step; the 16x16 fp32
+// result sits in lane l as rows 4 (l >> 4) .. +3 of column l & 15.  The packed weight
+// layout puts exactly one such B fragment per K step in each lane's 16-byte chunk, so a
+// wavefront turns one coalesced 1 KiB load into MFMA operands with register-only
+// unpacking: the dequantize-in-registers pattern of Low Bit Triton Kernels (GPU MODE
+// lecture 034, core pattern), without the shared-memory re-layout that the Bitblas
+// lecture 033 (layout section) measures as the dominant cost when fragments mismatch.
+//
+// Dequantization (value semantics of each format):
+//   INT4: the nibble (stored value + 8) is OR-ed into the mantissa of an fp16 constant
+//         (0x6400 = 1024 for a low nibble, 0x5400 = 64 for a nibble at bit 4), the
+//         constant plus 8 is subtracted (exact), and the result is multiplied by the fp16
+//         group scale: RNE_fp16((nibble - 8) * s), the 16-bit tile of the gemlite snippet.
+//   FP8 : v_cvt_scalef32_pk_bf16_fp8 with scale 1.0 (OCP e4m3, exact in bf16); the
+//         per-tensor alpha multiplies the fp32 accumulator in the epilogue (FlashInfer
+//         PR #7495 analysis, introduction).
+//   FP4 : v_cvt_scalef32_pk_f32_fp4 with scale 1.0, times the e4m3 block scale in fp32
+//         (exact), then RNE to bf16 (exact).  The scale operand of the scalef32 converts
+//         only honours its exponent, so it cannot carry an e4m3 block scale.
+//
+// Split-K (when the output tiles alone cannot fill 256 compute units): each K slice writes
+// an fp32 partial tile to the workspace, then takes a ticket; the workgroup that draws the
+// last ticket sums all partials in slice order (bitwise deterministic, whichever slice
+// arrives last) and resets the ticket.  No workgroup ever waits for another, so nothing
+// assumes co-residency (FlashInfer PR #7495 analysis, section 3(d), describes the deadlock
+// that assumption caused and the slice-ordered sum that keeps results bitwise identical).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qgemm_internal.h"
+
+namespace qgemm {
+namespace dev {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct KArgs {
+  const uint16_t* A;          // [M][K] 16-bit
+  const uint8_t* W;           // packed weights
+  const void* S;              // packed scales (INT4: fp16, FP4: e4m3 bytes)
+  const float* alpha;         // FP8 / FP4: device scalar
+  void* out;                  // [M][N]
+  unsigned* counters;         // split-K tickets, one per tile
+  float* partials;            // split-K partial tiles
+  int M, N, K;
+  int out_dtype;
+  int splits, kb_per_split;
+  int tiles_n;                // prefill: output tiles along N
+};
+
+// ----------------------------------------------------------------------------- dequant
+// (a & m) | o in one VALU op.  The compiler splits it into AND + OR because the two
+// constants cannot both be instruction operands; as VGPR operands they can.
+__device__ __forceinline__ unsigned and_or(unsigned a, unsigned m, unsigned o) {
+  unsigned r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+__device__ __forceinline__ u32x4 dq_int4(unsigned w, unsigned s2) {
+  const unsigned hi = w >> 8;
+  const unsigned p0 = and_or(w, 0x000F000Fu, 0x64006400u);    // k slots j0, j1: 1024 + nibble
+  const unsigned p1 = and_or(w, 0x00F000F0u, 0x54005400u);    // j2, j3: 64 + nibble
+  const unsigned p2 = and_or(hi, 0x000F000Fu, 0x64006400u);   // j4, j5
+  const unsigned p3 = and_or(hi, 0x00F000F0u, 0x54005400u);   // j6, j7
+  const f16x2 s = __builtin_bit_cast(f16x2, s2);
+  const f16x2 big = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 small = {(_Float16)72.0f, (_Float16)72.0f};
+  const f16x2 h0 = (__builtin_bit_cast(f16x2, p0) - big) * s;
+  const f16x2 h1 = (__builtin_bit_cast(f16x2, p1) - small) * s;
+  const f16x2 h2 = (__builtin_bit_cast(f16x2, p2) - big) * s;
+  const f16x2 h3 = (__builtin_bit_cast(f16x2, p3) - small) * s;
+  return u32x4{__builtin_bit_cast(unsigned, h0), __builtin_bit_cast(unsigned, h1),
+               __builtin_bit_cast(unsigned, h2), __builtin_bit_cast(unsigned, h3)};
+}
+
+__device__ __forceinline__ u32x4 dq_fp8(unsigned lo, unsigned hi) {
+  return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
+
+__device__ __forceinline__ unsigned pk_bf16(f32x2 f, float s) {
+  bf16x2 r;
+  r[0] = (__bf16)(f[0] * s);
+  r[1] = (__bf16)(f[1] * s);
+  return __builtin_bit_cast(unsigned, r);
+}
+
+__device__ __forceinline__ u32x4 dq_fp4(unsigned w, float s) {
+  return u32x4{pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), s),
+               pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), s),
+               pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), s),
+               pk_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), s)};
+}
+
+// Four e4m3 block-scale bytes -> fp32 (exact through the verified e4m3 -> bf16 convert).
+__device__ __forceinline__ void fp4_scales(unsigned sw, float (&s)[4]) {
+  const unsigned a = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(sw, 1.0f, false));
+  const unsigned b = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(sw, 1.0f, true));
+  s[0] = __builtin_bit_cast(float, a << 16);
+  s[1] = __builtin_bit_cast(float, a & 0xFFFF0000u);
+  s[2] = __builtin_bit_cast(float, b << 16);
+  s[3] = __builtin_bit_cast(float, b & 0xFFFF0000u);
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (FMT == qgemm::FMT_INT4)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Weights + scales of one (column block, 128-wide k block) as seen by one lane.  Scales
+// are kept as loaded (raw bits) and expanded only where they are used, so that nothing
+// consumes a load before the MFMA loop does (a consumer forces a wait for every load
+// issued before it).
+template <int FMT>
+struct WFrag {
+  u32x4 w[FMT == qgemm::FMT_FP8 ? 2 : 1];
+  unsigned s[2];    // INT4: 1, 2 or 4 fp16 scales (G = 128|256, 64, 32); FP4: 4 e4m3 bytes
+};
+
+// G is the INT4 group size (a template parameter, so the scale load has no branches:
+// a branch around a load ends in a wait for every outstanding load); 0 for FP8 / FP4.
+// STREAM marks weights read once (decode: non-temporal loads keep them out of the way in
+// the caches); prefill re-reads each weight fragment once per row tile and caches it.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 wload(const u32x4* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int FMT, int G, bool STREAM = true>
+__device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int lane, WFrag<FMT>& f) {
+  const int KB = a.K >> 7;
+  if constexpr (FMT == qgemm::FMT_FP8) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * (KB * 2) + 2 * kb) * 1024) + lane;
+    f.w[0] = wload<STREAM>(p);
+    f.w[1] = wload<STREAM>(p + 64);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * KB + kb) * 1024) + lane;
+    f.w[0] = wload<STREAM>(p);
+  }
+  if constexpr (FMT == qgemm::FMT_INT4) {
+    const uint16_t* S = static_cast<const uint16_t*>(a.S);
+    const int c = lane & 15;
+    if constexpr (G <= 128) {
+      constexpr int T = 128 / G;
+      const size_t base = ((size_t)nb * KB + kb) * 16 * T + (size_t)c * T;
+      if constexpr (T == 4) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(S + base);
+        f.s[0] = x[0];
+        f.s[1] = x[1];
+      } else if constexpr (T == 2) {
+        f.s[0] = *reinterpret_cast<const unsigned*>(S + base);
+      } else {
+        f.s[0] = S[base];
+      }
+    } else {   // G == 256: one scale per two k blocks
+      f.s[0] = S[((size_t)nb * (KB >> 1) + (kb >> 1)) * 16 + c];
+    }
+  } else if constexpr (FMT == qgemm::FMT_FP4) {
+    const uint8_t* S = static_cast<const uint8_t*>(a.S);
+    f.s[0] = *reinterpret_cast<const unsigned*>(S + (((size_t)nb * KB + kb) * 16 + (lane & 15)) * 8 + 4 * (lane >> 5));
+  }
+}
+
+// fp16 scale of K step t, duplicated into both halves (INT4).
+template <int G>
+__device__ __forceinline__ unsigned int4_scale_pair(const unsigned (&s)[2], int t) {
+  unsigned h;
+  if constexpr (G == 32) h = (t & 1) ? (s[t >> 1] >> 16) : (s[t >> 1] & 0xFFFFu);
+  else if constexpr (G == 64) h = (t >> 1) ? (s[0] >> 16) : (s[0] & 0xFFFFu);
+  else h = s[0] & 0xFFFFu;
+  return h | (h << 16);
+}
+
+// The B operand (dequantized weights) of K step t.
+template <int FMT, int G>
+__device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (&fs)[4]) {
+  if constexpr (FMT == qgemm::FMT_INT4) {
+    return dq_int4(f.w[0][t], int4_scale_pair<G>(f.s, t));
+  } else if constexpr (FMT == qgemm::FMT_FP8) {
+    return dq_fp8(f.w[t >> 1][2 * (t & 1)], f.w[t >> 1][2 * (t & 1) + 1]);
+  } else {
+    return dq_fp4(f.w[0][t], fs[t]);
+  }
+}
+
+// ----------------------------------------------------------------------------- epilogue
+__device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v) {
+  const size_t i = (size_t)m * a.N + n;
+  if (a.out_dtype == QGEMM_DT_F32) {
+    static_cast<float*>(a.out)[i] = v;
+  } else if (a.out_dtype == QGEMM_DT_F16) {
+    static_cast<_Float16*>(a.out)[i] = (_Float16)v;
+  } else {
+    static_cast<__bf16*>(a.out)[i] = (__bf16)v;
+  }
+}
+
+// Split-K hand-off.  Every thread of the workgroup calls this with its NF fragments
+// (`active` false for threads that hold none).  Returns true in the workgroup that must
+// write the output; then `v` holds the slice-ordered sum of all partials.
+//
+// Visibility across XCDs without L2 maintenance: partials are written with device-scope
+// stores (write-through past the XCD-private L2), every thread waits for its stores to
+// be acknowledged before the barrier that precedes the ticket, and the last workgroup
+// reads the partials back with device-scope loads.  A device-scope fence would instead
+// write back and invalidate the whole XCD L2 in every workgroup.
+__device__ __forceinline__ void store_dev(float* p, f32x4 v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) __hip_atomic_store(p + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_dev(const float* p) {
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+template <int NF, int NT = 256>
+__device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  float* base = a.partials + (size_t)tile * a.splits * tile_elems;
+  if (active) {
+    float* mine = base + (size_t)split * tile_elems;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) store_dev(mine + 4 * (f * NT + tid), v[f]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores are complete
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned ticket = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ticket == (unsigned)(a.splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return false;
+  if (active) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) v[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.splits; ++s) {
+      const float* p = base + (size_t)s * tile_elems;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) v[f] += load_dev(p + 4 * (f * NT + tid));
+    }
+  }
+  if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// ----------------------------------------------------------------------------- launchers
+// Launch the kernel instance the plan names on `stream`; return hipGetLastError().
+hipError_t launch_decode(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
+
+}  // namespace dev
+}  // namespace qgemm

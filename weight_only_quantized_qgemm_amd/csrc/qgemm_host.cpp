@@ -129,8 +129,17 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // loads would otherwise fetch each A value many times.  With larger M the rows are
     // distinct and fragments are loaded directly.
     pl->astage = p->M <= 4;
-    // Column blocks per workgroup: wider workgroups cut A re-reads when M > 1.
-    pl->cb = p->tile_hint ? p->tile_hint : (p->M == 1 ? 1 : (p->M <= 4 ? 2 : 4));
+    // Column blocks per workgroup.  Every workgroup reads all M x K of A once, so wider
+    // workgroups cut A traffic; narrower ones put more compute units to work.  M = 1: A is
+    // negligible, one block each.  M <= 4: two.  Larger M: the fewest blocks (1, 2 or 4)
+    // that keep the grid within one workgroup per compute unit.
+    int cb = 1;
+    if (p->M > 4) {
+      while (cb < 4 && ceil_div(nblocks, cb) > kCUs) cb *= 2;
+    } else if (p->M > 1) {
+      cb = 2;
+    }
+    pl->cb = p->tile_hint ? p->tile_hint : cb;
     const int groups = ceil_div(nblocks, pl->cb);
     // K is split only when needed to bound the staged A slice, or when the output alone
     // gives fewer than 128 workgroups (a split-K hand-off costs three dependent memory

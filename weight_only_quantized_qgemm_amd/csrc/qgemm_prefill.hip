@@ -1,0 +1,250 @@
+// The prefill kernel (MFMA tiles, any M) of the weight-only quantized GEMM on gfx950.
+#include "qgemm_device.h"
+
+namespace qgemm {
+namespace dev {
+namespace {
+
+// ============================================================================= prefill
+// Workgroup = WGM x WGN wavefronts; each wavefront owns TM x TN MFMA tiles (16 x 16), so
+// the workgroup tile is (16 WGM TM) x (16 WGN TN); one 128-wide k block per step.
+//
+// A goes from HBM straight into LDS (buffer loads with the LDS-destination bit: no VGPR
+// staging), double-buffered in two separate arrays so that the compiler can tell the
+// buffer being read from the one being filled.  A DMA load writes its 64 lanes' 16 bytes
+// contiguously, so LDS rows cannot be padded; instead the 16-byte chunk c of tile row r
+// is stored at chunk position c ^ (r & 15).  The MFMA A-fragment read (lane l: row l & 15,
+// chunk 4t + l / 16) then touches 16 distinct positions per 16 lanes: no bank conflicts.
+// The buffer resource covers the tile's valid rows only and the row sits in the range-
+// checked per-lane offset (the k block in the scalar offset never leaves its row), so rows
+// at or beyond M read as zero (and are never stored).
+//
+// Each wavefront loads its own packed weight fragments into registers (one k block
+// ahead) and dequantizes each once per K step, reusing it for its TM row tiles; the
+// dequantization of K step t + 1 is issued with the MFMAs of step t.  A fragments are
+// read from LDS in units of RU row tiles, LA units ahead of the MFMAs that consume them.
+// One barrier per k block: step k issues the weight loads of block k + 1, computes block k
+// while spreading the A DMA loads of block k + 1 over its first read units, waits for its
+// own loads and meets the other wavefronts at the barrier.  The
+// loop is unrolled by two so buffers and register sets alternate without copies; every
+// load is unconditional (the last step re-loads its own block, never used) and
+// sched_barrier pins the phase order (a load under a branch, or a consumer scheduled
+// early, would make the wavefront wait for all outstanding loads).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Output tile of workgroup b.  Workgroups are dispatched to the eight XCDs (each with its
+// own L2) round-robin by id, so the id is first mapped to a position such that each XCD
+// owns one contiguous range of positions; positions then walk the tile grid in bands of
+// GM tile rows, column by column, so that the tiles an XCD runs at the same time share
+// few A row blocks and weight column blocks.
+#ifndef QGEMM_PF_GM
+#define QGEMM_PF_GM 4
+#endif
+#ifndef QGEMM_PF_DS
+#define QGEMM_PF_DS 1
+#endif
+__device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& tm, int& tn) {
+  const int x = b & 7, slot = b >> 3, q = tiles >> 3, r = tiles & 7;
+  const int L = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+  const int tiles_m = tiles / tiles_n;
+  const int band = L / (QGEMM_PF_GM * tiles_n), first = band * QGEMM_PF_GM;
+  const int gm = min(QGEMM_PF_GM, tiles_m - first);
+  const int in = L - band * QGEMM_PF_GM * tiles_n;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA>
+__global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
+  constexpr int NW = WGM * WGN;                      // wavefronts
+  constexpr int NT = 64 * NW;                        // threads
+  constexpr int BM = 16 * WGM * TM, BN = 16 * WGN * TN;
+  constexpr int ROWB = 256;                          // bytes of one A row per k block
+  constexpr int NDMA = BM / (4 * NW);                // 1 KiB DMA loads per wavefront per k block
+  constexpr int TU = TM / RU;                        // read units per K step
+  constexpr int NU = 4 * TU;                         // read units per k block
+  static_assert(NDMA * 4 * NW == BM && (4 * NW) % 16 == 0, "A tile must split into whole 4-row DMA loads");
+  static_assert(TU * RU == TM, "RU must divide TM");
+  constexpr int DS = QGEMM_PF_DS;                    // read units between two DMA issues
+  static_assert(DS * (NDMA - 1) < NU, "the DMA loads must all be issued within one k block");
+  __shared__ __attribute__((aligned(1024))) unsigned char As0[BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char As1[BM * ROWB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  int tm, tn;
+  pf_tile_of(tile, gridDim.x, a.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KB = a.K >> 7, NB = a.N >> 4;
+  const int kb_begin = split * a.kb_per_split;
+  const int kb_end = min(KB, kb_begin + a.kb_per_split);
+
+  // DMA load i of this wavefront fills LDS bytes [(NW i + wave) KiB, +1 KiB): tile rows
+  // 4 (NW i + wave) + lane / 16, chunk position lane & 15.  Since 4 NW is a multiple of 16,
+  // the row's low four bits, and so the swizzled source chunk, do not depend on i.
+  const int drow = 4 * wave + (lane >> 4);
+  const int dchunk = (lane & 15) ^ (drow & 15);
+  const int rows = min(a.M - m0, BM);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.A + (size_t)m0 * a.K), (short)0, rows * a.K * 2, 0x00020000);
+  const int dvoff = drow * a.K * 2 + 16 * dchunk;
+  const int dstride = 4 * NW * a.K * 2;              // bytes between a wavefront's DMA loads
+  auto load_a = [&](int kb, unsigned char* As, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_ptr_t)(As + (NW * i + wave) * 1024), 16,
+                                             dvoff + i * dstride, kb * ROWB, 0, 0);
+  };
+
+  // A-fragment read offsets, one per K step: row 16 TM wm + 16 i + (l & 15), chunk 4t + l / 16.
+  int aoff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    aoff[t] = (16 * TM * wm + (lane & 15)) * ROWB + 16 * ((4 * t + (lane >> 4)) ^ (lane & 15));
+
+  int nbw[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) nbw[j] = min((n0 >> 4) + TN * wn + j, NB - 1);
+  auto load_w = [&](int kb, WFrag<FMT> (&wf)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) load_wfrag<FMT, G, false>(a, nbw[j], kb, lane, wf[j]);
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Computes one k block from As / wf while issuing the DMA loads of the next one (into
+  // Ad), DS read units apart: issued all at once they would fill the memory pipeline's
+  // queue and stall the wavefront's MFMAs behind it.
+  auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN], int kb_next, unsigned char* Ad) {
+    float fs[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fs[j][t] = 0.f;
+      if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[j].s[0], fs[j]);
+    }
+    u32x4 af[LA + 1][RU];
+    auto read_unit = [&](int u, u32x4 (&dst)[RU]) {
+      const int t = u / TU, i0 = (u % TU) * RU;
+#pragma unroll
+      for (int r = 0; r < RU; ++r) dst[r] = *reinterpret_cast<const u32x4*>(As + aoff[t] + (i0 + r) * 16 * ROWB);
+    };
+    u32x4 b[2][TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[0][j] = bfrag<FMT, G>(wf[j], 0, fs[j]);
+#pragma unroll
+    for (int u = 0; u < LA && u < NU; ++u) read_unit(u, af[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int t = u / TU, i0 = (u % TU) * RU;
+      if (u + LA < NU) read_unit(u + LA, af[(u + LA) % (LA + 1)]);
+      if (u % DS == 0 && u / DS < NDMA) load_a(kb_next, Ad, u / DS);
+      __builtin_amdgcn_sched_barrier(0);   // later units' reads go out before this unit's MFMAs
+      if (i0 + RU == TM && t < 3) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[(t + 1) & 1][j] = bfrag<FMT, G>(wf[j], t + 1, fs[j]);
+      }
+#pragma unroll
+      for (int r = 0; r < RU; ++r)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i0 + r][j] = mfma<FMT>(af[u % (LA + 1)][r], b[t & 1][j], acc[i0 + r][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  WFrag<FMT> w0[TN], w1[TN];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) load_a(kb_begin, As0, i);
+  load_w(kb_begin, w0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
+    // even step: block kb from As0 / w0; loads of block kb + 1 into As1 / w1
+    const int k1 = min(kb + 1, kb_end - 1);
+    load_w(k1, w1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As0, w0, k1, As1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 >= kb_end) break;
+    // odd step: block kb + 1 from As1 / w1; loads of block kb + 2 into As0 / w0
+    const int k2 = min(kb + 2, kb_end - 1);
+    load_w(k2, w0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As1, w1, k2, As0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  f32x4 v[TM * TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) v[TN * i + j] = acc[i][j];
+  if (a.splits > 1) {
+    if (!splitk_finish<TM * TN, NT>(a, tile, split, BM * BN, true, v)) return;
+  }
+  const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int nb = (n0 >> 4) + TN * wn + j;
+    if (nb >= NB) continue;
+    const int n = nb * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * TM * wm + 16 * i + 4 * (lane >> 4) + r;
+        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[TN * i + j][r] : v[TN * i + j][r] * alpha);
+      }
+  }
+}
+
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA>
+void launch_shape(const Plan& pl, const KArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA>), dim3(pl.grid_x, pl.grid_y),
+                     dim3(64 * WGM * WGN), 0, stream, a);
+}
+
+template <int FMT, int G>
+struct PrefillLauncher {
+  static hipError_t run(const Plan& pl, const KArgs& a, hipStream_t stream) {
+    if (pl.bm == pf_bm(kPfLarge))
+      launch_shape<FMT, G, kPfLarge.wgm, kPfLarge.wgn, kPfLarge.tm, kPfLarge.tn, kPfLarge.ru, kPfLarge.la>(pl, a, stream);
+    else
+      launch_shape<FMT, G, kPfMedium.wgm, kPfMedium.wgn, kPfMedium.tm, kPfMedium.tn, kPfMedium.ru, kPfMedium.la>(pl, a,
+                                                                                                            stream);
+    return hipGetLastError();
+  }
+};
+
+// Instances for every group size the format has (INT4: 32, 64, 128, 256; FP8 / FP4: none).
+template <template <int, int> class L>
+hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  switch (pl.fmt) {
+    case FMT_INT4:
+      switch (group_size) {
+        case 32: return L<FMT_INT4, 32>::run(pl, a, stream);
+        case 64: return L<FMT_INT4, 64>::run(pl, a, stream);
+        case 128: return L<FMT_INT4, 128>::run(pl, a, stream);
+        case 256: return L<FMT_INT4, 256>::run(pl, a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);
+    default: return L<FMT_FP4, 0>::run(pl, a, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  return by_format<PrefillLauncher>(pl, group_size, a, stream);
+}
+
+}  // namespace dev
+}  // namespace qgemm
