@@ -224,31 +224,25 @@ __device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v)
 // write the output; then `v` holds the slice-ordered sum of all partials.
 //
 // Visibility across XCDs without L2 maintenance: partials are written with device-scope
-// stores (write-through past the XCD-private L2), every thread waits for its stores to
-// be acknowledged before the barrier that precedes the ticket, and the last workgroup
-// reads the partials back with device-scope loads.  A device-scope fence would instead
-// write back and invalidate the whole XCD L2 in every workgroup.
-__device__ __forceinline__ void store_dev(float* p, f32x4 v) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) __hip_atomic_store(p + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ f32x4 load_dev(const float* p) {
-  f32x4 v;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
-}
+// (sc1) stores, which write through the XCD-private L2, every thread waits for its stores
+// to be acknowledged before the barrier that precedes the ticket, and the last workgroup
+// reads the partials back with device-scope loads, which do not hit in its own L2.  A
+// device-scope fence would instead write back and invalidate the whole XCD L2 in every
+// workgroup.  The accesses are 16-byte buffer loads and stores carrying the sc1 policy
+// (the relaxed device-scope atomics of the same bits move 4 bytes per instruction).
+constexpr int kCPolDevice = 16;   // buffer-instruction cache policy: sc1 (device scope)
 
 template <int NF, int NT = 256>
 __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  float* base = a.partials + (size_t)tile * a.splits * tile_elems;
+  const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+      a.partials + (size_t)tile * a.splits * tile_elems, (short)0, a.splits * tile_elems * 4, 0x00020000);
   if (active) {
-    float* mine = base + (size_t)split * tile_elems;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) store_dev(mine + 4 * (f * NT + tid), v[f]);
+    for (int f = 0; f < NF; ++f)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[f]), part,
+                                             (split * tile_elems + 4 * (f * NT + tid)) * 4, 0, kCPolDevice);
   }
   __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores are complete
   __syncthreads();
@@ -261,10 +255,19 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
   if (active) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) v[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int B = NF < 8 ? NF : 8;                // loads in flight per batch
     for (int s = 0; s < a.splits; ++s) {
-      const float* p = base + (size_t)s * tile_elems;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) v[f] += load_dev(p + 4 * (f * NT + tid));
+      for (int f0 = 0; f0 < NF; f0 += B) {
+        f32x4 p[B];
+#pragma unroll
+        for (int f = 0; f < B; ++f)
+          p[f] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               part, (s * tile_elems + 4 * ((f0 + f) * NT + tid)) * 4, 0, kCPolDevice));
+#pragma unroll
+        for (int f = 0; f < B; ++f) v[f0 + f] += p[f];
+        __builtin_amdgcn_sched_barrier(0);          // one batch at a time: bounded registers
+      }
     }
   }
   if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

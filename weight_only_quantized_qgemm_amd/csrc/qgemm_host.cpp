@@ -179,9 +179,19 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       return fail(QGEMM_ERR_UNSUPPORTED, "the prefill kernel needs %d * K * 2 < 2^31 (K = %lld)", pl->bm,
                   (long long)p->K);
     const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
-    int s = 1;
-    while ((int64_t)mt * nt * s < kCUs && s * 2 <= kblocks / 4) s *= 2;
-    pl->splits = s;
+    // K split: the count that minimises a step-count model of the launch, in units of one
+    // k block of one workgroup: rounds of the grid over the CUs x (k blocks per slice +
+    // pipeline fill and drain), plus, when split, the final workgroup's reads of one
+    // partial tile per slice.  Slices keep at least two k blocks.
+    const double kFill = 3.0, kPartialRead = 1.5;
+    int best = 1;
+    double best_cost = 0.0;
+    for (int s = 1; s <= 64 && s <= kblocks / 2; ++s) {
+      const double rounds = (double)((mt * nt * s + kCUs - 1) / kCUs);
+      const double cost = rounds * (ceil_div(kblocks, s) + kFill) + (s > 1 ? kPartialRead * s : 0.0);
+      if (s == 1 || cost < best_cost) { best = s; best_cost = cost; }
+    }
+    pl->splits = best;
     finish_split(pl, kblocks, p->split_k_hint);
     if (mt * nt > 0x7fffffffLL) return fail(QGEMM_ERR_UNSUPPORTED, "too many output tiles (%lld)", (long long)(mt * nt));
     pl->grid_x = (unsigned)(mt * nt);

@@ -10,15 +10,17 @@ namespace qgemm {
 
 // Prefill workgroup shapes: one row of eight wavefronts (two per SIMD), each owning
 // TM x TN MFMA tiles of 16 x 16.  The large shape amortises every dequantized weight
-// fragment over 16 row tiles; the medium one halves the rows for small M.
-// RU: row tiles per LDS read unit; LA: units read ahead of the MFMAs that consume them.
-struct PfShape { int wgm, wgn, tm, tn, ru, la; };
+// fragment over 16 row tiles; the medium one (small M) has a quarter of the area, so its
+// k steps are short and it keeps four A stages in flight instead of two.
+// RU: row tiles per LDS read unit; LA: units read ahead of the MFMAs that consume them;
+// ST: A stages in LDS (ST - 1 k blocks are loaded ahead of the one being computed).
+struct PfShape { int wgm, wgn, tm, tn, ru, la, st; };
 #ifndef QGEMM_PF_LARGE
-#define QGEMM_PF_LARGE 1, 8, 16, 2, 4, 1
-#define QGEMM_PF_MEDIUM 1, 8, 8, 2, 8, 1
+#define QGEMM_PF_LARGE 1, 8, 16, 2, 4, 1, 2
+#define QGEMM_PF_MEDIUM 1, 8, 8, 1, 8, 1, 4
 #endif
 constexpr PfShape kPfLarge{QGEMM_PF_LARGE};    // 256 x 256 output tile
-constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 256 output tile
+constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 128 output tile
 constexpr int pf_bm(PfShape s) { return 16 * s.wgm * s.tm; }
 constexpr int pf_bn(PfShape s) { return 16 * s.wgn * s.tn; }
 // Decode kernel: wavefronts per workgroup.

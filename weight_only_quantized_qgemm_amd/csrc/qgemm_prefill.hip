@@ -32,6 +32,17 @@ namespace {
 // early, would make the wavefront wait for all outstanding loads).
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Workgroup barrier without the release fence of __syncthreads(), which waits for every
+// outstanding load, the A stages still meant to be in flight included.  Callers first
+// wait for the loads that must have landed; every LDS read before the barrier has been
+// consumed (so completed) by then; the clobbers keep the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Output tile of workgroup b.  Workgroups are dispatched to the eight XCDs (each with its
 // own L2) round-robin by id, so the id is first mapped to a position such that each XCD
 // owns one contiguous range of positions; positions then walk the tile grid in bands of
@@ -54,7 +65,7 @@ __device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& t
   tn = in / gm;
 }
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA>
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST>
 __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   constexpr int NW = WGM * WGN;                      // wavefronts
   constexpr int NT = 64 * NW;                        // threads
@@ -67,8 +78,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   static_assert(TU * RU == TM, "RU must divide TM");
   constexpr int DS = QGEMM_PF_DS;                    // read units between two DMA issues
   static_assert(DS * (NDMA - 1) < NU, "the DMA loads must all be issued within one k block");
+  static_assert(ST >= 2 && ST <= 4, "two to four A stages");
+  // Each stage is its own array, so that the compiler can tell the buffer being read from
+  // the ones being filled (it would otherwise wait for every DMA load before a read).
   __shared__ __attribute__((aligned(1024))) unsigned char As0[BM * ROWB];
   __shared__ __attribute__((aligned(1024))) unsigned char As1[BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char As2[ST > 2 ? BM * ROWB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char As3[ST > 3 ? BM * ROWB : 16];
+  auto stage = [&](int i) -> unsigned char* { return i == 0 ? As0 : i == 1 ? As1 : i == 2 ? As2 : As3; };
+  // Vector-memory instructions per k block per wavefront: NDMA A loads and, per weight
+  // column block, two (the fragment and its scales, or FP8's two fragment halves).  At the
+  // end of a step the next block must have landed while the ST - 2 blocks after it may
+  // still be in flight; loads complete in issue order, so that is this many pending.
+  constexpr int PEND = (ST - 2) * (NDMA + 2 * TN);
+  static_assert(PEND <= 63, "vmcnt counts at most 63 outstanding loads");
+  // s_waitcnt immediate: vmcnt = PEND (bits 3:0 and 15:14), expcnt and lgkmcnt left open.
+  // Through the builtin (not inline asm) the compiler's own wait insertion knows of it.
+  constexpr int WAIT_PEND = (PEND & 15) | (7 << 4) | (15 << 8) | ((PEND >> 4) << 14);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
@@ -156,30 +182,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     }
   };
 
-  WFrag<FMT> w0[TN], w1[TN];
+  // Prologue: blocks kb_begin .. kb_begin + ST - 2 into stages 0 .. ST - 2.  Step kb computes
+  // stage kb mod ST while loading block kb + ST - 1 into the stage the previous step read.
+  WFrag<FMT> w[ST][TN];
 #pragma unroll
-  for (int i = 0; i < NDMA; ++i) load_a(kb_begin, As0, i);
-  load_w(kb_begin, w0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int kb = kb_begin; kb < kb_end; kb += 2) {
-    // even step: block kb from As0 / w0; loads of block kb + 1 into As1 / w1
-    const int k1 = min(kb + 1, kb_end - 1);
-    load_w(k1, w1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As0, w0, k1, As1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 1 >= kb_end) break;
-    // odd step: block kb + 1 from As1 / w1; loads of block kb + 2 into As0 / w0
-    const int k2 = min(kb + 2, kb_end - 1);
-    load_w(k2, w0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As1, w1, k2, As0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  for (int s = 0; s < ST - 1; ++s) {
+    const int kb = min(kb_begin + s, kb_end - 1);
+    load_w(kb, w[s]);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) load_a(kb, stage(s), i);
   }
+  __builtin_amdgcn_s_waitcnt(WAIT_PEND);
+  barrier_no_fence();
+
+  for (int kb = kb_begin; kb < kb_end; kb += ST) {
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      const int sn = (j + ST - 1) % ST;                // stage that receives block kn
+      const int kn = min(kb + j + ST - 1, kb_end - 1);
+      load_w(kn, w[sn]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage(j), w[j], kn, stage(sn));
+      __builtin_amdgcn_s_waitcnt(WAIT_PEND);
+      barrier_no_fence();
+      if (kb + j + 1 >= kb_end) break;
+    }
+  }
+  // clamped re-loads past the last block may still be writing LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   f32x4 v[TM * TN];
 #pragma unroll
@@ -205,20 +235,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   }
 }
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA>
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST>
 void launch_shape(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA>), dim3(pl.grid_x, pl.grid_y),
+  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST>), dim3(pl.grid_x, pl.grid_y),
                      dim3(64 * WGM * WGN), 0, stream, a);
 }
 
 template <int FMT, int G>
 struct PrefillLauncher {
   static hipError_t run(const Plan& pl, const KArgs& a, hipStream_t stream) {
-    if (pl.bm == pf_bm(kPfLarge))
-      launch_shape<FMT, G, kPfLarge.wgm, kPfLarge.wgn, kPfLarge.tm, kPfLarge.tn, kPfLarge.ru, kPfLarge.la>(pl, a, stream);
+    constexpr PfShape L = kPfLarge, S = kPfMedium;
+    if (pl.bm == pf_bm(L))
+      launch_shape<FMT, G, L.wgm, L.wgn, L.tm, L.tn, L.ru, L.la, L.st>(pl, a, stream);
     else
-      launch_shape<FMT, G, kPfMedium.wgm, kPfMedium.wgn, kPfMedium.tm, kPfMedium.tn, kPfMedium.ru, kPfMedium.la>(pl, a,
-                                                                                                            stream);
+      launch_shape<FMT, G, S.wgm, S.wgn, S.tm, S.tn, S.ru, S.la, S.st>(pl, a, stream);
     return hipGetLastError();
   }
 };
