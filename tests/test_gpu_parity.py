@@ -126,6 +126,18 @@ def test_split_k_and_kernel_hints(q, fmt, M, hint, split, tile):
     check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, tile_hint=tile)
 
 
+@pytest.mark.parametrize("fmt,G", [("int4", 64), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128 * 44), (3, 512, 128 * 60), (16, 256, 128 * 60), (16, 8192, 128 * 44),
+                                   (9, 4352, 128 * 23)])
+def test_decode_multi_run(q, fmt, G, M, N, K):
+    # Wavefront shares longer than one run (the pipelined decode path), with uneven run
+    # counts, shares that end mid-run, and staged / unstaged A.
+    say(f"case decode-multirun fmt={fmt} G={G} M={M} N={N} K={K}")
+    prep = Prepared(q, fmt, N, K, G or 0, (54, N, K))
+    A = _act(fmt, M, K, (54, M))
+    check_against_oracle(q, prep, A)
+
+
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("fp8", None), ("fp4", None)])
 @pytest.mark.parametrize("tile,split", [(128, 1), (128, 3), (256, 1), (256, 3)])
 def test_prefill_tile_shapes(q, fmt, G, tile, split):

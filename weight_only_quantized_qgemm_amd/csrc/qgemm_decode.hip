@@ -21,11 +21,17 @@ namespace {
 // compiler waits for every outstanding load at the end of a branch that contains one).
 // Each wavefront keeps two accumulators per column block (even / odd K steps) to halve the
 // MFMA dependency chain; the NW wavefront tiles are summed through LDS in wave order.
+// NR >= 2 (a share of NR runs): two register sets alternate and the loads of run r + 1
+// are issued before run r is computed, so consecutive runs overlap their memory round
+// trips.  The runs are unrolled (a loop carrying loads across its back edge defeats the
+// compiler's wait tracking, which then drains every load at the loop head).  NR = 1: one
+// run, or, for shares longer than four runs, runs one after another.
 constexpr int DEC_A_CHUNKS = 2048;                  // 32 KiB of staged A per workgroup
 constexpr bool DEC_ACC2 = true;                     // two accumulators per column block
 
-template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE>
+template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE, int NR>
 __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
+  constexpr bool MULTI = NR > 1;
   constexpr int NT = 64 * NW;
   constexpr int SCH = ASTAGE ? DEC_A_CHUNKS / NT : 1;   // staging chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[ASTAGE ? DEC_A_CHUNKS * 8 + 16 * 8 : 8];
@@ -89,15 +95,27 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
       for (int c = 0; c < CB; ++c) load_wfrag<FMT, G>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // MULTI: no branch around a k block (the compiler would wait for every load in flight,
+  // the next run's included, at its end); a block past the share multiplies a zero A
+  // fragment instead, and the staged-A read stays inside the staged slice.
   auto run_compute = [&](int run, const u32x4 (&afr)[ASTAGE ? 1 : KPW][4], const WFrag<FMT> (&wf)[KPW][CB]) {
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
-      if (run + u < w_end) {
+      const bool valid = run + u < w_end;
+      if (MULTI || valid) {
         u32x4 al[4];
         if constexpr (ASTAGE) {
-          const uint16_t* ap = arow_l + (run + u - kb_begin) * 128;
+          const int kbl = MULTI ? min(run + u, kb_end - 1) : run + u;
+          const uint16_t* ap = arow_l + (kbl - kb_begin) * 128;
 #pragma unroll
           for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const u32x4*>(ap + 32 * t);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) al[t] = afr[ASTAGE ? 0 : u][t];
+        }
+        if constexpr (MULTI) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) al[t] = valid ? al[t] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
@@ -105,7 +123,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
           if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const u32x4 av = ASTAGE ? al[t] : afr[ASTAGE ? 0 : u][t];
+            const u32x4 av = al[t];
             acc[c][DEC_ACC2 ? (t & 1) : 0] = mfma<FMT>(av, bfrag<FMT, G>(wf[u][c], t, fs), acc[c][DEC_ACC2 ? (t & 1) : 0]);
           }
         }
@@ -114,28 +132,39 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
     }
   };
 
-  {   // first run: every wavefront, with or without k blocks, also stages A and syncs
-    u32x4 afr[ASTAGE ? 1 : KPW][4];
-    WFrag<FMT> wf[KPW][CB];
-    run_loads(w_begin, afr, wf);
-    if constexpr (ASTAGE) {
+  u32x4 afr[MULTI ? 2 : 1][ASTAGE ? 1 : KPW][4];
+  WFrag<FMT> wf[MULTI ? 2 : 1][KPW][CB];
+  // first run: every wavefront, with or without k blocks, also stages A and syncs
+  run_loads(w_begin, afr[0], wf[0]);
+  if constexpr (ASTAGE) {
 #pragma unroll
-      for (int i = 0; i < SCH; ++i)
-        if (soff[i] >= 0) *reinterpret_cast<u32x4*>(a_lds + soff[i]) = stage[i];
-      __syncthreads();
-    }
-    if (w_begin < w_end) run_compute(w_begin, afr, wf);
+    for (int i = 0; i < SCH; ++i)
+      if (soff[i] >= 0) *reinterpret_cast<u32x4*>(a_lds + soff[i]) = stage[i];
+    __syncthreads();
   }
-  for (int run = w_begin + KPW; run < w_end; run += KPW) {
-    u32x4 afr[ASTAGE ? 1 : KPW][4];
-    WFrag<FMT> wf[KPW][CB];
-    run_loads(run, afr, wf);
-    run_compute(run, afr, wf);
+  if constexpr (!MULTI) {
+    if (w_begin < w_end) run_compute(w_begin, afr[0], wf[0]);
+    for (int run = w_begin + KPW; run < w_end; run += KPW) {
+      run_loads(run, afr[0], wf[0]);
+      run_compute(run, afr[0], wf[0]);
+    }
+  } else {
+    run_loads(w_begin + KPW, afr[1], wf[1]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      run_compute(w_begin + r * KPW, afr[r & 1], wf[r & 1]);
+      if (r + 2 < NR) run_loads(w_begin + (r + 2) * KPW, afr[r & 1], wf[r & 1]);
+    }
   }
 
 #pragma unroll
   for (int c = 0; c < CB; ++c) red[wave][c][lane] = DEC_ACC2 ? acc[c][0] + acc[c][1] : acc[c][0];
-  __syncthreads();
+  // Barrier without the release fence of __syncthreads(): that fence would also wait for
+  // the clamped re-loads still in flight; the LDS writes above are what must land.
+  __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): vmcnt and expcnt left open
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   const bool active = tid < CB * 64;
   const int c = tid >> 6, ln = tid & 63;
   f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -157,13 +186,23 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   }
 }
 
+template <int FMT, int G, int CB, int KPW, bool ASTAGE>
+void launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
+  const dim3 grid(pl.grid_x, pl.grid_y), block(64 * QGEMM_DEC_NW);
+  switch (pl.nruns) {
+    case 2: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 2>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 3>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 4>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 1>), grid, block, 0, stream, a);
+  }
+}
+
 template <int FMT, int G, int CB, int KPW>
 void launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  const dim3 grid(pl.grid_x, pl.grid_y);
   if (pl.astage)
-    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, true>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
+    launch_nr<FMT, G, CB, KPW, true>(pl, a, stream);
   else
-    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, false>), grid, dim3(64 * QGEMM_DEC_NW), 0, stream, a);
+    launch_nr<FMT, G, CB, KPW, false>(pl, a, stream);
 }
 
 template <int FMT, int G>

@@ -154,15 +154,25 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d leaves %d k blocks per slice; the decode kernel "
                   "stages at most %d at M=%lld", p->split_k_hint, pl->kb_per_split, max_kb, (long long)p->M);
     // Each wavefront owns ceil(kb_per_split / waves) consecutive k blocks, streamed in runs
-    // of KPW (at most 8 weight blocks in flight per wavefront).
+    // of KPW (at most 8 weight blocks in flight per wavefront): the whole share in one run
+    // when an instance exists for it, else the largest instance below.  A share longer
+    // than one run alternates two register sets, each KPW x (4 A fragments unless A is
+    // staged + CB weight fragments of 5 registers, FP8 8); the run is shortened until both
+    // sets fit in 210 registers (measured: more spills).
     const int share = ceil_div(pl->kb_per_split, kDecodeWaves);
-    const int cap = 8 / pl->cb;
+    static const int kRuns[] = {8, 5, 4, 2, 1};            // instantiated KPW values
+    auto instantiated = [&](int k) {
+      return k * pl->cb <= 8 && (k != 5 || pl->cb == 1) && (k != 8 || pl->cb == 1);
+    };
+    auto fits_twice = [&](int k) {
+      const int wregs = pl->fmt == FMT_FP8 ? 8 : 5;
+      return 2 * k * ((pl->astage ? 0 : 16) + pl->cb * wregs) <= 210;
+    };
     pl->kpw = 1;
-    if (share <= cap && (share == 8 || share == 5 || share == 4 || share == 2 || share == 1) && (pl->cb == 1 || share != 5))
-      pl->kpw = share;
-    else
-      for (int k = cap; k >= 1; k /= 2)
-        if (k <= share) { pl->kpw = k; break; }
+    for (int k : kRuns)
+      if (instantiated(k) && k <= share && (k == share || (k < share && fits_twice(k)))) { pl->kpw = k; break; }
+    const int runs = ceil_div(share, pl->kpw);
+    pl->nruns = runs >= 2 && runs <= 4 ? runs : 1;
     pl->grid_x = (unsigned)groups;
     pl->grid_y = (unsigned)pl->splits;
     pl->tiles = groups;

@@ -47,6 +47,7 @@ struct Plan {
   // decode: column blocks (16 columns each) per workgroup, k blocks per wavefront run
   int cb, kpw;
   bool astage;            // decode: stage the A slice in LDS (small M)
+  int nruns;              // decode: runs per wavefront share, pipelined when 2..4 (else 1)
   // prefill: workgroup tile (bm == pf_bm(kPfLarge) selects the large shape)
   int bm, bn;
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
