@@ -77,7 +77,9 @@ typedef enum qgemm_scale_layout {
  * The problem descriptor, after the BitBLAS MatmulConfig (Bitblas lecture 033, API
  * example): sizes, operand dtypes, group size and scale layout.  Fields are fixed-width
  * so the struct has the same layout from C, C++ and ctypes (56 bytes).
- *   M >= 1 (any value); N % 16 == 0; K % 128 == 0; for INT4 also K % group_size == 0.
+ *   M >= 0 (any value; M = 0 is an empty product: qgemm_run validates the descriptor and
+ *   enqueues nothing, ignoring the pointers); N % 16 == 0; K % 128 == 0; for INT4 also
+ *   K % group_size == 0.  Each of M, N, K is at most 2^24.
  *   group_size: INT4 only, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
  *   slices (1..64) the chosen kernel uses; tile_hint: 0 = automatic, else for the decode

@@ -36,7 +36,11 @@ def test_status_strings_and_version():
 
 
 BAD = [
-    (dict(M=0, N=256, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "M must be"),
+    (dict(M=-1, N=256, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "M must be"),
+    (dict(M=(1 << 24) + 1, N=256, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "M must be"),
+    (dict(M=1, N=(1 << 24) + 16, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "N must be"),
+    (dict(M=1, N=256, K=(1 << 24) + 128, fmt="int4"), q.ERR_INVALID_ARGUMENT, "K must be"),
+    (dict(M=4096, N=256, K=1 << 23, fmt="int4"), q.ERR_UNSUPPORTED, "prefill kernel needs"),
     (dict(M=1, N=250, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "N must be"),
     (dict(M=1, N=256, K=500, fmt="int4"), q.ERR_INVALID_ARGUMENT, "K must be"),
     (dict(M=1, N=256, K=640, fmt="int4", group_size=256), q.ERR_INVALID_ARGUMENT, "multiple of group_size"),
@@ -59,6 +63,17 @@ def test_validation_errors(kw, status, text):
         q.workspace_bytes(p)
     assert ei.value.status == status
     assert text in ei.value.detail
+
+
+def test_empty_product_needs_nothing_and_launches_nothing():
+    # M = 0: no workspace; qgemm_run validates the descriptor and returns without touching
+    # (or checking) any pointer, so it needs no GPU.
+    for fmt in ("int4", "fp8", "fp4"):
+        p = q.problem(0, 256, 512, fmt)
+        assert q.workspace_bytes(p) == 0
+        assert q.run_raw(p, None, None, None, None, None, None, 0, None) == q.OK
+    p = q.problem(0, 250, 512, "int4")               # the descriptor is still checked
+    assert q.run_raw(p, None, None, None, None, None, None, 0, None) == q.ERR_INVALID_ARGUMENT
 
 
 def test_bad_enums_and_hints():

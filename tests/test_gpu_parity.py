@@ -207,3 +207,31 @@ def test_int4_closed_form_equal_nibbles_unit_scales(q):
             assert not y.any()
         else:
             tolerance.check_e1_e2(y, want)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+def test_empty_m_enqueues_nothing(q, fmt):
+    # M = 0 is an empty product: the call succeeds and writes nothing (the output buffer
+    # handed over here has a row of sentinels that must survive).
+    N, K = 256, 512
+    say(f"case empty-m fmt={fmt}")
+    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (55, N, K))
+    dt = torch.float16 if fmt == "int4" else torch.bfloat16
+    A = torch.zeros((1, K), dtype=dt, device="cuda")
+    out = torch.full((1, N), 7.0, dtype=dt, device="cuda")
+    p = q.problem(0, N, K, fmt, group_size=128 if fmt == "int4" else None)
+    q.run(p, A, prep.w, prep.s, None if fmt == "int4" else prep.alpha_t, out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("fmt,G", [("int4", 128), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 131072), (16, 256, 131072), (300, 32, 65536)])
+def test_long_k(q, fmt, G, M, N, K):
+    # Long reductions: M = 1 needs many K slices to keep its staged A slice within LDS;
+    # M = 16 streams A fragments over a long share; the prefill case splits K deeply.
+    say(f"case long-k fmt={fmt} G={G} M={M} N={N} K={K}")
+    prep = Prepared(q, fmt, N, K, G or 0, (56, N, K))
+    A = _act(fmt, M, K, (56, M))
+    st, _ = check_against_oracle(q, prep, A)
+    say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")

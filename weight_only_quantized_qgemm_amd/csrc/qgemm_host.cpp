@@ -54,8 +54,8 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "dtype value %d is not a qgemm_dtype_t", d);
   if (p->scale_layout < QGEMM_SCALE_GROUP_F16 || p->scale_layout > QGEMM_SCALE_BLOCK16_E4M3)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "scale_layout %d is not a qgemm_scale_layout_t", p->scale_layout);
-  if (p->M < 1 || p->M > kMaxDim)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "M must be in [1, %lld], got %lld", (long long)kMaxDim, (long long)p->M);
+  if (p->M < 0 || p->M > kMaxDim)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "M must be in [0, %lld], got %lld", (long long)kMaxDim, (long long)p->M);
   if (p->N < 16 || p->N % 16 || p->N > kMaxDim)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "N must be a positive multiple of 16 (<= %lld), got %lld",
                 (long long)kMaxDim, (long long)p->N);
@@ -120,6 +120,7 @@ static void finish_split(Plan* pl, int kblocks, int requested) {
 qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
   std::memset(pl, 0, sizeof(*pl));
   pl->fmt = format_of(p);
+  if (p->M == 0) return QGEMM_OK;                    // empty product: no launch, no workspace
   const int kblocks = (int)(p->K / 128);
   const int nblocks = (int)(p->N / 16);
   const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);

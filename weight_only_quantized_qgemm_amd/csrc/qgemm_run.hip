@@ -17,6 +17,7 @@ extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, con
   clear_error();
   qgemm_status_t st = validate_problem(p);
   if (st != QGEMM_OK) return st;
+  if (p->M == 0) return QGEMM_OK;                    // empty product: nothing to enqueue
   const Format fmt = format_of(p);
   if (!A) return fail(QGEMM_ERR_INVALID_ARGUMENT, "A is NULL");
   if (!w_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed is NULL");
