@@ -80,7 +80,7 @@ def test_bad_enums_and_hints():
     p = q.problem(1, 256, 512, "int4")
     p.a_dtype = 17
     assert q.run_raw(p, 16, 16, 16, None, 16, None, 0, None) == q.ERR_INVALID_ARGUMENT
-    p = q.problem(1, 256, 512, "int4", tile_hint=3)
+    p = q.problem(1, 256, 512, "int4", tile_hint=5)
     assert q.run_raw(p, 16, 16, 16, None, 16, None, 0, None) == q.ERR_INVALID_ARGUMENT
     p = q.problem(64, 256, 512, "int4", tile_hint=1)
     assert q.run_raw(p, 16, 16, 16, None, 16, None, 0, None) == q.ERR_INVALID_ARGUMENT

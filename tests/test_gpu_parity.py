@@ -116,7 +116,8 @@ def test_m_sweep_ragged(q, fmt, G, M):
 
 @pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
 @pytest.mark.parametrize("M,hint,split,tile", [(16, 1, 2, 0), (16, 1, 3, 1), (16, 1, 7, 2), (16, 1, 14, 4),
-                                               (4, 1, 1, 4), (4, 1, 5, 1), (16, 2, 1, 0), (16, 2, 2, 0),
+                                               (4, 1, 1, 4), (4, 1, 5, 1), (16, 1, 1, 3), (16, 1, 4, 3),
+                                               (3, 1, 2, 3), (16, 2, 1, 0), (16, 2, 2, 0),
                                                (16, 2, 5, 0)])
 def test_split_k_and_kernel_hints(q, fmt, M, hint, split, tile):
     N, K = 256, 1792    # 14 k blocks

@@ -217,6 +217,8 @@ struct DecodeLauncher {
       case 32 + 4: launch_cb<FMT, G, 2, 4>(pl, a, stream); break;
       case 32 + 2: launch_cb<FMT, G, 2, 2>(pl, a, stream); break;
       case 32 + 1: launch_cb<FMT, G, 2, 1>(pl, a, stream); break;
+      case 48 + 2: launch_cb<FMT, G, 3, 2>(pl, a, stream); break;
+      case 48 + 1: launch_cb<FMT, G, 3, 1>(pl, a, stream); break;
       case 64 + 2: launch_cb<FMT, G, 4, 2>(pl, a, stream); break;
       case 64 + 1: launch_cb<FMT, G, 4, 1>(pl, a, stream); break;
       default: return hipErrorInvalidConfiguration;

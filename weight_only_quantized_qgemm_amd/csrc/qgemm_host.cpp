@@ -95,8 +95,8 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d exceeds the %lld 128-wide K blocks",
                 p->split_k_hint, (long long)(p->K / 128));
   const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
-  if (decode && p->tile_hint != 0 && p->tile_hint != 1 && p->tile_hint != 2 && p->tile_hint != 4)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the decode kernel must be 0, 1, 2 or 4, got %d", p->tile_hint);
+  if (decode && (p->tile_hint < 0 || p->tile_hint > 4))
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the decode kernel must be 0 to 4, got %d", p->tile_hint);
   if (!decode && p->tile_hint != 0 && p->tile_hint != pf_bm(kPfMedium) && p->tile_hint != pf_bm(kPfLarge))
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the prefill kernel must be 0, %d or %d, got %d",
                 pf_bm(kPfMedium), pf_bm(kPfLarge), p->tile_hint);
@@ -132,11 +132,11 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->astage = p->M <= 4;
     // Column blocks per workgroup.  Every workgroup reads all M x K of A once, so wider
     // workgroups cut A traffic; narrower ones put more compute units to work.  M = 1: A is
-    // negligible, one block each.  M <= 4: two.  Larger M: the fewest blocks (1, 2 or 4)
+    // negligible, one block each.  M <= 4: two.  Larger M: the fewest blocks (1 to 4)
     // that keep the grid within one workgroup per compute unit.
     int cb = 1;
     if (p->M > 4) {
-      while (cb < 4 && ceil_div(nblocks, cb) > kCUs) cb *= 2;
+      while (cb < 4 && ceil_div(nblocks, cb) > kCUs) ++cb;
     } else if (p->M > 1) {
       cb = 2;
     }
