@@ -9,14 +9,19 @@ namespace {
 // M <= 16.  Workgroup = NW wavefronts; it owns CB column blocks (16 columns each) and one
 // K slice (normally all of K: a split-K hand-off costs three dependent memory round trips,
 // more than a whole small GEMM).  Wavefront w owns a contiguous share of the slice's k
-// blocks, streamed in runs of up to KPW blocks: all weight and scale loads of a run are
-// issued before any is consumed, and the k blocks are then consumed in load order, so each
-// waits only for its own data.
-// A fragments: with ASTAGE (small M) every thread first loads distinct 16-byte chunks of the
-// A slice (M rows, at most 32 KiB) into LDS, because a wave's fragment loads would otherwise
-// fetch each A value 16 times; otherwise (rows all distinct) each wavefront loads its
-// fragments from global memory before the run's weights.  Rows at or beyond M read row
-// M - 1 (MFMA output row m depends on A row m only; rows >= M are never stored).
+// blocks, streamed in runs of up to KPW blocks: all weight loads of a run are issued before
+// any is consumed, and the k blocks are then consumed in load order, so each waits only for
+// its own data.
+//
+// With ASTAGE (small M) each wavefront first stages its own share of A (M rows) and of the
+// packed scales into a private LDS region, in 16-byte chunks, one load instruction per 64
+// chunks: the MFMA fragment loads would otherwise fetch each A value 16 times, and the
+// compute unit's vector-memory pipeline spends about the same time on a load instruction
+// however few distinct bytes it carries.  Nothing staged is shared between wavefronts, so no
+// workgroup barrier holds a wavefront back once its own data has arrived.  With larger M
+// the rows are distinct: each wavefront loads its A fragments and its scales from global
+// memory with its weights.  Rows at or beyond M read row M - 1 (MFMA output row m depends
+// on A row m only; rows >= M are never stored).
 // Control flow is wavefront-uniform and loads are clamped rather than predicated (the
 // compiler waits for every outstanding load at the end of a branch that contains one).
 // Each wavefront keeps two accumulators per column block (even / odd K steps) to halve the
@@ -26,16 +31,17 @@ namespace {
 // trips.  The runs are unrolled (a loop carrying loads across its back edge defeats the
 // compiler's wait tracking, which then drains every load at the loop head).  NR = 1: one
 // run, or, for shares longer than four runs, runs one after another.
-constexpr int DEC_A_CHUNKS = 2048;                  // 32 KiB of staged A per workgroup
 constexpr bool DEC_ACC2 = true;                     // two accumulators per column block
 
 template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE, int NR>
 __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   constexpr bool MULTI = NR > 1;
   constexpr int NT = 64 * NW;
-  constexpr int SCH = ASTAGE ? DEC_A_CHUNKS / NT : 1;   // staging chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t a_lds[ASTAGE ? DEC_A_CHUNKS * 8 + 16 * 8 : 8];
-  __shared__ f32x4 red[NW][CB][64];
+  // Scales are staged with the A share (small M); otherwise each wavefront loads its own
+  // with its weights (staging them alone measured slower at M = 16).
+  constexpr bool HAS_S = FMT != qgemm::FMT_FP8 && ASTAGE;
+  constexpr bool STAGE = ASTAGE;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dec_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = blockIdx.x, split = blockIdx.y;
@@ -43,43 +49,88 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   const int kb_begin = split * a.kb_per_split;
   const int kb_end = min(KB, kb_begin + a.kb_per_split);
   const int nb0 = group * CB;
-  const int kslice = (kb_end - kb_begin) * 128;     // halves per A row in this slice
-  const int lda = kslice + 8;                        // LDS row stride (halves)
   // this wavefront's contiguous share of the slice
   const int share = (kb_end - kb_begin + NW - 1) / NW;
   const int w_begin = min(kb_end, kb_begin + wave * share);
   const int w_end = min(kb_end, w_begin + share);
   const int row = min(lane & 15, a.M - 1);
+  const int s_col = sc_rel<FMT, G>(KB);              // scale bytes of one whole column block
 
-  int soff[SCH];
-  u32x4 stage[SCH];
+  // LDS: one private region per wavefront ([its A share: M rows of share x 128 + 8 halves]
+  // [its scales: CB x SW bytes]), then the wave tiles of the final reduction.
+  const int ldw = share * 128 + 8;                   // LDS A row stride (halves)
+  const int aw_bytes = ASTAGE ? ((a.M * ldw * 2 + 15) & ~15) : 0;
+  const int SW = HAS_S ? sc_span<FMT, G>(share) : 0;   // scale bytes of a share, per column block (bound)
+  const int region = aw_bytes + ((CB * SW + 15) & ~15);
+  unsigned char* w_lds = dec_lds + wave * region;
+  const unsigned char* s_lds = w_lds + aw_bytes;
+  f32x4* red = reinterpret_cast<f32x4*>(dec_lds + NW * region);     // [NW][CB][64]
+
+  // Staging of this wavefront's share, 16-byte chunks through buffer loads (32-bit offsets):
+  // the A share (chunk q: row q / cpr, chunk q % cpr of the row), then its scales (chunk q:
+  // column block q / spc, chunk q % spc of its range).  Iteration i covers chunks 64 i .. + 63
+  // and is skipped (wavefront-uniformly) when all of them are past the end; lanes past the end
+  // re-load the last chunk and write nothing.  Nothing here is shared with other wavefronts,
+  // so no workgroup barrier delays the first k block.
+  constexpr int SA = ASTAGE ? qgemm::kDecodeStageA : 0, SS = HAS_S ? qgemm::kDecodeStageS : 0;
+  const int nkw = w_end - w_begin;                   // k blocks of this share (may be 0)
+  const int cpr = nkw * 16;
+  const int a_chunks = ASTAGE ? a.M * cpr : 0;
+  const int sw0 = sc_rel<FMT, G>(w_begin);
+  const int spc = (sc_end<FMT, G>(w_end) - sw0) >> 4;
+  const int s_chunks = nkw > 0 ? CB * spc : 0;
+  int soff[SA + SS + 1];
+  u32x4 stage[SA + SS + 1];
   if constexpr (ASTAGE) {
-    const int cpr = kslice >> 3;                     // 16-byte chunks per row
-    const int chunks = a.M * cpr;                    // <= DEC_A_CHUNKS by the launch plan
-    const float inv_cpr = 1.0f / (float)cpr;
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.A + (size_t)w_begin * 128), (short)0, 0x7fffffff, 0x00020000);
+    const float inv = 1.0f / (float)max(cpr, 1);
 #pragma unroll
-    for (int i = 0; i < SCH; ++i) {                  // no branch around a load: surplus threads re-load the last chunk
-      const int q = tid + NT * i;
-      const int qq = min(q, chunks - 1);
-      const int r = (int)(((float)qq + 0.5f) * inv_cpr);
-      const int c8 = qq - r * cpr;
-      stage[i] = *reinterpret_cast<const u32x4*>(a.A + (size_t)r * a.K + (size_t)kb_begin * 128 + 8 * c8);
-      soff[i] = q < chunks ? r * lda + 8 * c8 : -1;
+    for (int i = 0; i < SA; ++i) {
+      soff[i] = -1;
+      if (64 * i < a_chunks) {
+        const int q = min(lane + 64 * i, a_chunks - 1);
+        int r = (int)(((float)q + 0.5f) * inv);
+        r -= r * cpr > q;
+        const int c8 = q - r * cpr;
+        stage[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, (r * a.K + 8 * c8) * 2, 0, 0));
+        if (lane + 64 * i < a_chunks) soff[i] = r * ldw * 2 + 16 * c8;
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (HAS_S) {
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(static_cast<const unsigned char*>(a.S) + (size_t)nb0 * s_col + sw0), (short)0,
+        0x7fffffff, 0x00020000);
+    const int cmax = NB - 1 - nb0;                   // last column block of the matrix, relative
+    const float inv = 1.0f / (float)max(spc, 1);
+#pragma unroll
+    for (int i = 0; i < SS; ++i) {
+      soff[SA + i] = -1;
+      if (64 * i < s_chunks) {
+        const int q = min(lane + 64 * i, s_chunks - 1);
+        int c = (int)(((float)q + 0.5f) * inv);
+        c -= c * spc > q;
+        const int o = q - c * spc;
+        stage[SA + i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, min(c, cmax) * s_col + 16 * o, 0, 0));
+        if (lane + 64 * i < s_chunks) soff[SA + i] = aw_bytes + c * SW + 16 * o;
+      }
+    }
+  }
+  if constexpr (STAGE) __builtin_amdgcn_sched_barrier(0);
 
   f32x4 acc[CB][2];
 #pragma unroll
   for (int c = 0; c < CB; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* arow_g = a.A + (size_t)row * a.K + 8 * (lane >> 4);
-  const uint16_t* arow_l = a_lds + row * lda + 8 * (lane >> 4);
+  const uint16_t* arow_l = reinterpret_cast<const uint16_t*>(w_lds) + row * ldw + 8 * (lane >> 4);
   const int last = max(w_end - 1, w_begin);          // clamp target (valid even for an empty share)
   const int kb_cap = min(last, KB - 1);
 
-  // one run: loads first (A fragments, then weights and scales), then the k blocks in
-  // load order, each waiting only for its own data
+  // one run: loads first (A fragments, then weights), then the k blocks in load order,
+  // each waiting only for its own data
   auto run_loads = [&](int run, u32x4 (&afr)[ASTAGE ? 1 : KPW][4], WFrag<FMT> (&wf)[KPW][CB]) {
     if constexpr (!ASTAGE) {
 #pragma unroll
@@ -92,21 +143,22 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
 #pragma unroll
     for (int u = 0; u < KPW; ++u)
 #pragma unroll
-      for (int c = 0; c < CB; ++c) load_wfrag<FMT, G>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
+      for (int c = 0; c < CB; ++c)
+        load_wfrag<FMT, G, true, !HAS_S>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
     __builtin_amdgcn_sched_barrier(0);
   };
   // MULTI: no branch around a k block (the compiler would wait for every load in flight,
   // the next run's included, at its end); a block past the share multiplies a zero A
-  // fragment instead, and the staged-A read stays inside the staged slice.
-  auto run_compute = [&](int run, const u32x4 (&afr)[ASTAGE ? 1 : KPW][4], const WFrag<FMT> (&wf)[KPW][CB]) {
+  // fragment instead, and the staged reads stay inside the staged slice.
+  auto run_compute = [&](int run, const u32x4 (&afr)[ASTAGE ? 1 : KPW][4], WFrag<FMT> (&wf)[KPW][CB]) {
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
       const bool valid = run + u < w_end;
       if (MULTI || valid) {
+        const int kbl = MULTI ? max(min(run + u, w_end - 1), w_begin) : run + u;   // inside the staged share
         u32x4 al[4];
         if constexpr (ASTAGE) {
-          const int kbl = MULTI ? min(run + u, kb_end - 1) : run + u;
-          const uint16_t* ap = arow_l + (kbl - kb_begin) * 128;
+          const uint16_t* ap = arow_l + (kbl - w_begin) * 128;
 #pragma unroll
           for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const u32x4*>(ap + 32 * t);
         } else {
@@ -119,6 +171,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
+          if constexpr (HAS_S) {
+            read_staged_scales<FMT, G>(s_lds + c * SW, kbl, w_begin, lane, wf[u][c]);
+            if constexpr (MULTI) {                   // a block past the share: zero weights, never NaN
+              wf[u][c].s[0] = valid ? wf[u][c].s[0] : 0u;
+              wf[u][c].s[1] = valid ? wf[u][c].s[1] : 0u;
+            }
+          }
           float fs[4] = {0.f, 0.f, 0.f, 0.f};
           if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[u][c].s[0], fs);
 #pragma unroll
@@ -134,13 +193,14 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
 
   u32x4 afr[MULTI ? 2 : 1][ASTAGE ? 1 : KPW][4];
   WFrag<FMT> wf[MULTI ? 2 : 1][KPW][CB];
-  // first run: every wavefront, with or without k blocks, also stages A and syncs
+  // first run (every wavefront, with or without k blocks), then the staged share lands in LDS
   run_loads(w_begin, afr[0], wf[0]);
-  if constexpr (ASTAGE) {
+  if constexpr (STAGE) {
 #pragma unroll
-    for (int i = 0; i < SCH; ++i)
-      if (soff[i] >= 0) *reinterpret_cast<u32x4*>(a_lds + soff[i]) = stage[i];
-    __syncthreads();
+    for (int i = 0; i < SA + SS; ++i)
+      if (soff[i] >= 0) *reinterpret_cast<u32x4*>(w_lds + soff[i]) = stage[i];
+    __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the wavefront's own LDS writes have landed
+    __builtin_amdgcn_wave_barrier();
   }
   if constexpr (!MULTI) {
     if (w_begin < w_end) run_compute(w_begin, afr[0], wf[0]);
@@ -158,7 +218,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   }
 
 #pragma unroll
-  for (int c = 0; c < CB; ++c) red[wave][c][lane] = DEC_ACC2 ? acc[c][0] + acc[c][1] : acc[c][0];
+  for (int c = 0; c < CB; ++c) red[(wave * CB + c) * 64 + lane] = DEC_ACC2 ? acc[c][0] + acc[c][1] : acc[c][0];
   // Barrier without the release fence of __syncthreads(): that fence would also wait for
   // the clamped re-loads still in flight; the LDS writes above are what must land.
   __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): vmcnt and expcnt left open
@@ -169,9 +229,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   const int c = tid >> 6, ln = tid & 63;
   f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
   if (active) {
-    v[0] = red[0][c][ln];
+    v[0] = red[c * 64 + ln];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v[0] += red[w][c][ln];
+    for (int w = 1; w < NW; ++w) v[0] += red[(w * CB + c) * 64 + ln];
   }
   if (a.splits > 1) {
     if (!splitk_finish<1, NT>(a, group, split, CB * 256, active, v)) return;
@@ -189,11 +249,12 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
 template <int FMT, int G, int CB, int KPW, bool ASTAGE>
 void launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
   const dim3 grid(pl.grid_x, pl.grid_y), block(64 * QGEMM_DEC_NW);
+  const size_t lds = pl.lds_bytes;
   switch (pl.nruns) {
-    case 2: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 2>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 3>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 4>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 1>), grid, block, 0, stream, a);
+    case 2: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 2>), grid, block, lds, stream, a); break;
+    case 3: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 3>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 4>), grid, block, lds, stream, a); break;
+    default: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 1>), grid, block, lds, stream, a);
   }
 }
 

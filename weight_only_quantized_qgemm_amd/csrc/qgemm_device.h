@@ -150,7 +150,7 @@ __device__ __forceinline__ u32x4 wload(const u32x4* p) {
   else return *p;
 }
 
-template <int FMT, int G, bool STREAM = true>
+template <int FMT, int G, bool STREAM = true, bool SCALES = true>
 __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int lane, WFrag<FMT>& f) {
   const int KB = a.K >> 7;
   if constexpr (FMT == qgemm::FMT_FP8) {
@@ -161,7 +161,9 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
     const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * KB + kb) * 1024) + lane;
     f.w[0] = wload<STREAM>(p);
   }
-  if constexpr (FMT == qgemm::FMT_INT4) {
+  if constexpr (!SCALES) {
+    return;
+  } else if constexpr (FMT == qgemm::FMT_INT4) {
     const uint16_t* S = static_cast<const uint16_t*>(a.S);
     const int c = lane & 15;
     if constexpr (G <= 128) {
@@ -182,6 +184,54 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
   } else if constexpr (FMT == qgemm::FMT_FP4) {
     const uint8_t* S = static_cast<const uint8_t*>(a.S);
     f.s[0] = *reinterpret_cast<const unsigned*>(S + (((size_t)nb * KB + kb) * 16 + (lane & 15)) * 8 + 4 * (lane >> 5));
+  }
+}
+
+// ----------------------------------------------------------------------------- scales
+// Byte offset, inside one column block's packed scales, of the scales k block kb uses
+// (INT4 with G = 256: of its group, which spans two k blocks); sc_rel(KB) is the size of one
+// column block's scales.  FP8 has none.
+template <int FMT, int G>
+__device__ __forceinline__ int sc_rel(int kb) {
+  if constexpr (FMT == qgemm::FMT_INT4) return G <= 128 ? kb * 32 * (128 / G) : (kb >> 1) * 32;
+  else if constexpr (FMT == qgemm::FMT_FP4) return kb * 128;
+  else return 0;
+}
+// End of the scale bytes that cover k blocks up to kb_end (exclusive); a group of 256 is kept whole.
+template <int FMT, int G>
+__device__ __forceinline__ int sc_end(int kb_end) {
+  return sc_rel<FMT, G>(FMT == qgemm::FMT_INT4 && G > 128 ? kb_end + 1 : kb_end);
+}
+
+// Scale bytes of one column block that nkb consecutive k blocks read, at most (INT4 with
+// G = 256: a run may start in the middle of a group).
+template <int FMT, int G>
+__device__ __forceinline__ int sc_span(int nkb) {
+  if constexpr (FMT == qgemm::FMT_INT4) return G <= 128 ? nkb * 32 * (128 / G) : 32 * (nkb / 2 + 1);
+  else if constexpr (FMT == qgemm::FMT_FP4) return nkb * 128;
+  else return 0;
+}
+
+// Scales of k block kb for this lane's column, from an LDS copy of one column block's packed
+// scales that starts with those of k block kb_begin.
+template <int FMT, int G>
+__device__ __forceinline__ void read_staged_scales(const unsigned char* s, int kb, int kb_begin, int lane,
+                                                   WFrag<FMT>& f) {
+  const unsigned char* p = s + (sc_rel<FMT, G>(kb) - sc_rel<FMT, G>(kb_begin));
+  if constexpr (FMT == qgemm::FMT_INT4) {
+    constexpr int T = G <= 128 ? 128 / G : 1;
+    p += (lane & 15) * T * 2;
+    if constexpr (T == 4) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+      f.s[0] = x[0];
+      f.s[1] = x[1];
+    } else if constexpr (T == 2) {
+      f.s[0] = *reinterpret_cast<const unsigned*>(p);
+    } else {
+      f.s[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  } else if constexpr (FMT == qgemm::FMT_FP4) {
+    f.s[0] = *reinterpret_cast<const unsigned*>(p + (lane & 15) * 8 + 4 * (lane >> 5));
   }
 }
 

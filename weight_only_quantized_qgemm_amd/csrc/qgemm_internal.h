@@ -28,6 +28,12 @@ constexpr int pf_bn(PfShape s) { return 16 * s.wgn * s.tn; }
 #define QGEMM_DEC_NW 8
 #endif
 constexpr int kDecodeWaves = QGEMM_DEC_NW;
+// Decode staging pass (A slice and scales into LDS): the largest staged A slice and scale
+// range per workgroup, and the 16-byte chunks per thread they take at most.
+constexpr int kDecodeMaxA = 32 * 1024;
+constexpr int kDecodeMaxScales = 16 * 1024;
+constexpr int kDecodeStageA = kDecodeMaxA / (16 * 64 * kDecodeWaves);
+constexpr int kDecodeStageS = kDecodeMaxScales / (16 * 64 * kDecodeWaves);
 
 enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
 enum Kind : int { KIND_DECODE = 1, KIND_PREFILL = 2 };
@@ -48,6 +54,7 @@ struct Plan {
   int cb, kpw;
   bool astage;            // decode: stage the A slice in LDS (small M)
   int nruns;              // decode: runs per wavefront share, pipelined when 2..4 (else 1)
+  int lds_bytes;          // decode: dynamic LDS per workgroup (staged A, staged scales, wave tiles)
   // prefill: workgroup tile (bm == pf_bm(kPfLarge) selects the large shape)
   int bm, bn;
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
