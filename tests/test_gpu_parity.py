@@ -47,14 +47,19 @@ def _dequant_16bit_values(fmt, prep):
 
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 64), ("int4", 128), ("int4", 256),
                                    ("fp8", None), ("fp4", None)])
-@pytest.mark.parametrize("hint", [1, 2])
-def test_identity_activations_give_dequantized_weights_bit_exact(q, fmt, G, hint):
+@pytest.mark.parametrize("hint,step", [(1, 16), (1, 4), (1, 1), (2, None)],
+                         ids=["decode-M16", "decode-M4", "decode-M1", "prefill"])
+def test_identity_activations_give_dequantized_weights_bit_exact(q, fmt, G, hint, step):
     N, K = 48, 512
-    say(f"case identity fmt={fmt} G={G} hint={hint}")
+    say(f"case identity fmt={fmt} G={G} hint={hint} rows={step}")
     prep = Prepared(q, fmt, N, K, G or 0, (7, N, K), alpha_override=1.0)
+    step = step or K
     want = _dequant_16bit_values(fmt, prep)              # [N, K]
-    step = 16 if hint == 1 else K
-    for k0 in range(0, K, step):
+    if step == 1:
+        k0s = list(range(0, K, 37)) + [K - 1]            # M = 1: a sample of single rows
+    else:
+        k0s = list(range(0, K, step))
+    for k0 in k0s:
         rows = list(range(k0, k0 + step))
         A = _identity_rows(fmt, rows, K)
         y32, _ = run_gpu(q, prep, A, q.DT_F32, kernel_hint=hint)

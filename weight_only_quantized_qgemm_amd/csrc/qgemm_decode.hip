@@ -56,12 +56,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   const int row = min(lane & 15, a.M - 1);
   const int s_col = sc_rel<FMT, G>(KB);              // scale bytes of one whole column block
 
-  // LDS: one private region per wavefront ([its A share: M rows of share x 128 + 8 halves]
-  // [its scales: CB x SW bytes]), then the wave tiles of the final reduction.
+  // LDS (layout shared with the launch plan): one private region per wavefront ([its A share:
+  // M rows of share x 128 + 8 halves][its scales: CB x SW bytes]), then the wave tiles of the
+  // final reduction.
   const int ldw = share * 128 + 8;                   // LDS A row stride (halves)
-  const int aw_bytes = ASTAGE ? ((a.M * ldw * 2 + 15) & ~15) : 0;
-  const int SW = HAS_S ? sc_span<FMT, G>(share) : 0;   // scale bytes of a share, per column block (bound)
-  const int region = aw_bytes + ((CB * SW + 15) & ~15);
+  const int aw_bytes = qgemm::dec_a_bytes(a.M, share, ASTAGE);
+  const int SW = HAS_S ? qgemm::dec_scale_span(FMT, G, share) : 0;   // scale bytes of a share, per column block
+  const int region = qgemm::dec_region_bytes(FMT, G, a.M, share, CB, ASTAGE);
   unsigned char* w_lds = dec_lds + wave * region;
   const unsigned char* s_lds = w_lds + aw_bytes;
   f32x4* red = reinterpret_cast<f32x4*>(dec_lds + NW * region);     // [NW][CB][64]

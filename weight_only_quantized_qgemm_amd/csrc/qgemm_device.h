@@ -203,15 +203,6 @@ __device__ __forceinline__ int sc_end(int kb_end) {
   return sc_rel<FMT, G>(FMT == qgemm::FMT_INT4 && G > 128 ? kb_end + 1 : kb_end);
 }
 
-// Scale bytes of one column block that nkb consecutive k blocks read, at most (INT4 with
-// G = 256: a run may start in the middle of a group).
-template <int FMT, int G>
-__device__ __forceinline__ int sc_span(int nkb) {
-  if constexpr (FMT == qgemm::FMT_INT4) return G <= 128 ? nkb * 32 * (128 / G) : 32 * (nkb / 2 + 1);
-  else if constexpr (FMT == qgemm::FMT_FP4) return nkb * 128;
-  else return 0;
-}
-
 // Scales of k block kb for this lane's column, from an LDS copy of one column block's packed
 // scales that starts with those of k block kb_begin.
 template <int FMT, int G>

@@ -109,16 +109,6 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // The chip has 256 compute units; grids are sized against that.
 static const int kCUs = 256;
 
-// Packed scale bytes of one column block that kb consecutive k blocks read (an upper bound
-// over their position: an INT4 group of 256 spans two k blocks and may be cut by a boundary).
-// The decode kernel lays out its LDS with the same bound.
-static int scale_slice_bytes(Format fmt, int group_size, int kb) {
-  if (fmt == FMT_FP4) return 128 * kb;
-  if (fmt == FMT_FP8) return 0;
-  if (group_size <= 128) return 32 * (128 / group_size) * kb;
-  return 32 * (kb / 2 + 1);
-}
-
 static void finish_split(Plan* pl, int kblocks, int requested) {
   int s = requested > 0 ? requested : pl->splits;
   if (s < 1) s = 1;
@@ -161,7 +151,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       const int share = ceil_div(kb, kDecodeWaves);
       return (!pl->astage || 2 * 128 * p->M * (int64_t)share * kDecodeWaves <= kDecodeMaxA) &&
              (!pl->astage ||
-              (int64_t)pl->cb * scale_slice_bytes(pl->fmt, p->group_size, share) * kDecodeWaves <= kDecodeMaxScales);
+              (int64_t)pl->cb * dec_scale_span(pl->fmt, p->group_size, share) * kDecodeWaves <= kDecodeMaxScales);
     };
     int max_kb = kblocks;
     while (max_kb > 1 && !staged_ok(max_kb)) --max_kb;
@@ -173,14 +163,8 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     if (pl->kb_per_split > max_kb)
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d leaves %d k blocks per slice; the decode kernel "
                   "stages at most %d at M=%lld", p->split_k_hint, pl->kb_per_split, max_kb, (long long)p->M);
-    {
-      // one private region per wavefront (its A share with rows padded by 8 halves, its
-      // scales), then the wave tiles of the final reduction
-      const int share = ceil_div(pl->kb_per_split, kDecodeWaves);
-      const int a_bytes = pl->astage ? (int)((p->M * (share * 128 + 8) * 2 + 15) / 16 * 16) : 0;
-      const int s_bytes = pl->astage ? (pl->cb * scale_slice_bytes(pl->fmt, p->group_size, share) + 15) / 16 * 16 : 0;
-      pl->lds_bytes = kDecodeWaves * (a_bytes + s_bytes) + kDecodeWaves * pl->cb * 64 * 16;
-    }
+    pl->lds_bytes = dec_lds_bytes(pl->fmt, p->group_size, (int)p->M, ceil_div(pl->kb_per_split, kDecodeWaves),
+                                  pl->cb, pl->astage, kDecodeWaves);
     // Each wavefront owns ceil(kb_per_split / waves) consecutive k blocks, streamed in runs
     // of KPW (at most 8 weight blocks in flight per wavefront): the whole share in one run
     // when an instance exists for it, else the largest instance below.  A share longer

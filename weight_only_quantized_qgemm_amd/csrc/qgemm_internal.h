@@ -36,6 +36,32 @@ constexpr int kDecodeStageA = kDecodeMaxA / (16 * 64 * kDecodeWaves);
 constexpr int kDecodeStageS = kDecodeMaxScales / (16 * 64 * kDecodeWaves);
 
 enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
+
+// ---- Decode LDS layout, shared by the launch plan (which sizes the allocation) and the kernel.
+// Packed scale bytes of one column block that nkb consecutive k blocks read, at most (an INT4
+// group of 256 spans two k blocks and may be cut by a boundary).
+constexpr int dec_scale_span(int fmt, int group_size, int nkb) {
+  return fmt == FMT_FP4 ? 128 * nkb
+         : fmt == FMT_FP8 ? 0
+         : group_size <= 128 ? 32 * (128 / group_size) * nkb
+                             : 32 * (nkb / 2 + 1);
+}
+// Per wavefront: its A share (M rows of share x 128 + 8 halves) and its scales (cb column
+// blocks), each padded to 16 bytes.
+constexpr int dec_a_bytes(int M, int share, bool astage) {
+  return astage ? (M * (share * 128 + 8) * 2 + 15) / 16 * 16 : 0;
+}
+constexpr int dec_s_bytes(int fmt, int group_size, int share, int cb, bool astage) {
+  return astage ? (cb * dec_scale_span(fmt, group_size, share) + 15) / 16 * 16 : 0;
+}
+constexpr int dec_region_bytes(int fmt, int group_size, int M, int share, int cb, bool astage) {
+  return dec_a_bytes(M, share, astage) + dec_s_bytes(fmt, group_size, share, cb, astage);
+}
+// Whole workgroup: the regions, then the wave tiles of the final reduction (64 lanes x 16 B
+// per wavefront and column block).
+constexpr int dec_lds_bytes(int fmt, int group_size, int M, int share, int cb, bool astage, int waves) {
+  return waves * dec_region_bytes(fmt, group_size, M, share, cb, astage) + waves * cb * 64 * 16;
+}
 enum Kind : int { KIND_DECODE = 1, KIND_PREFILL = 2 };
 
 // Records a detail message for qgemm_last_error() and returns `st`.
