@@ -66,20 +66,29 @@ struct KArgs {
 };
 
 // ----------------------------------------------------------------------------- dequant
-// (a & m) | o in one VALU op.  The compiler splits it into AND + OR because the two
-// constants cannot both be instruction operands; as VGPR operands they can.
-__device__ __forceinline__ unsigned and_or(unsigned a, unsigned m, unsigned o) {
+// (a & M) | O in one VALU op (v_and_or_b32).  With both constants as literals the compiler
+// splits it into AND + OR (an instruction takes one literal); held in registers they fit
+// one instruction.  The constants are moved into registers by an opaque (non-volatile,
+// hence shared) asm statement, and the operation itself stays in C so the compiler sees
+// every register it writes: an MFMA that reads a register a VALU op has just written needs
+// wait states, which the compiler inserts only for instructions it knows.
+template <unsigned C>
+__device__ __forceinline__ unsigned vconst() {
   unsigned r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(C));
   return r;
+}
+template <unsigned M, unsigned O>
+__device__ __forceinline__ unsigned and_or(unsigned a) {
+  return (a & vconst<M>()) | vconst<O>();
 }
 
 __device__ __forceinline__ u32x4 dq_int4(unsigned w, unsigned s2) {
   const unsigned hi = w >> 8;
-  const unsigned p0 = and_or(w, 0x000F000Fu, 0x64006400u);    // k slots j0, j1: 1024 + nibble
-  const unsigned p1 = and_or(w, 0x00F000F0u, 0x54005400u);    // j2, j3: 64 + nibble
-  const unsigned p2 = and_or(hi, 0x000F000Fu, 0x64006400u);   // j4, j5
-  const unsigned p3 = and_or(hi, 0x00F000F0u, 0x54005400u);   // j6, j7
+  const unsigned p0 = and_or<0x000F000Fu, 0x64006400u>(w);    // k slots j0, j1: 1024 + nibble
+  const unsigned p1 = and_or<0x00F000F0u, 0x54005400u>(w);    // j2, j3: 64 + nibble
+  const unsigned p2 = and_or<0x000F000Fu, 0x64006400u>(hi);   // j4, j5
+  const unsigned p3 = and_or<0x00F000F0u, 0x54005400u>(hi);   // j6, j7
   const f16x2 s = __builtin_bit_cast(f16x2, s2);
   const f16x2 big = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 small = {(_Float16)72.0f, (_Float16)72.0f};
