@@ -40,7 +40,7 @@ def log(msg):
 def weight_bytes(fmt, N, K, G):
     if fmt == "int4":
         return N * K // 2 + (K // G) * N * 2
-    if fmt == "fp8":
+    if fmt in ("fp8", "fp8h"):
         return N * K
     return N * K // 2 + N * K // 16
 
@@ -48,12 +48,12 @@ def weight_bytes(fmt, N, K, G):
 class Gemm:
     """One GEMM with rotating device copies of its packed weights."""
 
-    def __init__(self, q, torch, fmt, M, N, K, G, key, min_rotate_bytes):
+    def __init__(self, q, torch, fmt, M, N, K, G, key, min_rotate_bytes, with_bias=False):
         import synthetic
         self.fmt, self.M, self.N, self.K, self.G = fmt, M, N, K, G
         self.p = q.problem(M, N, K, fmt, group_size=G if fmt == "int4" else None)
         pq = q.problem(1, N, K, fmt, group_size=G if fmt == "int4" else None)
-        w = synthetic.weights(N, K, {"int4": 0.02, "fp8": 0.05, "fp4": 0.02}[fmt], key)
+        w = synthetic.weights(N, K, {"int4": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}[fmt], key)
         codes, scales, alpha = q.quantize(pq, w)            # the library's own quantizer
         wpk, spk = q.pack(pq, codes, scales)
         self.wbytes = weight_bytes(fmt, N, K, G)
@@ -64,9 +64,11 @@ class Gemm:
         self.w = [w0] + [w0.clone() for _ in range(ncopies - 1)]
         self.s = [s0] + [None if s0 is None else s0.clone() for _ in range(ncopies - 1)]
         self.alpha = torch.tensor([alpha], dtype=torch.float32, device="cuda")
-        self.A = synthetic.activations(M, K, "f16" if fmt == "int4" else "bf16", key).cuda()
-        odt = torch.float16 if fmt == "int4" else torch.bfloat16
+        kind = "f16" if fmt in ("int4", "fp8h") else "bf16"
+        self.A = synthetic.activations(M, K, kind, key).cuda()
+        odt = torch.float16 if kind == "f16" else torch.bfloat16
         self.out = torch.empty((M, N), dtype=odt, device="cuda")
+        self.bias = synthetic.bias(N, kind, key).cuda() if with_bias else None
         self.ws = q.alloc_workspace(self.p)
         self.i = 0
         self.q = q
@@ -75,7 +77,7 @@ class Gemm:
         c = self.i % len(self.w)
         self.i += 1
         self.q.run(self.p, self.A, self.w[c], self.s[c], None if self.fmt == "int4" else self.alpha,
-                   self.out, self.ws)
+                   self.out, self.ws, bias=self.bias)
 
     @property
     def flops(self):
@@ -178,7 +180,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--all", action="store_true", help="also time the FP8 and FP4 workloads")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the FP8, FP4 and FP8-with-fp16-activations (+bias) workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--counter-pass", nargs="?", const="decode", choices=("decode", "prefill"),
@@ -298,18 +301,20 @@ def main():
         torch.cuda.empty_cache()
 
     if args.all:
-        for name in ("fp8", "fp4"):
+        for name in ("fp8", "fp4", "fp8h"):
             wk = synthetic.WORKLOADS[name]
             wix = synthetic.WORKLOAD_INDEX[name]
             for si, (M, N, K) in enumerate(wk["shapes"]):
                 big = M >= 128
-                g = Gemm(q, torch, name, M, N, K, 0, (wix, si), (64 << 20) if big else rot)
+                g = Gemm(q, torch, name, M, N, K, 0, (wix, si), (64 << 20) if big else rot,
+                         with_bias=name == "fp8h")
                 n = 10 if big else 64
                 gg = graph_of(torch, g.launch, n)
                 ms = time_graph(torch, gg, 3) / n
                 tf = g.flops / (ms * 1e-3) / 1e12
                 gbs = g.wbytes / (ms * 1e-3) / 1e9
-                secondary.append({"gemm": f"{name} M={M} N={N} K={K}", "us_per_launch": round(ms * 1e3, 2),
+                label = f"{name} M={M} N={N} K={K}" + (" +bias" if name == "fp8h" else "")
+                secondary.append({"gemm": label, "us_per_launch": round(ms * 1e3, 2),
                                   "TFLOPs": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                   "weight_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
                 del gg, g

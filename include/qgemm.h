@@ -15,16 +15,20 @@
  *   BF16     FP8_E4M3       TENSOR_F32            BF16 or F32   FlashInfer PR #7495 analysis
  *                                                               (mm_bf16_fp8), introduction and
  *                                                               section 2 (public API)
+ *   F16      FP8_E4M3       TENSOR_F32            F16 or F32    the same analysis, section 2
+ *                                                               (mm_fp16_fp8)
  *   BF16     FP4_E2M1       BLOCK16_E4M3          BF16 or F32   FlashInfer PR #4466 analysis
  *                                                               (BF16 x FP4 GEMM), sections 1-3
  *
  * Value semantics (what the kernels compute):
  *   INT4 : w[k][n] = RNE_fp16((nibble - 8) * s[k / G][n]) -- the 16-bit operand the
  *          gemlite snippet forms -- accumulated in fp32.  No alpha.
- *   FP8  : w = e4m3(code) (exact in bf16); the fp32 per-tensor alpha multiplies the fp32
- *          accumulator once, in the epilogue, as the PR #7495 analysis prescribes.
+ *   FP8  : w = e4m3(code) (exact in bf16 and in fp16; the MFMA takes the activations'
+ *          type); the fp32 per-tensor alpha multiplies the fp32 accumulator once, in the
+ *          epilogue, as the PR #7495 analysis prescribes.
  *   FP4  : w = e2m1(code) * e4m3(s_b) (exact in bf16) with one scale per 16 consecutive
  *          K of a column; alpha multiplies the fp32 accumulator in the epilogue.
+ *   Bias (qgemm_run_bias): bias[n] is added in fp32 after alpha.
  *   The 16-bit output is the round-to-nearest-even cast of the fp32 result, so a call
  *   with out_dtype F32 yields exactly the values a 16-bit call rounds.
  *
@@ -81,6 +85,8 @@ typedef enum qgemm_scale_layout {
  *   enqueues nothing, ignoring the pointers); N % 16 == 0; K % 128 == 0; for INT4 also
  *   K % group_size == 0.  Each of M, N, K is at most 2^24.
  *   group_size: INT4 only, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
+ *   FP8 weights take a_dtype BF16 (mm_bf16_fp8) or F16 (mm_fp16_fp8); the packed weights
+ *   are the same for both.
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
  *   slices (1..64) the chosen kernel uses; tile_hint: 0 = automatic, else for the decode
  *   kernel the number of 16-column blocks per workgroup (1 to 4), for the prefill
@@ -172,6 +178,20 @@ qgemm_status_t qgemm_workspace_bytes(const qgemm_problem_t* problem, size_t* byt
 qgemm_status_t qgemm_run(const qgemm_problem_t* problem, const void* A, const void* w_packed,
                          const void* s_packed, const float* alpha, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * qgemm_run_bias -- enqueue out[m][n] = A . dequant(W) (* alpha) + bias[n] on `stream`, the
+ * bias argument of mm_bf16_fp8 / mm_fp16_fp8 (FlashInfer PR #7495 analysis, section 2),
+ * available for every format.  Arguments as qgemm_run, plus:
+ *   bias     device, N values of out_dtype (fp32 for out_dtype F32), 16-byte aligned (the
+ *            alignment that analysis, section 3(a), requires of a bias), else
+ *            QGEMM_ERR_MISALIGNED; NULL means no bias, and the call is then exactly qgemm_run.
+ * The bias is converted to fp32 (exact) and added to the fp32 result after alpha, before the
+ * one rounding to out_dtype.
+ */
+qgemm_status_t qgemm_run_bias(const qgemm_problem_t* problem, const void* A, const void* w_packed,
+                              const void* s_packed, const float* alpha, const void* bias, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* qgemm_status_string(qgemm_status_t status);

@@ -35,7 +35,10 @@ def dequant_int4_f16(codes, scale_bits, group_size):
 
 
 def dequant_fp8(codes):
-    """e4m3 code -> value (exact); alpha is NOT applied here.  Returns float32 [N, K]."""
+    """e4m3 code -> value (exact); alpha is NOT applied here.  Returns float32 [N, K].
+
+    The same values serve fp16 and bf16 activations (mm_fp16_fp8 and mm_bf16_fp8): every
+    e4m3 value is exact in both 16-bit formats."""
     return codecs.e4m3_decode(codes).astype(np.float32)
 
 
@@ -46,14 +49,21 @@ def dequant_fp4(codes, sf_codes):
     return (v * np.repeat(s, 16, axis=1)).astype(np.float32)
 
 
-def gemm_fp64(a_values, wdq_nk, alpha=1.0):
-    """R = (A . Wdq^T) * alpha in float64.  a_values [M, K], wdq_nk [N, K]."""
+def gemm_fp64(a_values, wdq_nk, alpha=1.0, bias=None):
+    """R = (A . Wdq^T) * alpha (+ bias[n]) in float64.  a_values [M, K], wdq_nk [N, K].
+
+    The bias is the optional bias argument of mm_bf16_fp8 / mm_fp16_fp8 (FlashInfer PR
+    #7495 analysis, section 2), one value per output column, added after alpha.
+    """
     a = np.asarray(a_values, dtype=np.float64)
     w = np.asarray(wdq_nk, dtype=np.float64)
-    return (a @ w.T) * float(alpha)
+    r = (a @ w.T) * float(alpha)
+    if bias is not None:
+        r = r + np.asarray(bias, dtype=np.float64)[None, :]
+    return r
 
 
-def gemm_fp64_rows(a_values, wdq_nk, rows, alpha=1.0):
+def gemm_fp64_rows(a_values, wdq_nk, rows, alpha=1.0, bias=None):
     """Reference for a subset of output rows (sampled checks at full size)."""
     a = np.asarray(a_values, dtype=np.float64)[np.asarray(rows)]
-    return gemm_fp64(a, wdq_nk, alpha)
+    return gemm_fp64(a, wdq_nk, alpha, bias)

@@ -5,14 +5,17 @@ casts activations to their 16-bit type with torch's own cast.  Quantization, pac
 the GEMM live in the library (GPU path) and, independently, in the oracle.
 
 Workloads (LLM linear layers; no dataset or trained weights are involved):
-  A ~ N(0, 1) cast to fp16 (INT4 shapes) or bf16 (FP8 / FP4 shapes);
+  A ~ N(0, 1) cast to fp16 (INT4 shapes, FP8 with fp16 activations) or bf16 (FP8 / FP4
+  shapes);
   W ~ N(0, sigma) in fp32, sigma = 0.02 (INT4, FP4) or 0.05 (FP8), drawn in the
   "nt" orientation [N, K] (row n = output column n).
-Seeds are numpy ``default_rng([workload, shape, role])`` with role 0 = A, 1 = W.
+  a bias (the bias argument of mm_bf16_fp8 / mm_fp16_fp8) ~ N(0, 0.1) per output column,
+  cast to the output's 16-bit type.
+Seeds are numpy ``default_rng([workload, shape, role])`` with role 0 = A, 1 = W, 2 = bias.
 """
 import numpy as np
 
-ROLE_A, ROLE_W = 0, 1
+ROLE_A, ROLE_W, ROLE_BIAS = 0, 1, 2
 
 # named workloads: (name, format, list of (M, N, K), extra)
 WORKLOADS = {
@@ -27,6 +30,9 @@ WORKLOADS = {
                 group_sizes=[0], sigma=0.05),
     "fp4": dict(fmt="fp4", shapes=[(1, 8192, 8192), (128, 8192, 8192), (8192, 8192, 8192)],
                 group_sizes=[16], sigma=0.02),
+    # mm_fp16_fp8: the FP8 layer shapes with fp16 activations and a bias
+    "fp8h": dict(fmt="fp8h", shapes=[(1, 10240, 5120), (16, 10240, 5120), (8192, 10240, 5120)],
+                 group_sizes=[0], sigma=0.05),
 }
 WORKLOAD_INDEX = {name: i for i, name in enumerate(WORKLOADS)}
 
@@ -48,3 +54,10 @@ def weights(N, K, sigma, key):
     w = rng(*key, ROLE_W).standard_normal((N, K), dtype=np.float32)
     w *= np.float32(sigma)
     return w
+
+
+def bias(N, kind, key):
+    """bias ~ N(0, 0.1) as a CPU torch tensor [N] of dtype fp16 ('f16') or bf16 ('bf16')."""
+    import torch
+    x = rng(*key, ROLE_BIAS).standard_normal(N, dtype=np.float32) * np.float32(0.1)
+    return torch.from_numpy(x).to(torch.float16 if kind == "f16" else torch.bfloat16)

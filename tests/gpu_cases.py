@@ -8,8 +8,8 @@ import numpy as np
 import synthetic
 from oracle import codecs, quant, reference, tolerance
 
-FMT_ACT = {"int4": "f16", "fp8": "bf16", "fp4": "bf16"}
-SIGMA = {"int4": 0.02, "fp8": 0.05, "fp4": 0.02}
+FMT_ACT = {"int4": "f16", "fp8": "bf16", "fp8h": "f16", "fp4": "bf16"}
+SIGMA = {"int4": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}
 
 
 def say(msg):
@@ -24,7 +24,7 @@ def oracle_weights(fmt, N, K, G, key):
     if fmt == "int4":
         codes, sbits = quant.quantize_int4(w, G)
         return quant.pack_nibbles(codes), sbits, 1.0, reference.dequant_int4(codes, sbits, G)
-    if fmt == "fp8":
+    if fmt in ("fp8", "fp8h"):           # one quantization for both activation types
         codes, alpha = quant.quantize_fp8(w)
         return codes, None, alpha, reference.dequant_fp8(codes)
     codes, sf, alpha = quant.quantize_fp4(w)
@@ -52,8 +52,11 @@ class Prepared:
         self.alpha_t = torch.tensor([self.alpha], dtype=torch.float32, device="cuda")
 
 
-def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=None, tile_hint=0):
-    """Run through the C ABI; returns (out as numpy float64 or 16-bit bits, the workspace)."""
+def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=None, tile_hint=0, bias=None):
+    """Run through the C ABI; returns (out as numpy float64 or 16-bit bits, the workspace).
+
+    bias: optional CPU tensor [N] (16-bit); it is passed in out_dtype (fp32 for F32 output,
+    an exact widening), through qgemm_run_bias."""
     import torch
     M, K = A16.shape
     p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt == "int4" else None,
@@ -64,7 +67,8 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     A = A16.cuda()
     if workspace is None:
         workspace = q.alloc_workspace(p)
-    q.run(p, A, prep.w, prep.s, None if prep.fmt == "int4" else prep.alpha_t, out, workspace)
+    b = None if bias is None else bias.to(tdt).cuda()
+    q.run(p, A, prep.w, prep.s, None if prep.fmt == "int4" else prep.alpha_t, out, workspace, bias=b)
     torch.cuda.synchronize()
     o = out.cpu()
     if out_dtype == q.DT_F32:
@@ -72,30 +76,31 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     return o.view(torch.int16).numpy().view(np.uint16), workspace
 
 
-def ref_rows(prep, A16, rows):
-    return reference.gemm_fp64_rows(a_values(A16), prep.wdq, rows, prep.alpha)
+def ref_rows(prep, A16, rows, bias=None):
+    b = None if bias is None else a_values(bias)
+    return reference.gemm_fp64_rows(a_values(A16), prep.wdq, rows, prep.alpha, b)
 
 
 def out16_kind(fmt):
-    return "f16" if fmt == "int4" else "bf16"
+    return "f16" if fmt in ("int4", "fp8h") else "bf16"
 
 
 def out16_dtype(q, fmt):
-    return q.DT_F16 if fmt == "int4" else q.DT_BF16
+    return q.DT_F16 if fmt in ("int4", "fp8h") else q.DT_BF16
 
 
 def out16_values(bits, fmt):
-    return codecs.f16_from_bits(bits) if fmt == "int4" else codecs.bf16_from_bits(bits)
+    return codecs.f16_from_bits(bits) if out16_kind(fmt) == "f16" else codecs.bf16_from_bits(bits)
 
 
-def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0, tile_hint=0):
+def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0, tile_hint=0, bias=None):
     """E1/E2 on the fp32 output, E2 on the 16-bit output, E3 between them."""
     M = A16.shape[0]
     rows = np.arange(M) if rows is None else np.asarray(rows)
-    y32, ws = run_gpu(q, prep, A16, q.DT_F32, kernel_hint, split_k_hint, tile_hint=tile_hint)
-    r = ref_rows(prep, A16, rows)
+    y32, ws = run_gpu(q, prep, A16, q.DT_F32, kernel_hint, split_k_hint, tile_hint=tile_hint, bias=bias)
+    r = ref_rows(prep, A16, rows, bias)
     st = tolerance.check_e1_e2(y32[rows], r)
-    y16, _ = run_gpu(q, prep, A16, out16_dtype(q, prep.fmt), kernel_hint, split_k_hint, ws, tile_hint)
+    y16, _ = run_gpu(q, prep, A16, out16_dtype(q, prep.fmt), kernel_hint, split_k_hint, ws, tile_hint, bias=bias)
     tolerance.check_e3(y16, y32.astype(np.float32), out16_kind(prep.fmt))
     tolerance.check_e2(out16_values(y16[rows], prep.fmt), r)
     return st, y32

@@ -3,6 +3,7 @@ return before anything is enqueued, workspace sizing.  No kernel is launched her
 import os
 import re
 
+import numpy as np
 import pytest
 
 import weight_only_quantized_qgemm_amd as q
@@ -22,7 +23,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert set(names) >= {"qgemm_pack", "qgemm_run", "qgemm_workspace_bytes", "qgemm_quantize",
+    assert set(names) >= {"qgemm_pack", "qgemm_run", "qgemm_run_bias", "qgemm_workspace_bytes", "qgemm_quantize",
                           "qgemm_status_string", "qgemm_last_error", "qgemm_version"}
     for n in names:
         assert hasattr(q.lib, n), n
@@ -47,6 +48,7 @@ BAD = [
     (dict(M=1, N=256, K=512, fmt="int4", group_size=48), q.ERR_UNSUPPORTED, "group_size"),
     (dict(M=1, N=256, K=512, fmt="int4", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "INT4 weights need"),
     (dict(M=1, N=256, K=512, fmt="fp8", out_dtype=q.DT_F16), q.ERR_UNSUPPORTED, "FP8_E4M3 weights need"),
+    (dict(M=1, N=256, K=512, fmt="fp8h", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "FP8_E4M3 weights need"),
     (dict(M=1, N=256, K=512, fmt="fp8", group_size=128), q.ERR_INVALID_ARGUMENT, "group_size 0"),
     (dict(M=1, N=256, K=512, fmt="fp4", group_size=32), q.ERR_INVALID_ARGUMENT, "group_size 16"),
     (dict(M=17, N=256, K=512, fmt="int4", kernel_hint=q.KERNEL_DECODE), q.ERR_INVALID_ARGUMENT, "DECODE needs"),
@@ -68,10 +70,11 @@ def test_validation_errors(kw, status, text):
 def test_empty_product_needs_nothing_and_launches_nothing():
     # M = 0: no workspace; qgemm_run validates the descriptor and returns without touching
     # (or checking) any pointer, so it needs no GPU.
-    for fmt in ("int4", "fp8", "fp4"):
+    for fmt in ("int4", "fp8", "fp8h", "fp4"):
         p = q.problem(0, 256, 512, fmt)
         assert q.workspace_bytes(p) == 0
         assert q.run_raw(p, None, None, None, None, None, None, 0, None) == q.OK
+        assert q.run_bias_raw(p, None, None, None, None, None, None, None, 0, None) == q.OK
     p = q.problem(0, 250, 512, "int4")               # the descriptor is still checked
     assert q.run_raw(p, None, None, None, None, None, None, 0, None) == q.ERR_INVALID_ARGUMENT
 
@@ -106,6 +109,25 @@ def test_null_and_misaligned_pointers_fail_before_launch():
     assert _valid_run_status(f8, alpha=0x4002) == q.ERR_MISALIGNED     # 2 mod 4
     f4 = q.problem(1, 256, 512, "fp4")
     assert _valid_run_status(f4, S=0x3008) == q.ERR_MISALIGNED
+
+
+def test_bias_needs_16_byte_alignment():
+    # the FlashInfer fix (PR #7495 analysis, section 3(a)): a bias is 16-byte aligned, the
+    # scalar alpha only 4; a misaligned bias fails before anything is enqueued
+    for fmt in ("int4", "fp8", "fp8h", "fp4"):
+        p = q.problem(1, 256, 512, fmt)
+        st = q.run_bias_raw(p, 0x1000, 0x2000, 0x3000, 0x4004, 0x6008, 0x5000, None, 0, None)
+        assert st == q.ERR_MISALIGNED and "bias must be 16-byte aligned" in q.last_error()
+
+
+def test_fp8_weights_pack_the_same_for_both_activation_types():
+    g = np.random.default_rng(3)
+    w = (g.standard_normal((64, 256)) * 0.05).astype(np.float32)
+    pb, ph = q.problem(1, 64, 256, "fp8"), q.problem(1, 64, 256, "fp8h")
+    cb, _, ab = q.quantize(pb, w)
+    ch, _, ah = q.quantize(ph, w)
+    assert np.array_equal(cb, ch) and ab == ah
+    assert np.array_equal(q.pack(pb, cb, None)[0], q.pack(ph, ch, None)[0])
 
 
 def test_scalar_alpha_needs_only_4_byte_alignment():

@@ -24,12 +24,12 @@ def q():
 
 
 def _act(fmt, M, K, key):
-    return synthetic.activations(M, K, "f16" if fmt == "int4" else "bf16", key)
+    return synthetic.activations(M, K, out16_kind(fmt), key)
 
 
 def _identity_rows(fmt, rows, K):
     import torch as T
-    dt = T.float16 if fmt == "int4" else T.bfloat16
+    dt = T.float16 if out16_kind(fmt) == "f16" else T.bfloat16
     A = T.zeros((len(rows), K), dtype=dt)
     for i, k in enumerate(rows):
         A[i, k] = 1.0
@@ -46,7 +46,7 @@ def _dequant_16bit_values(fmt, prep):
 
 
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 64), ("int4", 128), ("int4", 256),
-                                   ("fp8", None), ("fp4", None)])
+                                   ("fp8", None), ("fp8h", None), ("fp4", None)])
 @pytest.mark.parametrize("hint,step", [(1, 16), (1, 4), (1, 1), (2, None)],
                          ids=["decode-M16", "decode-M4", "decode-M1", "prefill"])
 def test_identity_activations_give_dequantized_weights_bit_exact(q, fmt, G, hint, step):
@@ -86,6 +86,9 @@ CONFIGS = [
     ("fp8", 2, (8192, 10240, 5120), None, 64),
     ("fp8", 3, (32768, 3200, 5120), None, 64),
     ("fp8", 4, (16384, 12800, 5120), None, 64),
+    ("fp8h", 0, (1, 10240, 5120), None, None),
+    ("fp8h", 1, (16, 10240, 5120), None, None),
+    ("fp8h", 2, (8192, 10240, 5120), None, 64),
     ("fp4", 0, (1, 8192, 8192), None, None),
     ("fp4", 1, (128, 8192, 8192), None, None),
     ("fp4", 2, (8192, 8192, 8192), None, 64),
@@ -105,11 +108,14 @@ def test_workload_parity(q, name, si, shape, G, nrows):
     if nrows:
         g = np.random.default_rng([wi, si, 2])
         rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, nrows, replace=False)]))
-    st, _ = check_against_oracle(q, prep, A, rows)
+    # the fp16-activation FP8 workload carries a bias (mm_fp16_fp8's bias argument)
+    b = synthetic.bias(N, out16_kind(fmt), (wi, si)) if name == "fp8h" else None
+    st, _ = check_against_oracle(q, prep, A, rows, bias=b)
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f} max_abs={st['max_abs']:.3e}")
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int4", 256), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int4", 256), ("fp8", None), ("fp8h", None),
+                                   ("fp4", None)])
 @pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 33, 127, 128, 129])
 def test_m_sweep_ragged(q, fmt, G, M):
     N, K = 272, 768          # N: 17 column blocks (ragged against 128-wide tiles); K: 6 k blocks
@@ -241,3 +247,41 @@ def test_long_k(q, fmt, G, M, N, K):
     A = _act(fmt, M, K, (56, M))
     st, _ = check_against_oracle(q, prep, A)
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp8h", "fp4"])
+@pytest.mark.parametrize("M,hint,split", [(1, 0, 0), (16, 0, 3), (33, 0, 0), (300, 2, 2)])
+def test_bias_epilogue(q, fmt, M, hint, split):
+    # qgemm_run_bias: out = A . dequant(W) (* alpha) + bias[n], the bias added in fp32 after
+    # alpha and rounded once with the rest (mm_bf16_fp8 / mm_fp16_fp8 bias argument).
+    import torch as T
+    N, K = 272, 1024
+    say(f"case bias fmt={fmt} M={M} hint={hint} split={split}")
+    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (57, N, K))
+    A = _act(fmt, M, K, (57, M))
+    b = synthetic.bias(N, out16_kind(fmt), (57, N))
+    check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, bias=b)
+    # zero activations: the output is exactly the bias in every row (both output types)
+    y32, _ = run_gpu(q, prep, T.zeros_like(A), q.DT_F32, hint, split, bias=b)
+    assert np.array_equal(y32, np.tile(b.to(T.float64).numpy(), (M, 1)))
+    y16, _ = run_gpu(q, prep, T.zeros_like(A), out16_dtype(q, fmt), hint, split, bias=b)
+    assert np.array_equal(y16, np.tile(b.view(T.int16).numpy().view(np.uint16), (M, 1)))
+
+
+def test_bias_null_is_plain_run_bitwise(q):
+    # qgemm_run_bias with a NULL bias is exactly qgemm_run
+    import torch as T
+    N, K, M = 256, 1024, 16
+    prep = Prepared(q, "fp8h", N, K, 0, (58, N, K))
+    A = _act("fp8h", M, K, (58, M)).cuda()
+    p = q.problem(M, N, K, "fp8h", out_dtype=q.DT_F32)
+    o1 = T.empty((M, N), dtype=T.float32, device="cuda")
+    o2 = T.empty_like(o1)
+    ws = q.alloc_workspace(p)
+    q.run(p, A, prep.w, None, prep.alpha_t, o1, ws)
+    st = q.run_bias_raw(p, A.data_ptr(), prep.w.data_ptr(), None, prep.alpha_t.data_ptr(), None, o2.data_ptr(),
+                        None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+                        T.cuda.current_stream().cuda_stream)
+    assert st == q.OK, q.last_error()
+    T.cuda.synchronize()
+    assert T.equal(o1, o2)

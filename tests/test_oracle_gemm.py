@@ -74,3 +74,32 @@ def test_int4_f16_operand_is_rounded_product():
     sval = codecs.f16_from_bits(s)[0, 0]
     for i, q in enumerate([-7, 7, 0, -5]):
         assert v[0, i] == np.float64(np.float16(q * sval))
+
+
+def test_gemm_fp64_bias_vs_brute_force():
+    # the bias lands on its own column, after alpha: a triple loop with the bias written out
+    g = np.random.default_rng(15)
+    M, N, K = 3, 7, 64
+    a = g.standard_normal((M, K))
+    w = g.standard_normal((N, K))
+    b = g.standard_normal(N)
+    r = reference.gemm_fp64(a, w, 0.5, b)
+    for m in range(M):
+        for n in range(N):
+            exact = math.fsum(a[m, k] * w[n, k] for k in range(K)) * 0.5 + b[n]
+            tol = K * 2.0 ** -52 * (math.fsum(abs(a[m, k] * w[n, k]) for k in range(K)) + abs(b[n]))
+            assert abs(r[m, n] - exact) <= tol + 1e-300
+    # zero activations leave exactly the bias in every row; rows keep their own columns
+    z = reference.gemm_fp64(np.zeros((M, K)), w, 3.0, b)
+    assert np.array_equal(z, np.tile(b, (M, 1)))
+    rows = reference.gemm_fp64_rows(a, w, [2, 0], 0.5, b)
+    assert np.array_equal(rows, r[[2, 0]])
+
+
+def test_fp8_values_are_exact_in_fp16_and_bf16():
+    # mm_fp16_fp8 feeds the same dequantized weights to an fp16 matrix unit: every finite
+    # e4m3 value must survive both 16-bit casts unchanged
+    v = codecs.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = v[np.isfinite(v)]
+    assert np.array_equal(codecs.f16_round(fin), fin)
+    assert np.array_equal(codecs.bf16_round(fin), fin)

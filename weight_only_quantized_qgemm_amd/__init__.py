@@ -53,12 +53,13 @@ _lib.qgemm_quantize.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_float
 _lib.qgemm_pack.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp, ctypes.POINTER(_sz)]
 _lib.qgemm_workspace_bytes.argtypes = [_P, ctypes.POINTER(_sz)]
 _lib.qgemm_run.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.qgemm_run_bias.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qgemm_status_string.argtypes = [ctypes.c_int]
 _lib.qgemm_status_string.restype = ctypes.c_char_p
 _lib.qgemm_last_error.argtypes = []
 _lib.qgemm_last_error.restype = ctypes.c_char_p
 _lib.qgemm_version.restype = ctypes.c_int32
-for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run"):
+for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run", "qgemm_run_bias"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 lib = _lib
@@ -80,23 +81,27 @@ def _check(status):
 _FORMATS = {
     "int4": (DT_F16, DT_INT4, SCALE_GROUP_F16, DT_F16),
     "fp8": (DT_BF16, DT_FP8_E4M3, SCALE_TENSOR_F32, DT_BF16),
+    "fp8h": (DT_F16, DT_FP8_E4M3, SCALE_TENSOR_F32, DT_F16),      # FP8 weights, fp16 activations
     "fp4": (DT_BF16, DT_FP4_E2M1, SCALE_BLOCK16_E4M3, DT_BF16),
 }
 
 
 def problem(M, N, K, fmt, group_size=None, out_dtype=None, kernel_hint=KERNEL_AUTO, split_k_hint=0,
             tile_hint=0):
-    """Problem descriptor for one of the formats 'int4', 'fp8', 'fp4'."""
+    """Problem descriptor for one of the formats 'int4', 'fp8' (bf16 activations), 'fp8h'
+    (fp16 activations), 'fp4'."""
     a, w, sl, o = _FORMATS[fmt]
     if group_size is None:
-        group_size = {"int4": 128, "fp8": 0, "fp4": 16}[fmt]
+        group_size = {"int4": 128, "fp8": 0, "fp8h": 0, "fp4": 16}[fmt]
     if out_dtype is not None:
         o = out_dtype
     return Problem(M, N, K, a, w, o, group_size, sl, kernel_hint, split_k_hint, tile_hint)
 
 
 def fmt_of(p):
-    return {DT_INT4: "int4", DT_FP8_E4M3: "fp8", DT_FP4_E2M1: "fp4"}[p.w_dtype]
+    if p.w_dtype == DT_FP8_E4M3:
+        return "fp8h" if p.a_dtype == DT_F16 else "fp8"
+    return {DT_INT4: "int4", DT_FP4_E2M1: "fp4"}[p.w_dtype]
 
 
 def _ptr(x):
@@ -114,7 +119,7 @@ def quantize(p, w_nk):
     N, K = int(p.N), int(p.K)
     assert w.shape == (N, K)
     f = fmt_of(p)
-    codes = np.empty((N, K // 2) if f != "fp8" else (N, K), np.uint8)
+    codes = np.empty((N, K) if f in ("fp8", "fp8h") else (N, K // 2), np.uint8)
     scales = None
     if f == "int4":
         scales = np.empty((K // p.group_size, N), np.uint16)
@@ -164,22 +169,33 @@ def alloc_workspace(p, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def run(p, A, w_packed, s_packed, alpha, out, workspace=None, stream=None):
-    """Enqueue out = A . dequant(W) (* alpha) on `stream` (default: torch's current stream)."""
+def run(p, A, w_packed, s_packed, alpha, out, workspace=None, stream=None, bias=None):
+    """Enqueue out = A . dequant(W) (* alpha) (+ bias) on `stream` (default: torch's current
+    stream); qgemm_run, or qgemm_run_bias when a bias is given."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.qgemm_run(ctypes.byref(p), _ptr(A), _ptr(w_packed), _ptr(s_packed), _ptr(alpha),
-                          _ptr(out), _ptr(workspace), ws_bytes, stream))
+    if bias is None:
+        _check(_lib.qgemm_run(ctypes.byref(p), _ptr(A), _ptr(w_packed), _ptr(s_packed), _ptr(alpha),
+                              _ptr(out), _ptr(workspace), ws_bytes, stream))
+    else:
+        _check(_lib.qgemm_run_bias(ctypes.byref(p), _ptr(A), _ptr(w_packed), _ptr(s_packed), _ptr(alpha),
+                                   _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes, stream))
 
 
 def run_raw(p, A, w_packed, s_packed, alpha, out, workspace, workspace_bytes_, stream):
     """qgemm_run on raw integer addresses; returns the status (no exception)."""
     return _lib.qgemm_run(ctypes.byref(p), A, w_packed, s_packed, alpha, out, workspace,
                           workspace_bytes_, stream)
+
+
+def run_bias_raw(p, A, w_packed, s_packed, alpha, bias, out, workspace, workspace_bytes_, stream):
+    """qgemm_run_bias on raw integer addresses; returns the status (no exception)."""
+    return _lib.qgemm_run_bias(ctypes.byref(p), A, w_packed, s_packed, alpha, bias, out, workspace,
+                               workspace_bytes_, stream)
 
 
 def last_error():

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   constexpr int NT = 64 * NW;
   // Scales are staged with the A share (small M); otherwise each wavefront loads its own
   // with its weights (staging them alone measured slower at M = 16).
-  constexpr bool HAS_S = FMT != qgemm::FMT_FP8 && ASTAGE;
+  constexpr bool HAS_S = !qgemm::fp8_weights(FMT) && ASTAGE;
   constexpr bool STAGE = ASTAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char dec_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -240,10 +240,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   if (!active || nb0 + c >= NB) return;
   const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
   const int n = (nb0 + c) * 16 + (ln & 15);
+  const float bv = bias_of(a, n);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * (ln >> 4) + r;
-    if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[0][r] : v[0][r] * alpha);
+    if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[0][r] : v[0][r] * alpha, bv);
   }
 }
 
@@ -302,6 +303,7 @@ hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t
         default: return hipErrorInvalidValue;
       }
     case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);
+    case FMT_FP8H: return L<FMT_FP8H, 0>::run(pl, a, stream);
     default: return L<FMT_FP4, 0>::run(pl, a, stream);
   }
 }

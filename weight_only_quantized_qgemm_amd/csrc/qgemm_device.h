@@ -57,6 +57,7 @@ struct KArgs {
   const void* S;              // packed scales (INT4: fp16, FP4: e4m3 bytes)
   const float* alpha;         // FP8 / FP4: device scalar
   void* out;                  // [M][N]
+  const void* bias;           // [N] of out_dtype, added after alpha; NULL for none
   unsigned* counters;         // split-K tickets, one per tile
   float* partials;            // split-K partial tiles
   int M, N, K;
@@ -107,6 +108,14 @@ __device__ __forceinline__ u32x4 dq_fp8(unsigned lo, unsigned hi) {
                __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
 }
 
+// e4m3 -> fp16 is exact too (fp16 covers e4m3's range and precision, subnormals included).
+__device__ __forceinline__ u32x4 dq_fp8h(unsigned lo, unsigned hi) {
+  return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true))};
+}
+
 __device__ __forceinline__ unsigned pk_bf16(f32x2 f, float s) {
   bf16x2 r;
   r[0] = (__bf16)(f[0] * s);
@@ -133,7 +142,7 @@ __device__ __forceinline__ void fp4_scales(unsigned sw, float (&s)[4]) {
 
 template <int FMT>
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (FMT == qgemm::FMT_INT4)
+  if constexpr (qgemm::f16_mfma(FMT))
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -145,7 +154,7 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 // issued before it).
 template <int FMT>
 struct WFrag {
-  u32x4 w[FMT == qgemm::FMT_FP8 ? 2 : 1];
+  u32x4 w[qgemm::fp8_weights(FMT) ? 2 : 1];
   unsigned s[2];    // INT4: 1, 2 or 4 fp16 scales (G = 128|256, 64, 32); FP4: 4 e4m3 bytes
 };
 
@@ -162,7 +171,7 @@ __device__ __forceinline__ u32x4 wload(const u32x4* p) {
 template <int FMT, int G, bool STREAM = true, bool SCALES = true>
 __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int lane, WFrag<FMT>& f) {
   const int KB = a.K >> 7;
-  if constexpr (FMT == qgemm::FMT_FP8) {
+  if constexpr (qgemm::fp8_weights(FMT)) {
     const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * (KB * 2) + 2 * kb) * 1024) + lane;
     f.w[0] = wload<STREAM>(p);
     f.w[1] = wload<STREAM>(p + 64);
@@ -252,13 +261,26 @@ __device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (
     return dq_int4(f.w[0][t], int4_scale_pair<G>(f.s, t));
   } else if constexpr (FMT == qgemm::FMT_FP8) {
     return dq_fp8(f.w[t >> 1][2 * (t & 1)], f.w[t >> 1][2 * (t & 1) + 1]);
+  } else if constexpr (FMT == qgemm::FMT_FP8H) {
+    return dq_fp8h(f.w[t >> 1][2 * (t & 1)], f.w[t >> 1][2 * (t & 1) + 1]);
   } else {
     return dq_fp4(f.w[0][t], fs[t]);
   }
 }
 
 // ----------------------------------------------------------------------------- epilogue
-__device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v) {
+// Bias of column n as fp32 (exact), 0 without a bias.  Wavefront-uniform branch.
+__device__ __forceinline__ float bias_of(const KArgs& a, int n) {
+  if (!a.bias) return 0.0f;
+  if (a.out_dtype == QGEMM_DT_F32) return static_cast<const float*>(a.bias)[n];
+  if (a.out_dtype == QGEMM_DT_F16) return (float)static_cast<const _Float16*>(a.bias)[n];
+  return (float)static_cast<const __bf16*>(a.bias)[n];
+}
+
+// v is the fp32 result (alpha already applied); the bias is added in fp32, then the value is
+// rounded once to the output type.
+__device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v, float bias) {
+  v += bias;
   const size_t i = (size_t)m * a.N + n;
   if (a.out_dtype == QGEMM_DT_F32) {
     static_cast<float*>(a.out)[i] = v;

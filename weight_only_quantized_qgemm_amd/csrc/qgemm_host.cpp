@@ -40,7 +40,9 @@ static const char* dtype_name(int d) {
 }
 
 Format format_of(const qgemm_problem_t* p) {
-  return p->w_dtype == QGEMM_DT_INT4 ? FMT_INT4 : p->w_dtype == QGEMM_DT_FP8_E4M3 ? FMT_FP8 : FMT_FP4;
+  if (p->w_dtype == QGEMM_DT_INT4) return FMT_INT4;
+  if (p->w_dtype == QGEMM_DT_FP8_E4M3) return p->a_dtype == QGEMM_DT_F16 ? FMT_FP8H : FMT_FP8;
+  return FMT_FP4;
 }
 
 // Each of M, N, K is limited to 2^24; the kernels address A, W, out and the workspace with
@@ -72,9 +74,10 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
       return fail(QGEMM_ERR_UNSUPPORTED, "INT4 group_size must be 32, 64, 128 or 256, got %d", g);
     if (p->K % g) return fail(QGEMM_ERR_INVALID_ARGUMENT, "K (%lld) must be a multiple of group_size (%d)", (long long)p->K, g);
   } else if (w == QGEMM_DT_FP8_E4M3) {
-    if (a != QGEMM_DT_BF16 || sl != QGEMM_SCALE_TENSOR_F32 || (o != QGEMM_DT_BF16 && o != QGEMM_DT_F32))
-      return fail(QGEMM_ERR_UNSUPPORTED, "FP8_E4M3 weights need a_dtype BF16, scale_layout TENSOR_F32 and out_dtype BF16 or F32; "
-                  "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
+    // mm_bf16_fp8 and mm_fp16_fp8: the output is the activations' 16-bit type or fp32
+    if ((a != QGEMM_DT_BF16 && a != QGEMM_DT_F16) || sl != QGEMM_SCALE_TENSOR_F32 || (o != a && o != QGEMM_DT_F32))
+      return fail(QGEMM_ERR_UNSUPPORTED, "FP8_E4M3 weights need a_dtype BF16 or F16, scale_layout TENSOR_F32 and out_dtype "
+                  "a_dtype or F32; got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
     if (g != 0) return fail(QGEMM_ERR_INVALID_ARGUMENT, "FP8_E4M3 takes group_size 0 (per-tensor scale), got %d", g);
   } else if (w == QGEMM_DT_FP4_E2M1) {
     if (a != QGEMM_DT_BF16 || sl != QGEMM_SCALE_BLOCK16_E4M3 || (o != QGEMM_DT_BF16 && o != QGEMM_DT_F32))
@@ -177,7 +180,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       return k * pl->cb <= 8 && (k != 5 || pl->cb == 1) && (k != 8 || pl->cb == 1);
     };
     auto fits_twice = [&](int k) {
-      const int wregs = pl->fmt == FMT_FP8 ? 8 : 5;
+      const int wregs = fp8_weights(pl->fmt) ? 8 : 5;
       return 2 * k * ((pl->astage ? 0 : 16) + pl->cb * wregs) <= 210;
     };
     pl->kpw = 1;
@@ -330,7 +333,7 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* p, const float* w_nk, void*
   if (st != QGEMM_OK) return st;
   if (!w_nk || !codes_canonical) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk and codes_canonical must not be NULL");
   const Format fmt = format_of(p);
-  if (fmt != FMT_FP8 && !scales_canonical)
+  if (!fp8_weights(fmt) && !scales_canonical)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical must not be NULL for INT4 / FP4");
   if (fmt != FMT_INT4 && !alpha_out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha_out must not be NULL for FP8 / FP4");
   const int64_t N = p->N, K = p->K;
@@ -373,7 +376,7 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* p, const float* w_nk, void*
     amax = v > amax ? v : amax;
   }
 
-  if (fmt == FMT_FP8) {
+  if (fp8_weights(fmt)) {
     const float alpha = (float)(amax / 448.0);
     *alpha_out = alpha;
     for (int64_t i = 0; i < N * K; ++i) {
@@ -422,7 +425,7 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed_bytes and s_packed_bytes must not be NULL");
   const Format fmt = format_of(p);
   const int64_t N = p->N, K = p->K, NB = N / 16;
-  const size_t need_w = fmt == FMT_FP8 ? (size_t)(N * K) : (size_t)(N * K / 2);
+  const size_t need_w = fp8_weights(fmt) ? (size_t)(N * K) : (size_t)(N * K / 2);
   size_t need_s = 0;
   if (fmt == FMT_INT4) need_s = (size_t)(N * (K / p->group_size)) * 2;
   if (fmt == FMT_FP4) need_s = (size_t)(N * (K / 16));
@@ -442,7 +445,7 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
   if (w_packed) {
     const uint8_t* src = static_cast<const uint8_t*>(w_canonical);
     uint8_t* dst = static_cast<uint8_t*>(w_packed);
-    if (fmt == FMT_FP8) {
+    if (fp8_weights(fmt)) {
       // 1 KiB block = 16 columns x 64 k; lane l: column l & 15, k = 32t + 8(l >> 4) + j.
       const int64_t KB = K / 64;
       for (int64_t nb = 0; nb < NB; ++nb)

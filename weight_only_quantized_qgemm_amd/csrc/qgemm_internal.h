@@ -35,14 +35,18 @@ constexpr int kDecodeMaxScales = 16 * 1024;
 constexpr int kDecodeStageA = kDecodeMaxA / (16 * 64 * kDecodeWaves);
 constexpr int kDecodeStageS = kDecodeMaxScales / (16 * 64 * kDecodeWaves);
 
-enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
+// Kernel formats.  FMT_FP8H is FP8 weights with fp16 activations (mm_fp16_fp8): the weight
+// layout, quantization and alpha are FP8's, the MFMA is the fp16 one.
+enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2, FMT_FP8H = 3 };
+constexpr bool fp8_weights(int fmt) { return fmt == FMT_FP8 || fmt == FMT_FP8H; }
+constexpr bool f16_mfma(int fmt) { return fmt == FMT_INT4 || fmt == FMT_FP8H; }
 
 // ---- Decode LDS layout, shared by the launch plan (which sizes the allocation) and the kernel.
 // Packed scale bytes of one column block that nkb consecutive k blocks read, at most (an INT4
 // group of 256 spans two k blocks and may be cut by a boundary).
 constexpr int dec_scale_span(int fmt, int group_size, int nkb) {
   return fmt == FMT_FP4 ? 128 * nkb
-         : fmt == FMT_FP8 ? 0
+         : fp8_weights(fmt) ? 0
          : group_size <= 128 ? 32 * (128 / group_size) * nkb
                              : 32 * (nkb / 2 + 1);
 }

@@ -225,12 +225,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     const int nb = (n0 >> 4) + TN * wn + j;
     if (nb >= NB) continue;
     const int n = nb * 16 + (lane & 15);
+    const float bv = bias_of(a, n);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * TM * wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[TN * i + j][r] : v[TN * i + j][r] * alpha);
+        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[TN * i + j][r] : v[TN * i + j][r] * alpha, bv);
       }
   }
 }
@@ -266,6 +267,7 @@ hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t
         default: return hipErrorInvalidValue;
       }
     case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);
+    case FMT_FP8H: return L<FMT_FP8H, 0>::run(pl, a, stream);
     default: return L<FMT_FP4, 0>::run(pl, a, stream);
   }
 }

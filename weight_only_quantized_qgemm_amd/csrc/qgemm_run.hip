@@ -10,9 +10,9 @@ namespace {
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 }  // namespace
 
-extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, const void* w_packed,
-                                    const void* s_packed, const float* alpha, void* out, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+extern "C" qgemm_status_t qgemm_run_bias(const qgemm_problem_t* p, const void* A, const void* w_packed,
+                                         const void* s_packed, const float* alpha, const void* bias, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
   using namespace qgemm;
   clear_error();
   qgemm_status_t st = validate_problem(p);
@@ -22,11 +22,14 @@ extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, con
   if (!A) return fail(QGEMM_ERR_INVALID_ARGUMENT, "A is NULL");
   if (!w_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed is NULL");
   if (!out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "out is NULL");
-  if (fmt != FMT_FP8 && !s_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "s_packed is NULL (needed for INT4 and FP4)");
+  if (!fp8_weights(fmt) && !s_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "s_packed is NULL (needed for INT4 and FP4)");
   if (fmt != FMT_INT4 && !alpha) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha is NULL (needed for FP8 and FP4)");
   if (!aligned(A, 16)) return fail(QGEMM_ERR_MISALIGNED, "A must be 16-byte aligned");
   if (!aligned(w_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "w_packed must be 16-byte aligned");
-  if (s_packed && fmt != FMT_FP8 && !aligned(s_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "s_packed must be 16-byte aligned");
+  if (s_packed && !fp8_weights(fmt) && !aligned(s_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "s_packed must be 16-byte aligned");
+  // a bias takes the alignment the FlashInfer fix requires of it (PR #7495 analysis,
+  // section 3(a): 16 bytes when a bias is given, 4 for the scalar alpha)
+  if (bias && !aligned(bias, 16)) return fail(QGEMM_ERR_MISALIGNED, "bias must be 16-byte aligned");
   if (alpha && fmt != FMT_INT4 && !aligned(alpha, 4)) return fail(QGEMM_ERR_MISALIGNED, "alpha must be 4-byte aligned");
   if (!aligned(out, 16)) return fail(QGEMM_ERR_MISALIGNED, "out must be 16-byte aligned");
 
@@ -47,6 +50,7 @@ extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, con
   a.S = s_packed;
   a.alpha = alpha;
   a.out = out;
+  a.bias = bias;
   if (pl.ws_bytes) {
     a.counters = static_cast<unsigned*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counters_bytes);
@@ -64,4 +68,10 @@ extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, con
                                                 : dev::launch_decode(pl, p->group_size, a, s);
   if (e != hipSuccess) return fail(QGEMM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return QGEMM_OK;
+}
+
+extern "C" qgemm_status_t qgemm_run(const qgemm_problem_t* p, const void* A, const void* w_packed,
+                                    const void* s_packed, const float* alpha, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return qgemm_run_bias(p, A, w_packed, s_packed, alpha, nullptr, out, workspace, workspace_bytes, stream);
 }
