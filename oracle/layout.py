@@ -19,11 +19,19 @@ INT4 (w_dtype INT4) and FP4 (w_dtype FP4_E2M1) weights
     for nibble slot s = 0..7 (slot s = bits 4s .. 4s+3 of the little-endian dword).
       INT4: J = (0, 2, 4, 6, 1, 3, 5, 7)
       FP4 : J = (0, 1, 2, 3, 4, 5, 6, 7)
+INT2 (w_dtype INT2) weights
+    block (nb, kb) = columns 16*nb .. 16*nb+15, k = 128*kb .. 128*kb+127, 512 bytes, block
+    index nb * (K/128) + kb.  Lane l owns bytes [8*l, 8*l + 8): dword d (d = 0..1) holds 16
+    2-bit codes; the code at bits 16*h + 8*b + 2*f (h, b = 0..1, f = 0..3) is column
+    16*nb + (l & 15) at k = 128*kb + 32*(2*d + b) + 8*(l >> 4) + 2*f + h.  So byte b of
+    either 16-bit half carries K step 2d + b, field f of it the k pair (2f, 2f + 1) with
+    the even k in the low half: a mask of the field and an OR of an fp16 exponent give an
+    fp16 pair 2^(10 - 2f) + code with no shift but the one for b = 1.
 FP8 weights
     block (nb, kb) = 16 columns x 64 k, 1024 bytes, block index nb * (K/64) + kb;
     lane l owns 16 bytes: byte 8*t + j (t = 0..1, j = 0..7) is column 16*nb + (l & 15),
     k = 64*kb + 32*t + 8*(l >> 4) + j.
-INT4 scales (fp16)
+INT4 and INT2 scales (fp16)
     span = max(G, 128); T = max(1, 128 / G) scales per (column, span).
     Element index ((nb * (K/span) + kb) * 16 + c) * T + t holds the scale of column
     16*nb + c for group  kb * (span / G) + t.
@@ -90,6 +98,48 @@ def device_fp4_weights(codes):
 
 def device_fp4_weights_inverse(packed, N, K):
     return _nibble_unlayout(packed, N, K, J_FP4)
+
+
+def _int2_positions(N, K):
+    """(n, k) of every packed 2-bit code, shape [N/16, K/128, 64 lanes, 2 dwords, 2 halves,
+    2 bytes, 4 fields]; its bit position is 16*h + 8*b + 2*f of dword d."""
+    assert N % 16 == 0 and K % 128 == 0
+    sh = (N // 16, K // 128, 64, 2, 2, 2, 4)
+    nb = np.arange(N // 16).reshape(-1, 1, 1, 1, 1, 1, 1)
+    kb = np.arange(K // 128).reshape(1, -1, 1, 1, 1, 1, 1)
+    l = np.arange(64).reshape(1, 1, -1, 1, 1, 1, 1)
+    d = np.arange(2).reshape(1, 1, 1, -1, 1, 1, 1)
+    h = np.arange(2).reshape(1, 1, 1, 1, -1, 1, 1)
+    b = np.arange(2).reshape(1, 1, 1, 1, 1, -1, 1)
+    f = np.arange(4).reshape(1, 1, 1, 1, 1, 1, -1)
+    n = np.broadcast_to(16 * nb + (l & 15), sh)
+    k = np.broadcast_to(128 * kb + 32 * (2 * d + b) + 8 * (l >> 4) + 2 * f + h, sh)
+    return n, k
+
+
+def device_int2_weights(codes):
+    """codes uint8 [N, K] (0..3) -> packed bytes per the INT2 block spec."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    n, k = _int2_positions(N, K)
+    c = codes[n, k].astype(np.uint32)                  # [NB, KB, 64, 2, 2(h), 2(b), 4(f)]
+    h = np.arange(2).reshape(1, 1, 1, 1, -1, 1, 1)
+    b = np.arange(2).reshape(1, 1, 1, 1, 1, -1, 1)
+    f = np.arange(4).reshape(1, 1, 1, 1, 1, 1, -1)
+    dword = (c << (16 * h + 8 * b + 2 * f).astype(np.uint32)).sum(axis=(4, 5, 6)).astype(np.uint32)
+    return dword.astype("<u4").view(np.uint8).reshape(-1)
+
+
+def device_int2_weights_inverse(packed, N, K):
+    dw = np.asarray(packed, dtype=np.uint8).view("<u4").reshape(N // 16, K // 128, 64, 2)
+    h = np.arange(2).reshape(1, 1, 1, 1, -1, 1, 1)
+    b = np.arange(2).reshape(1, 1, 1, 1, 1, -1, 1)
+    f = np.arange(4).reshape(1, 1, 1, 1, 1, 1, -1)
+    c = (dw[..., None, None, None] >> (16 * h + 8 * b + 2 * f).astype(np.uint32)) & 3
+    n, k = _int2_positions(N, K)
+    codes = np.zeros((N, K), np.uint8)
+    codes[n, k] = c.astype(np.uint8)
+    return codes
 
 
 def _fp8_positions(N, K):

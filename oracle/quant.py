@@ -10,8 +10,9 @@ Readings where the pages are silent (each is listed in the design notes):
   once to the target format;
 * the quantizer divides by the *stored* (already rounded) scale, so that dequantizing
   the stored codes and scales is self-consistent;
-* an all-zero INT4 group gets scale 0 and codes 8 (signed 0); an all-zero FP4 block gets
-  scale code 0 and codes 0; an all-zero FP8 tensor gets alpha 0 and codes 0.
+* an all-zero INT4 group gets scale 0 and codes 8 (signed 0), an all-zero INT2 group scale 0
+  and codes 2; an all-zero FP4 block gets scale code 0 and codes 0; an all-zero FP8 tensor
+  gets alpha 0 and codes 0.
 """
 import numpy as np
 
@@ -41,6 +42,33 @@ def quantize_int4(wt, group_size):
     q = np.clip(np.rint(w / safe[:, :, None]), -8, 7)
     q = np.where(s[:, :, None] == 0, 0.0, q)
     codes = (q + 8).astype(np.uint8).reshape(N, K)
+    scale_bits = codecs.f16_bits(s).T.copy()            # [K/G, N]
+    return codes, scale_bits
+
+
+# ----------------------------------------------------------------------------- INT2 (W2A16)
+def quantize_int2(wt, group_size):
+    """Symmetric absmax INT2 per (K-group, column): the W2A16 combination of the Bitblas
+    lecture (033, exercises: "W2A16 (INT2 weight)") with the INT4 recipe carried over to
+    2 bits.  Signed range [-2, 1], stored code = signed + 2 (as the nibble is signed + 8);
+    the scale is absmax / (2^(2-1) - 1) = absmax rounded to fp16 (INT4's absmax / 7 is
+    absmax / (2^(4-1) - 1)); code = clamp(rint(w / s), -2, 1) + 2.  Like -8 for INT4, -2
+    is never emitted by the absmax scale.
+
+    wt: float32 [N, K].  Returns (codes uint8 [N, K] in 0..3, scale_bits uint16 [K/G, N]).
+    """
+    wt = np.asarray(wt, dtype=np.float32)
+    N, K = wt.shape
+    G = int(group_size)
+    if K % G:
+        raise ValueError("K must be a multiple of group_size")
+    w = wt.astype(np.float64).reshape(N, K // G, G)
+    amax = np.abs(w).max(axis=2)                        # [N, K/G]
+    s = codecs.f16_round(amax / 1.0)                    # stored scale value
+    safe = np.where(s == 0, 1.0, s)
+    q = np.clip(np.rint(w / safe[:, :, None]), -2, 1)
+    q = np.where(s[:, :, None] == 0, 0.0, q)
+    codes = (q + 2).astype(np.uint8).reshape(N, K)
     scale_bits = codecs.f16_bits(s).T.copy()            # [K/G, N]
     return codes, scale_bits
 
@@ -118,3 +146,30 @@ def unpack_nibbles(packed):
 def int4_signed(codes):
     """Signed INT4 value of a stored nibble: nibble - 8 (gemlite snippet, lecture 034)."""
     return np.asarray(codes, dtype=np.int64) - 8
+
+
+def pack_crumbs(codes):
+    """Four 2-bit codes per byte along K, the lowest k in the lowest bits (INT2 canonical).
+
+    codes uint8 [N, K] (values 0..3) -> uint8 [N, K/4].
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    if c.shape[1] % 4:
+        raise ValueError("K must be a multiple of 4")
+    if np.any(c > 3):
+        raise ValueError("2-bit codes must be < 4")
+    return (c[:, 0::4] | (c[:, 1::4] << 2) | (c[:, 2::4] << 4) | (c[:, 3::4] << 6)).astype(np.uint8)
+
+
+def unpack_crumbs(packed):
+    """Inverse of pack_crumbs: uint8 [N, K/4] -> codes uint8 [N, K]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 4), np.uint8)
+    for i in range(4):
+        out[:, i::4] = (p >> (2 * i)) & 3
+    return out
+
+
+def int2_signed(codes):
+    """Signed INT2 value of a stored 2-bit code: code - 2."""
+    return np.asarray(codes, dtype=np.int64) - 2

@@ -34,6 +34,19 @@ def dequant_int4_f16(codes, scale_bits, group_size):
     return codecs.f16_round(dequant_int4(codes, scale_bits, group_size).astype(np.float64))
 
 
+def dequant_int2(codes, scale_bits, group_size):
+    """(code - 2) * s in float32, exact.  codes [N, K] in 0..3, scale_bits uint16 [K/G, N].
+
+    The INT2 (W2A16) counterpart of dequant_int4: signed value code - 2 times the scale of
+    group k // group_size of the same column.  The product has at most 12 significant bits
+    and |code - 2| <= 2, so it is also exact in fp16: the 16-bit operand equals it.
+    """
+    q = np.asarray(codes, dtype=np.int64) - 2
+    s = codecs.f16_from_bits(scale_bits)               # [K/G, N]
+    s_nk = np.repeat(s.T, group_size, axis=1)          # [N, K]
+    return (q * s_nk).astype(np.float32)
+
+
 def dequant_fp8(codes):
     """e4m3 code -> value (exact); alpha is NOT applied here.  Returns float32 [N, K].
 

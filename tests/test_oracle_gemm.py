@@ -103,3 +103,19 @@ def test_fp8_values_are_exact_in_fp16_and_bf16():
     fin = v[np.isfinite(v)]
     assert np.array_equal(codecs.f16_round(fin), fin)
     assert np.array_equal(codecs.bf16_round(fin), fin)
+
+
+def test_int2_closed_forms_and_identity():
+    M, N, K, G = 3, 32, 256, 128
+    a = np.random.default_rng(16).standard_normal((M, K)).astype(np.float16).astype(np.float64)
+    one = codecs.f16_bits(np.ones((K // G, N)))
+    for c in (0, 1, 2, 3):
+        codes = np.full((N, K), c, np.uint8)
+        r = reference.gemm_fp64(a, reference.dequant_int2(codes, one, G))
+        assert np.allclose(r, ((c - 2) * a.sum(axis=1))[:, None], rtol=0, atol=1e-12)
+    wt = (np.random.default_rng(17).standard_normal((N, K)) * 0.02).astype(np.float32)
+    codes, sb = quant.quantize_int2(wt, 32)
+    dq = reference.dequant_int2(codes, sb, 32)
+    assert np.array_equal(reference.gemm_fp64(np.eye(K), dq), dq.T.astype(np.float64))
+    # the products are exact in fp16 too: the 16-bit operand equals the exact value
+    assert np.array_equal(codecs.f16_round(dq.astype(np.float64)), dq.astype(np.float64))

@@ -89,3 +89,31 @@ def test_round_trips():
     assert np.array_equal(layout.device_fp4_weights_inverse(layout.device_fp4_weights(c4), 48, 384), c4)
     c8 = g.integers(0, 256, (48, 192)).astype(np.uint8)
     assert np.array_equal(layout.device_fp8_weights_inverse(layout.device_fp8_weights(c8), 48, 192), c8)
+
+
+@pytest.mark.parametrize("n,k,byte,shift", [
+    # INT2, N=32, K=256: 512-byte blocks, lane l owns bytes 8l..8l+7 (dwords d = 0, 1);
+    # a code sits at bit 16h + 8b + 2f of dword d for k = 32(2d+b) + 8(l>>4) + 2f + h
+    (0, 0, 0, 0),                      # d0 b0 f0 h0 -> bit 0
+    (0, 1, 2, 0),                      # h1 -> bit 16 -> byte 2
+    (0, 2, 0, 2),                      # f1 -> bit 2
+    (0, 7, 2, 6),                      # f3 h1 -> bit 22 -> byte 2, shift 6
+    (0, 32, 1, 0),                     # step 1 -> b1 -> bit 8 -> byte 1
+    (0, 64, 4, 0),                     # step 2 -> d1 -> byte 4
+    (5, 8, 8 * 21, 0),                 # lane 5 + 16 = 21
+    (17, 130, 3 * 512 + 8, 2),         # nb1 kb1 (block 3), lane 1, k' = 2 -> f1
+    # n=31 k=255: block 3; k' = 127 = 32*3 + 8*3 + 7 -> d1 b1, lane 63, f3 h1 -> bit 30 of dword 1
+    (31, 255, 3 * 512 + 8 * 63 + 4 + 3, 6),
+])
+def test_int2_single_hot(n, k, byte, shift):
+    codes = np.zeros((32, 256), np.uint8)
+    codes[n, k] = 3
+    p = layout.device_int2_weights(codes)
+    assert p.size == 32 * 256 // 4
+    assert list(np.flatnonzero(p)) == [byte]
+    assert p[byte] == 3 << shift
+
+
+def test_int2_round_trip():
+    c = np.random.default_rng(4).integers(0, 4, (48, 384)).astype(np.uint8)
+    assert np.array_equal(layout.device_int2_weights_inverse(layout.device_int2_weights(c), 48, 384), c)

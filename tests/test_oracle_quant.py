@@ -129,3 +129,53 @@ def test_fp4_brute_force_nearest_and_block_scales():
     d = np.abs(x[..., None] - grid)
     best = np.argmin(np.where(d == d.min(-1, keepdims=True), (np.arange(16) % 2) + (np.arange(16) == 8) * 2.0, np.inf), -1)
     assert np.array_equal(codes, best.astype(np.uint8))
+
+
+def test_crumbs_every_byte_and_round_trip():
+    # INT2 canonical packing: byte j holds k = 4j .. 4j+3, lowest k in the lowest two bits
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    codes = quant.unpack_crumbs(allb)
+    for i in range(4):
+        assert np.array_equal(codes[0, i::4], (allb[0] >> (2 * i)) & 3)
+    assert np.array_equal(quant.pack_crumbs(codes), allb)
+    assert list(quant.int2_signed(codes[0, :8])) == [-2, -2, -2, -2, -1, -2, -2, -2]   # bytes 0, 1
+    c = np.random.default_rng(7).integers(0, 4, (48, 384)).astype(np.uint8)
+    assert np.array_equal(quant.unpack_crumbs(quant.pack_crumbs(c)), c)
+
+
+def test_int2_worked_example():
+    g = tagged("worked_int2.txt")
+    wt = _w(g["w"])
+    codes, sbits = quant.quantize_int2(wt, 4)
+    want_s = np.array([g["scale"][i] for i in sorted(g["scale"])], np.uint16)
+    assert np.array_equal(sbits, want_s)
+    want_b = np.array([g["bytes"][i] for i in sorted(g["bytes"])], np.uint8)
+    assert np.array_equal(quant.pack_crumbs(codes), want_b)
+    a = np.array([g["a"][i] for i in sorted(g["a"])])
+    out = reference.gemm_fp64(a, reference.dequant_int2(codes, sbits, 4))
+    want = np.array([g["out"][i] for i in sorted(g["out"])])
+    assert np.array_equal(out, want)
+
+
+def test_int2_brute_force_nearest_and_invariants():
+    G = 64
+    wt = (np.random.default_rng(8).standard_normal((32, 256)) * 0.02).astype(np.float32)
+    wt[5, 128:192] = 0.0                                    # an all-zero group
+    codes, sbits = quant.quantize_int2(wt, G)
+    s = codecs.f16_from_bits(sbits)                         # [K/G, N]
+    s_nk = np.repeat(s.T, G, axis=1)
+    q = codes.astype(np.int64) - 2
+    # brute force over the four signed values, nearest to w/s, ties to the even one
+    cand = np.arange(-2, 2)
+    x = np.where(s_nk == 0, 0.0, wt.astype(np.float64) / np.where(s_nk == 0, 1, s_nk))
+    d = np.abs(x[..., None] - cand)
+    dmin = d.min(axis=-1, keepdims=True)
+    tie_even = np.where(d == dmin, (cand % 2 != 0) * 1.0 + d, np.inf)
+    assert np.array_equal(q, cand[np.argmin(tie_even, axis=-1)])
+    assert q.min() >= -1 and q.max() <= 1                   # absmax / 1 never emits -2
+    grp = np.abs(wt).reshape(32, -1, G)
+    hit = np.take_along_axis(np.abs(q.reshape(32, -1, G)), grp.argmax(axis=2)[..., None], axis=2)[..., 0]
+    assert np.all(hit[s.T > 0] == 1)                        # each group's absmax lands on +-1
+    assert np.all(codes[5, 128:192] == 2) and s[2, 5] == 0
+    err = np.abs(wt - reference.dequant_int2(codes, sbits, G))
+    assert np.all(err <= s_nk / 2 * (1 + 1e-6) + 1e-12)
