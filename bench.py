@@ -40,6 +40,8 @@ def log(msg):
 def weight_bytes(fmt, N, K, G):
     if fmt == "int4":
         return N * K // 2 + (K // G) * N * 2
+    if fmt == "int2":
+        return N * K // 4 + (K // G) * N * 2
     if fmt in ("fp8", "fp8h"):
         return N * K
     return N * K // 2 + N * K // 16
@@ -51,9 +53,9 @@ class Gemm:
     def __init__(self, q, torch, fmt, M, N, K, G, key, min_rotate_bytes, with_bias=False):
         import synthetic
         self.fmt, self.M, self.N, self.K, self.G = fmt, M, N, K, G
-        self.p = q.problem(M, N, K, fmt, group_size=G if fmt == "int4" else None)
-        pq = q.problem(1, N, K, fmt, group_size=G if fmt == "int4" else None)
-        w = synthetic.weights(N, K, {"int4": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}[fmt], key)
+        self.p = q.problem(M, N, K, fmt, group_size=G if fmt in ("int4", "int2") else None)
+        pq = q.problem(1, N, K, fmt, group_size=G if fmt in ("int4", "int2") else None)
+        w = synthetic.weights(N, K, {"int4": 0.02, "int2": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}[fmt], key)
         codes, scales, alpha = q.quantize(pq, w)            # the library's own quantizer
         wpk, spk = q.pack(pq, codes, scales)
         self.wbytes = weight_bytes(fmt, N, K, G)
@@ -64,7 +66,7 @@ class Gemm:
         self.w = [w0] + [w0.clone() for _ in range(ncopies - 1)]
         self.s = [s0] + [None if s0 is None else s0.clone() for _ in range(ncopies - 1)]
         self.alpha = torch.tensor([alpha], dtype=torch.float32, device="cuda")
-        kind = "f16" if fmt in ("int4", "fp8h") else "bf16"
+        kind = "f16" if fmt in ("int4", "int2", "fp8h") else "bf16"
         self.A = synthetic.activations(M, K, kind, key).cuda()
         odt = torch.float16 if kind == "f16" else torch.bfloat16
         self.out = torch.empty((M, N), dtype=odt, device="cuda")
@@ -76,7 +78,7 @@ class Gemm:
     def launch(self):
         c = self.i % len(self.w)
         self.i += 1
-        self.q.run(self.p, self.A, self.w[c], self.s[c], None if self.fmt == "int4" else self.alpha,
+        self.q.run(self.p, self.A, self.w[c], self.s[c], None if self.fmt in ("int4", "int2") else self.alpha,
                    self.out, self.ws, bias=self.bias)
 
     @property
@@ -181,7 +183,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true",
-                    help="also time the FP8, FP4 and FP8-with-fp16-activations (+bias) workloads")
+                    help="also time the FP8, FP4, FP8-with-fp16-activations (+bias) and INT2 workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--counter-pass", nargs="?", const="decode", choices=("decode", "prefill"),
@@ -301,12 +303,12 @@ def main():
         torch.cuda.empty_cache()
 
     if args.all:
-        for name in ("fp8", "fp4", "fp8h"):
+        for name in ("fp8", "fp4", "fp8h", "int2"):
             wk = synthetic.WORKLOADS[name]
             wix = synthetic.WORKLOAD_INDEX[name]
             for si, (M, N, K) in enumerate(wk["shapes"]):
                 big = M >= 128
-                g = Gemm(q, torch, name, M, N, K, 0, (wix, si), (64 << 20) if big else rot,
+                g = Gemm(q, torch, name, M, N, K, wk["group_sizes"][0], (wix, si), (64 << 20) if big else rot,
                          with_bias=name == "fp8h")
                 n = 10 if big else 64
                 gg = graph_of(torch, g.launch, n)

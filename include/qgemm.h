@@ -19,6 +19,9 @@
  *                                                               (mm_fp16_fp8)
  *   BF16     FP4_E2M1       BLOCK16_E4M3          BF16 or F32   FlashInfer PR #4466 analysis
  *                                                               (BF16 x FP4 GEMM), sections 1-3
+ *   F16      INT2           GROUP_F16 (G=32..256) F16 or F32    Bitblas lecture 033, exercises
+ *                                                               (the W2A16 combination), with
+ *                                                               the INT4 recipe at 2 bits
  *
  * Value semantics (what the kernels compute):
  *   INT4 : w[k][n] = RNE_fp16((nibble - 8) * s[k / G][n]) -- the 16-bit operand the
@@ -28,6 +31,7 @@
  *          epilogue, as the PR #7495 analysis prescribes.
  *   FP4  : w = e2m1(code) * e4m3(s_b) (exact in bf16) with one scale per 16 consecutive
  *          K of a column; alpha multiplies the fp32 accumulator in the epilogue.
+ *   INT2 : w[k][n] = (code - 2) * s[k / G][n] (exact in fp16), accumulated in fp32.
  *   Bias (qgemm_run_bias): bias[n] is added in fp32 after alpha.
  *   The 16-bit output is the round-to-nearest-even cast of the fp32 result, so a call
  *   with out_dtype F32 yields exactly the values a 16-bit call rounds.
@@ -63,7 +67,8 @@ typedef enum qgemm_dtype {
   QGEMM_DT_F32 = 2,
   QGEMM_DT_INT4 = 3,
   QGEMM_DT_FP8_E4M3 = 4,   /* OCP e4m3 ("fn"): max 448, code S.1111.111 is NaN        */
-  QGEMM_DT_FP4_E2M1 = 5    /* e2m1: +-{0, .5, 1, 1.5, 2, 3, 4, 6}                      */
+  QGEMM_DT_FP4_E2M1 = 5,   /* e2m1: +-{0, .5, 1, 1.5, 2, 3, 4, 6}                      */
+  QGEMM_DT_INT2 = 6        /* signed 2-bit integer in [-2, 1], stored + 2               */
 } qgemm_dtype_t;
 
 typedef enum qgemm_scale_layout {
@@ -84,7 +89,7 @@ typedef enum qgemm_scale_layout {
  *   M >= 0 (any value; M = 0 is an empty product: qgemm_run validates the descriptor and
  *   enqueues nothing, ignoring the pointers); N % 16 == 0; K % 128 == 0; for INT4 also
  *   K % group_size == 0.  Each of M, N, K is at most 2^24.
- *   group_size: INT4 only, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
+ *   group_size: INT4 and INT2, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
  *   FP8 weights take a_dtype BF16 (mm_bf16_fp8) or F16 (mm_fp16_fp8); the packed weights
  *   are the same for both.
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
@@ -114,6 +119,9 @@ typedef struct qgemm_problem {
  *         scale per 128-ish group along K; gemlite snippet: nibble - 8).
  *   FP8 : codes uint8[N][K] = e4m3(clamp(w / alpha, +-448)), alpha = absmax / 448 (fp32);
  *         scales_canonical unused (may be NULL).
+ *   INT2: codes_canonical uint8[N][K/4], byte j of row n = code(4j) | code(4j+1) << 2 |
+ *         code(4j+2) << 4 | code(4j+3) << 6, code = clamp(rint(w / s), -2, 1) + 2; scales
+ *         as INT4 with s = RNE_fp16(absmax_group / 1) (the INT4 recipe at 2 bits).
  *   FP4 : codes uint8[N][K/2] (nibble order as INT4) = e2m1(clamp(w / (s_b alpha), +-6)),
  *         scales_canonical e4m3 uint8[N][K/16] = e4m3(min(absmax_b / (6 alpha), 448)),
  *         alpha = absmax / (6 * 448) (fp32).
@@ -135,9 +143,12 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* problem, const float* w_nk,
  *     index nb*(K/128) + kb; dword t (0..3) of lane l holds column 16nb + (l & 15) at
  *     k = 128kb + 32t + 8(l >> 4) + J[s] in nibble s (bits 4s..4s+3), with
  *     J = (0,2,4,6,1,3,5,7) for INT4 and J = (0,1,...,7) for FP4.
+ *   INT2 weights: block (nb, kb) = 16 columns x 128 k = 512 bytes, index nb*(K/128) + kb;
+ *     lane l owns bytes [8 l, 8 l + 8); bits 16h + 8b + 2f (h, b = 0..1, f = 0..3) of its
+ *     dword d hold column 16nb + (l & 15), k = 128kb + 32(2d + b) + 8(l >> 4) + 2f + h.
  *   FP8 weights: block (nb, kb) = 16 columns x 64 k, index nb*(K/64) + kb; byte 8t + j
  *     (t = 0..1, j = 0..7) of lane l is column 16nb + (l & 15), k = 64kb + 32t + 8(l>>4) + j.
- *   INT4 scales (fp16): span = max(G, 128), T = max(1, 128/G); element
+ *   INT4 and INT2 scales (fp16): span = max(G, 128), T = max(1, 128/G); element
  *     ((nb*(K/span) + kb)*16 + c)*T + t = scale of column 16nb + c, group kb*(span/G) + t.
  *   FP4 scales (e4m3): byte ((nb*(K/128) + kb)*16 + c)*8 + 4h + t = scale of column
  *     16nb + c, 16-k block 8kb + 2t + h.

@@ -8,8 +8,8 @@ import numpy as np
 import synthetic
 from oracle import codecs, quant, reference, tolerance
 
-FMT_ACT = {"int4": "f16", "fp8": "bf16", "fp8h": "f16", "fp4": "bf16"}
-SIGMA = {"int4": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}
+FMT_ACT = {"int4": "f16", "int2": "f16", "fp8": "bf16", "fp8h": "f16", "fp4": "bf16"}
+SIGMA = {"int4": 0.02, "int2": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}
 
 
 def say(msg):
@@ -24,6 +24,9 @@ def oracle_weights(fmt, N, K, G, key):
     if fmt == "int4":
         codes, sbits = quant.quantize_int4(w, G)
         return quant.pack_nibbles(codes), sbits, 1.0, reference.dequant_int4(codes, sbits, G)
+    if fmt == "int2":
+        codes, sbits = quant.quantize_int2(w, G)
+        return quant.pack_crumbs(codes), sbits, 1.0, reference.dequant_int2(codes, sbits, G)
     if fmt in ("fp8", "fp8h"):           # one quantization for both activation types
         codes, alpha = quant.quantize_fp8(w)
         return codes, None, alpha, reference.dequant_fp8(codes)
@@ -45,7 +48,7 @@ class Prepared:
         self.fmt, self.N, self.K, self.G = fmt, N, K, G
         canon, scales, alpha, self.wdq = oracle_weights(fmt, N, K, G, key)
         self.alpha = alpha if alpha_override is None else alpha_override
-        p = q.problem(1, N, K, fmt, group_size=G if fmt == "int4" else None)
+        p = q.problem(1, N, K, fmt, group_size=G if fmt in ("int4", "int2") else None)
         wpk, spk = q.pack(p, canon, scales)
         self.w = torch.from_numpy(wpk).cuda()
         self.s = None if spk is None else torch.from_numpy(spk).cuda()
@@ -59,7 +62,7 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     an exact widening), through qgemm_run_bias."""
     import torch
     M, K = A16.shape
-    p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt == "int4" else None,
+    p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt in ("int4", "int2") else None,
                   out_dtype=out_dtype, kernel_hint=kernel_hint, split_k_hint=split_k_hint,
                   tile_hint=tile_hint)
     tdt = {q.DT_F32: torch.float32, q.DT_F16: torch.float16, q.DT_BF16: torch.bfloat16}[out_dtype]
@@ -68,7 +71,7 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     if workspace is None:
         workspace = q.alloc_workspace(p)
     b = None if bias is None else bias.to(tdt).cuda()
-    q.run(p, A, prep.w, prep.s, None if prep.fmt == "int4" else prep.alpha_t, out, workspace, bias=b)
+    q.run(p, A, prep.w, prep.s, None if prep.fmt in ("int4", "int2") else prep.alpha_t, out, workspace, bias=b)
     torch.cuda.synchronize()
     o = out.cpu()
     if out_dtype == q.DT_F32:
@@ -82,11 +85,11 @@ def ref_rows(prep, A16, rows, bias=None):
 
 
 def out16_kind(fmt):
-    return "f16" if fmt in ("int4", "fp8h") else "bf16"
+    return "f16" if fmt in ("int4", "int2", "fp8h") else "bf16"
 
 
 def out16_dtype(q, fmt):
-    return q.DT_F16 if fmt in ("int4", "fp8h") else q.DT_BF16
+    return q.DT_F16 if out16_kind(fmt) == "f16" else q.DT_BF16
 
 
 def out16_values(bits, fmt):

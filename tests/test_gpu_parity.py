@@ -23,6 +23,11 @@ def q():
     return lib
 
 
+def _g(fmt):
+    """Group size of the format in the generic cases (128 for the integer formats)."""
+    return 128 if fmt in ("int4", "int2") else 0
+
+
 def _act(fmt, M, K, key):
     return synthetic.activations(M, K, out16_kind(fmt), key)
 
@@ -42,10 +47,12 @@ def _dequant_16bit_values(fmt, prep):
     if fmt == "int4":
         from oracle import quant
         return reference.dequant_int4_f16(quant.unpack_nibbles(canon), scales, prep.G)
-    return wdq.astype(np.float64)        # exact in bf16 for FP8 (alpha not applied) and FP4
+    # INT2: (code - 2) s is exact in fp16; FP8 (alpha not applied), FP4: exact in 16 bits
+    return wdq.astype(np.float64)
 
 
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 64), ("int4", 128), ("int4", 256),
+                                   ("int2", 32), ("int2", 64), ("int2", 128), ("int2", 256),
                                    ("fp8", None), ("fp8h", None), ("fp4", None)])
 @pytest.mark.parametrize("hint,step", [(1, 16), (1, 4), (1, 1), (2, None)],
                          ids=["decode-M16", "decode-M4", "decode-M1", "prefill"])
@@ -89,6 +96,9 @@ CONFIGS = [
     ("fp8h", 0, (1, 10240, 5120), None, None),
     ("fp8h", 1, (16, 10240, 5120), None, None),
     ("fp8h", 2, (8192, 10240, 5120), None, 64),
+    ("int2", 0, (1, 4096, 4096), 128, None),
+    ("int2", 1, (16, 4096, 4096), 128, None),
+    ("int2", 2, (4096, 4096, 4096), 128, 96),
     ("fp4", 0, (1, 8192, 8192), None, None),
     ("fp4", 1, (128, 8192, 8192), None, None),
     ("fp4", 2, (8192, 8192, 8192), None, 64),
@@ -114,8 +124,8 @@ def test_workload_parity(q, name, si, shape, G, nrows):
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f} max_abs={st['max_abs']:.3e}")
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int4", 256), ("fp8", None), ("fp8h", None),
-                                   ("fp4", None)])
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int4", 256), ("int2", 64), ("int2", 256),
+                                   ("fp8", None), ("fp8h", None), ("fp4", None)])
 @pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 33, 127, 128, 129])
 def test_m_sweep_ragged(q, fmt, G, M):
     N, K = 272, 768          # N: 17 column blocks (ragged against 128-wide tiles); K: 6 k blocks
@@ -125,7 +135,7 @@ def test_m_sweep_ragged(q, fmt, G, M):
     check_against_oracle(q, prep, A)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp4"])
 @pytest.mark.parametrize("M,hint,split,tile", [(16, 1, 2, 0), (16, 1, 3, 1), (16, 1, 7, 2), (16, 1, 14, 4),
                                                (4, 1, 1, 4), (4, 1, 5, 1), (16, 1, 1, 3), (16, 1, 4, 3),
                                                (3, 1, 2, 3), (16, 2, 1, 0), (16, 2, 2, 0),
@@ -133,12 +143,12 @@ def test_m_sweep_ragged(q, fmt, G, M):
 def test_split_k_and_kernel_hints(q, fmt, M, hint, split, tile):
     N, K = 256, 1792    # 14 k blocks
     say(f"case hints fmt={fmt} M={M} kernel={hint} split={split} tile={tile}")
-    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (51, N, K))
+    prep = Prepared(q, fmt, N, K, _g(fmt), (51, N, K))
     A = _act(fmt, M, K, (51, M))
     check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, tile_hint=tile)
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 64), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("fmt,G", [("int4", 64), ("int2", 128), ("fp8", None), ("fp4", None)])
 @pytest.mark.parametrize("M,N,K", [(1, 256, 128 * 44), (3, 512, 128 * 60), (16, 256, 128 * 60), (16, 8192, 128 * 44),
                                    (9, 4352, 128 * 23)])
 def test_decode_multi_run(q, fmt, G, M, N, K):
@@ -150,7 +160,7 @@ def test_decode_multi_run(q, fmt, G, M, N, K):
     check_against_oracle(q, prep, A)
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int2", 32), ("fp8", None), ("fp4", None)])
 @pytest.mark.parametrize("tile,split", [(128, 1), (128, 3), (256, 1), (256, 3)])
 def test_prefill_tile_shapes(q, fmt, G, tile, split):
     # Both prefill workgroup shapes on every format: 600 rows are ragged against 128- and
@@ -162,12 +172,12 @@ def test_prefill_tile_shapes(q, fmt, G, tile, split):
     check_against_oracle(q, prep, A, kernel_hint=2, split_k_hint=split, tile_hint=tile)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp4"])
 @pytest.mark.parametrize("M", [16, 256])
 def test_deterministic_and_counters_reset(q, fmt, M):
     N, K = 512, 4096
     say(f"case determinism fmt={fmt} M={M}")
-    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (52, N, K))
+    prep = Prepared(q, fmt, N, K, _g(fmt), (52, N, K))
     A = _act(fmt, M, K, (52, M))
     outs = []
     ws = None
@@ -175,19 +185,19 @@ def test_deterministic_and_counters_reset(q, fmt, M):
         y, ws = run_gpu(q, prep, A, q.DT_F32, workspace=ws)
         outs.append(y)
         if ws is not None:
-            p = q.problem(M, N, K, fmt, group_size=128 if fmt == "int4" else None)
+            p = q.problem(M, N, K, fmt, group_size=_g(fmt) or None)
             assert q.workspace_bytes(p) > 0
             head = ws[:256].cpu().numpy()
             assert not head.any(), "split-K tickets must return to zero"
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp4"])
 def test_minimum_shape_and_zero_weights(q, fmt):
     import torch as T
     N, K = 16, 128
     say(f"case minimum fmt={fmt}")
-    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (53, N, K))
+    prep = Prepared(q, fmt, N, K, _g(fmt), (53, N, K))
     for M in (1, 16, 17):
         check_against_oracle(q, prep, _act(fmt, M, K, (53, M)))
     # all-zero packed weights give exact zeros
@@ -227,12 +237,12 @@ def test_empty_m_enqueues_nothing(q, fmt):
     # handed over here has a row of sentinels that must survive).
     N, K = 256, 512
     say(f"case empty-m fmt={fmt}")
-    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (55, N, K))
-    dt = torch.float16 if fmt == "int4" else torch.bfloat16
+    prep = Prepared(q, fmt, N, K, _g(fmt), (55, N, K))
+    dt = torch.float16 if out16_kind(fmt) == "f16" else torch.bfloat16
     A = torch.zeros((1, K), dtype=dt, device="cuda")
     out = torch.full((1, N), 7.0, dtype=dt, device="cuda")
-    p = q.problem(0, N, K, fmt, group_size=128 if fmt == "int4" else None)
-    q.run(p, A, prep.w, prep.s, None if fmt == "int4" else prep.alpha_t, out)
+    p = q.problem(0, N, K, fmt, group_size=_g(fmt) or None)
+    q.run(p, A, prep.w, prep.s, None if fmt in ("int4", "int2") else prep.alpha_t, out)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
 
@@ -249,7 +259,7 @@ def test_long_k(q, fmt, G, M, N, K):
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp8h", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp8h", "fp4"])
 @pytest.mark.parametrize("M,hint,split", [(1, 0, 0), (16, 0, 3), (33, 0, 0), (300, 2, 2)])
 def test_bias_epilogue(q, fmt, M, hint, split):
     # qgemm_run_bias: out = A . dequant(W) (* alpha) + bias[n], the bias added in fp32 after
@@ -257,7 +267,7 @@ def test_bias_epilogue(q, fmt, M, hint, split):
     import torch as T
     N, K = 272, 1024
     say(f"case bias fmt={fmt} M={M} hint={hint} split={split}")
-    prep = Prepared(q, fmt, N, K, 128 if fmt == "int4" else 0, (57, N, K))
+    prep = Prepared(q, fmt, N, K, _g(fmt), (57, N, K))
     A = _act(fmt, M, K, (57, M))
     b = synthetic.bias(N, out16_kind(fmt), (57, N))
     check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, bias=b)

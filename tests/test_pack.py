@@ -83,3 +83,30 @@ def test_quantizer_edge_cases():
     # an all-zero tensor quantizes to zero codes and alpha 0
     codes, sf, alpha = q.quantize(q.problem(1, 16, 128, "fp4"), np.zeros((16, 128), np.float32))
     assert alpha == 0.0 and not codes.any() and not sf.any()
+
+
+@pytest.mark.parametrize("N,K,G", [(16, 128, 32), (16, 128, 128), (16, 256, 256), (48, 384, 64),
+                                   (256, 512, 128), (64, 1024, 32)])
+def test_int2_quantize_and_pack_match_oracle(N, K, G):
+    w = _w(N, K, 0.02, 7 * N + K + G)
+    w[2, G:2 * G] = 0.0                                 # an all-zero group
+    p = q.problem(1, N, K, "int2", group_size=G)
+    codes_b, scales_b, alpha = q.quantize(p, w)
+    codes_o, sbits_o = quant.quantize_int2(w, G)
+    assert alpha == 1.0
+    assert np.array_equal(codes_b, quant.pack_crumbs(codes_o))
+    assert np.array_equal(scales_b, sbits_o)
+    wpk, spk = q.pack(p, codes_b, scales_b)
+    assert wpk.size == N * K // 4
+    assert np.array_equal(wpk, layout.device_int2_weights(codes_o))
+    assert np.array_equal(spk.view(np.uint16), layout.device_int4_scales(sbits_o, N, K, G))
+
+
+def test_int2_pack_every_code_position():
+    # random codes (the quantizer never emits code 0, the layout must still carry it)
+    N, K = 64, 512
+    codes = np.random.default_rng(9).integers(0, 4, (N, K)).astype(np.uint8)
+    sb = np.full((K // 128, N), 0x3C00, np.uint16)
+    wpk, _ = q.pack(q.problem(1, N, K, "int2"), quant.pack_crumbs(codes), sb)
+    assert np.array_equal(wpk, layout.device_int2_weights(codes))
+    assert np.array_equal(layout.device_int2_weights_inverse(wpk, N, K), codes)

@@ -238,13 +238,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
     if (!splitk_finish<1, NT>(a, group, split, CB * 256, active, v)) return;
   }
   if (!active || nb0 + c >= NB) return;
-  const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
+  const float alpha = qgemm::int_weights(FMT) ? 1.0f : *a.alpha;
   const int n = (nb0 + c) * 16 + (ln & 15);
   const float bv = bias_of(a, n);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * (ln >> 4) + r;
-    if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[0][r] : v[0][r] * alpha, bv);
+    if (m < a.M) store_out(a, m, n, qgemm::int_weights(FMT) ? v[0][r] : v[0][r] * alpha, bv);
   }
 }
 
@@ -290,7 +290,7 @@ struct DecodeLauncher {
   }
 };
 
-// Instances for every group size the format has (INT4: 32, 64, 128, 256; FP8 / FP4: none).
+// Instances for every group size the format has (INT4, INT2: 32, 64, 128, 256; FP8 / FP4: none).
 template <template <int, int> class L>
 hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
   switch (pl.fmt) {
@@ -300,6 +300,14 @@ hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t
         case 64: return L<FMT_INT4, 64>::run(pl, a, stream);
         case 128: return L<FMT_INT4, 128>::run(pl, a, stream);
         case 256: return L<FMT_INT4, 256>::run(pl, a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    case FMT_INT2:
+      switch (group_size) {
+        case 32: return L<FMT_INT2, 32>::run(pl, a, stream);
+        case 64: return L<FMT_INT2, 64>::run(pl, a, stream);
+        case 128: return L<FMT_INT2, 128>::run(pl, a, stream);
+        case 256: return L<FMT_INT2, 256>::run(pl, a, stream);
         default: return hipErrorInvalidValue;
       }
     case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);

@@ -101,6 +101,26 @@ __device__ __forceinline__ u32x4 dq_int4(unsigned w, unsigned s2) {
                __builtin_bit_cast(unsigned, h2), __builtin_bit_cast(unsigned, h3)};
 }
 
+// INT2: byte b of either 16-bit half of dword w carries one K step, field f (bits 2f, 2f+1
+// of the byte) the k pair (2f, 2f + 1), the even k in the low half.  OR-ing the masked
+// field into the exponent of 2^(10 - 2f) gives 2^(10 - 2f) + code exactly; subtracting
+// 2^(10 - 2f) + 2 leaves the signed value, which the scale multiplies (RNE_fp16, exact while
+// the product stays in range: at most 12 significant bits).
+__device__ __forceinline__ u32x4 dq_int2(unsigned w, int b, unsigned s2) {
+  const unsigned x = b ? w >> 8 : w;
+  const unsigned p0 = and_or<0x00030003u, 0x64006400u>(x);    // k 0, 1: 1024 + code
+  const unsigned p1 = and_or<0x000C000Cu, 0x5C005C00u>(x);    // k 2, 3: 256 + code
+  const unsigned p2 = and_or<0x00300030u, 0x54005400u>(x);    // k 4, 5: 64 + code
+  const unsigned p3 = and_or<0x00C000C0u, 0x4C004C00u>(x);    // k 6, 7: 16 + code
+  const f16x2 s = __builtin_bit_cast(f16x2, s2);
+  const f16x2 b0 = {(_Float16)1026.0f, (_Float16)1026.0f}, b1 = {(_Float16)258.0f, (_Float16)258.0f};
+  const f16x2 b2 = {(_Float16)66.0f, (_Float16)66.0f}, b3 = {(_Float16)18.0f, (_Float16)18.0f};
+  return u32x4{__builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p0) - b0) * s),
+               __builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p1) - b1) * s),
+               __builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p2) - b2) * s),
+               __builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p3) - b3) * s)};
+}
+
 __device__ __forceinline__ u32x4 dq_fp8(unsigned lo, unsigned hi) {
   return u32x4{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
                __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
@@ -158,7 +178,7 @@ struct WFrag {
   unsigned s[2];    // INT4: 1, 2 or 4 fp16 scales (G = 128|256, 64, 32); FP4: 4 e4m3 bytes
 };
 
-// G is the INT4 group size (a template parameter, so the scale load has no branches:
+// G is the INT4 / INT2 group size (a template parameter, so the scale load has no branches:
 // a branch around a load ends in a wait for every outstanding load); 0 for FP8 / FP4.
 // STREAM marks weights read once (decode: non-temporal loads keep them out of the way in
 // the caches); prefill re-reads each weight fragment once per row tile and caches it.
@@ -175,13 +195,19 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
     const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * (KB * 2) + 2 * kb) * 1024) + lane;
     f.w[0] = wload<STREAM>(p);
     f.w[1] = wload<STREAM>(p + 64);
+  } else if constexpr (FMT == qgemm::FMT_INT2) {   // 512-byte blocks, 8 bytes per lane
+    const u32x2* p = reinterpret_cast<const u32x2*>(a.W + ((size_t)nb * KB + kb) * 512) + lane;
+    u32x2 x;
+    if constexpr (STREAM) x = __builtin_nontemporal_load(p);
+    else x = *p;
+    f.w[0] = u32x4{x[0], x[1], 0u, 0u};
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(a.W + ((size_t)nb * KB + kb) * 1024) + lane;
     f.w[0] = wload<STREAM>(p);
   }
   if constexpr (!SCALES) {
     return;
-  } else if constexpr (FMT == qgemm::FMT_INT4) {
+  } else if constexpr (qgemm::int_weights(FMT)) {
     const uint16_t* S = static_cast<const uint16_t*>(a.S);
     const int c = lane & 15;
     if constexpr (G <= 128) {
@@ -211,14 +237,14 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
 // column block's scales.  FP8 has none.
 template <int FMT, int G>
 __device__ __forceinline__ int sc_rel(int kb) {
-  if constexpr (FMT == qgemm::FMT_INT4) return G <= 128 ? kb * 32 * (128 / G) : (kb >> 1) * 32;
+  if constexpr (qgemm::int_weights(FMT)) return G <= 128 ? kb * 32 * (128 / G) : (kb >> 1) * 32;
   else if constexpr (FMT == qgemm::FMT_FP4) return kb * 128;
   else return 0;
 }
 // End of the scale bytes that cover k blocks up to kb_end (exclusive); a group of 256 is kept whole.
 template <int FMT, int G>
 __device__ __forceinline__ int sc_end(int kb_end) {
-  return sc_rel<FMT, G>(FMT == qgemm::FMT_INT4 && G > 128 ? kb_end + 1 : kb_end);
+  return sc_rel<FMT, G>(qgemm::int_weights(FMT) && G > 128 ? kb_end + 1 : kb_end);
 }
 
 // Scales of k block kb for this lane's column, from an LDS copy of one column block's packed
@@ -227,7 +253,7 @@ template <int FMT, int G>
 __device__ __forceinline__ void read_staged_scales(const unsigned char* s, int kb, int kb_begin, int lane,
                                                    WFrag<FMT>& f) {
   const unsigned char* p = s + (sc_rel<FMT, G>(kb) - sc_rel<FMT, G>(kb_begin));
-  if constexpr (FMT == qgemm::FMT_INT4) {
+  if constexpr (qgemm::int_weights(FMT)) {
     constexpr int T = G <= 128 ? 128 / G : 1;
     p += (lane & 15) * T * 2;
     if constexpr (T == 4) {
@@ -259,6 +285,8 @@ template <int FMT, int G>
 __device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (&fs)[4]) {
   if constexpr (FMT == qgemm::FMT_INT4) {
     return dq_int4(f.w[0][t], int4_scale_pair<G>(f.s, t));
+  } else if constexpr (FMT == qgemm::FMT_INT2) {
+    return dq_int2(f.w[0][t >> 1], t & 1, int4_scale_pair<G>(f.s, t));
   } else if constexpr (FMT == qgemm::FMT_FP8) {
     return dq_fp8(f.w[t >> 1][2 * (t & 1)], f.w[t >> 1][2 * (t & 1) + 1]);
   } else if constexpr (FMT == qgemm::FMT_FP8H) {

@@ -35,12 +35,14 @@ static const char* dtype_name(int d) {
     case QGEMM_DT_INT4: return "INT4";
     case QGEMM_DT_FP8_E4M3: return "FP8_E4M3";
     case QGEMM_DT_FP4_E2M1: return "FP4_E2M1";
+    case QGEMM_DT_INT2: return "INT2";
     default: return "?";
   }
 }
 
 Format format_of(const qgemm_problem_t* p) {
   if (p->w_dtype == QGEMM_DT_INT4) return FMT_INT4;
+  if (p->w_dtype == QGEMM_DT_INT2) return FMT_INT2;
   if (p->w_dtype == QGEMM_DT_FP8_E4M3) return p->a_dtype == QGEMM_DT_F16 ? FMT_FP8H : FMT_FP8;
   return FMT_FP4;
 }
@@ -52,7 +54,7 @@ static const int64_t kMaxDim = int64_t(1) << 24;
 qgemm_status_t validate_problem(const qgemm_problem_t* p) {
   if (!p) return fail(QGEMM_ERR_INVALID_ARGUMENT, "problem is NULL");
   for (int d : {p->a_dtype, p->w_dtype, p->out_dtype})
-    if (d < QGEMM_DT_F16 || d > QGEMM_DT_FP4_E2M1)
+    if (d < QGEMM_DT_F16 || d > QGEMM_DT_INT2)
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "dtype value %d is not a qgemm_dtype_t", d);
   if (p->scale_layout < QGEMM_SCALE_GROUP_F16 || p->scale_layout > QGEMM_SCALE_BLOCK16_E4M3)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "scale_layout %d is not a qgemm_scale_layout_t", p->scale_layout);
@@ -66,12 +68,13 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
                 (long long)kMaxDim, (long long)p->K);
 
   const int a = p->a_dtype, w = p->w_dtype, o = p->out_dtype, sl = p->scale_layout, g = p->group_size;
-  if (w == QGEMM_DT_INT4) {
+  if (w == QGEMM_DT_INT4 || w == QGEMM_DT_INT2) {
+    const char* wn = dtype_name(w);
     if (a != QGEMM_DT_F16 || sl != QGEMM_SCALE_GROUP_F16 || (o != QGEMM_DT_F16 && o != QGEMM_DT_F32))
-      return fail(QGEMM_ERR_UNSUPPORTED, "INT4 weights need a_dtype F16, scale_layout GROUP_F16 and out_dtype F16 or F32; "
-                  "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
+      return fail(QGEMM_ERR_UNSUPPORTED, "%s weights need a_dtype F16, scale_layout GROUP_F16 and out_dtype F16 or F32; "
+                  "got a=%s out=%s scale_layout=%d", wn, dtype_name(a), dtype_name(o), sl);
     if (g != 32 && g != 64 && g != 128 && g != 256)
-      return fail(QGEMM_ERR_UNSUPPORTED, "INT4 group_size must be 32, 64, 128 or 256, got %d", g);
+      return fail(QGEMM_ERR_UNSUPPORTED, "%s group_size must be 32, 64, 128 or 256, got %d", wn, g);
     if (p->K % g) return fail(QGEMM_ERR_INVALID_ARGUMENT, "K (%lld) must be a multiple of group_size (%d)", (long long)p->K, g);
   } else if (w == QGEMM_DT_FP8_E4M3) {
     // mm_bf16_fp8 and mm_fp16_fp8: the output is the activations' 16-bit type or fp32
@@ -85,7 +88,7 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
                   "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
     if (g != 16) return fail(QGEMM_ERR_INVALID_ARGUMENT, "FP4_E2M1 takes group_size 16 (one e4m3 scale per 16 K), got %d", g);
   } else {
-    return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, FP8_E4M3, FP4_E2M1)", dtype_name(w));
+    return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, INT2, FP8_E4M3, FP4_E2M1)", dtype_name(w));
   }
 
   if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL)
@@ -334,12 +337,16 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* p, const float* w_nk, void*
   if (!w_nk || !codes_canonical) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk and codes_canonical must not be NULL");
   const Format fmt = format_of(p);
   if (!fp8_weights(fmt) && !scales_canonical)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical must not be NULL for INT4 / FP4");
-  if (fmt != FMT_INT4 && !alpha_out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha_out must not be NULL for FP8 / FP4");
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical must not be NULL for INT4 / INT2 / FP4");
+  if (!int_weights(fmt) && !alpha_out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha_out must not be NULL for FP8 / FP4");
   const int64_t N = p->N, K = p->K;
   uint8_t* codes = static_cast<uint8_t*>(codes_canonical);
 
-  if (fmt == FMT_INT4) {
+  if (int_weights(fmt)) {
+    // symmetric absmax per (group, column): s = RNE_fp16(absmax / qmax), code = clamp(rint(w / s),
+    // -qmax-1, qmax) + qmax + 1 with qmax = 7 (INT4) or 1 (INT2)
+    const bool i2 = fmt == FMT_INT2;
+    const double qmax = i2 ? 1.0 : 7.0;
     const int G = p->group_size;
     uint16_t* sc = static_cast<uint16_t*>(scales_canonical);   // [K/G][N]
     std::vector<uint8_t> q(K);
@@ -353,17 +360,23 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* p, const float* w_nk, void*
             return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk[%lld] is not finite", (long long)(n * K + g * G + i));
           amax = v > amax ? v : amax;
         }
-        double s = round_format(amax / 7.0, 10, -14);
+        double s = round_format(amax / qmax, 10, -14);
         if (!(s <= 65504.0))
           return fail(QGEMM_ERR_INVALID_ARGUMENT, "column %lld group %lld: absmax %g is not finite or its scale overflows fp16",
                       (long long)n, (long long)g, amax);
         sc[g * N + n] = f16_bits_of(s);
         for (int i = 0; i < G; ++i) {
-          double v = s == 0.0 ? 0.0 : clampd(std::nearbyint((double)row[g * G + i] / s), -8.0, 7.0);
-          q[g * G + i] = (uint8_t)((int)v + 8);
+          double v = s == 0.0 ? 0.0 : clampd(std::nearbyint((double)row[g * G + i] / s), -qmax - 1.0, qmax);
+          q[g * G + i] = (uint8_t)((int)v + (int)qmax + 1);
         }
       }
-      for (int64_t j = 0; j < K / 2; ++j) codes[n * (K / 2) + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+      if (i2) {   // four codes per byte, lowest k in the lowest bits
+        for (int64_t j = 0; j < K / 4; ++j)
+          codes[n * (K / 4) + j] =
+              (uint8_t)(q[4 * j] | (q[4 * j + 1] << 2) | (q[4 * j + 2] << 4) | (q[4 * j + 3] << 6));
+      } else {    // two per byte, low nibble = even k
+        for (int64_t j = 0; j < K / 2; ++j) codes[n * (K / 2) + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+      }
     }
     if (alpha_out) *alpha_out = 1.0f;
     return QGEMM_OK;
@@ -425,9 +438,9 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed_bytes and s_packed_bytes must not be NULL");
   const Format fmt = format_of(p);
   const int64_t N = p->N, K = p->K, NB = N / 16;
-  const size_t need_w = fp8_weights(fmt) ? (size_t)(N * K) : (size_t)(N * K / 2);
+  const size_t need_w = fp8_weights(fmt) ? (size_t)(N * K) : fmt == FMT_INT2 ? (size_t)(N * K / 4) : (size_t)(N * K / 2);
   size_t need_s = 0;
-  if (fmt == FMT_INT4) need_s = (size_t)(N * (K / p->group_size)) * 2;
+  if (int_weights(fmt)) need_s = (size_t)(N * (K / p->group_size)) * 2;
   if (fmt == FMT_FP4) need_s = (size_t)(N * (K / 16));
   const size_t cap_w = *w_packed_bytes, cap_s = *s_packed_bytes;
   *w_packed_bytes = need_w;
@@ -454,6 +467,28 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
           for (int lane = 0; lane < 64; ++lane) {
             const uint8_t* col = src + (nb * 16 + (lane & 15)) * K + kb * 64 + 8 * (lane >> 4);
             for (int t = 0; t < 2; ++t) std::memcpy(blk + 16 * lane + 8 * t, col + 32 * t, 8);
+          }
+        }
+    } else if (fmt == FMT_INT2) {
+      // 512-byte block = 16 columns x 128 k; lane l owns 2 dwords; bits 16h + 8b + 2f of dword
+      // d hold column l & 15 at k = 32(2d + b) + 8(l >> 4) + 2f + h.
+      const int64_t KB = K / 128;
+      for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t kb = 0; kb < KB; ++kb) {
+          uint8_t* blk = dst + (nb * KB + kb) * 512;
+          for (int lane = 0; lane < 64; ++lane) {
+            const uint8_t* col = src + (nb * 16 + (lane & 15)) * (K / 4);
+            for (int d = 0; d < 2; ++d) {
+              uint32_t word = 0;
+              for (int h = 0; h < 2; ++h)
+                for (int b = 0; b < 2; ++b)
+                  for (int f = 0; f < 4; ++f) {
+                    const int64_t k = kb * 128 + 32 * (2 * d + b) + 8 * (lane >> 4) + 2 * f + h;
+                    const uint32_t code = (col[k >> 2] >> (2 * (k & 3))) & 3;
+                    word |= code << (16 * h + 8 * b + 2 * f);
+                  }
+              std::memcpy(blk + 8 * lane + 4 * d, &word, 4);
+            }
           }
         }
     } else {
@@ -484,7 +519,7 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
   }
 
   if (s_packed && need_s) {
-    if (fmt == FMT_INT4) {
+    if (int_weights(fmt)) {
       const int G = p->group_size;
       const int span = G > 128 ? G : 128;
       const int T = G < 128 ? 128 / G : 1;

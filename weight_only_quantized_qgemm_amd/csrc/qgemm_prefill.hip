@@ -219,7 +219,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   if (a.splits > 1) {
     if (!splitk_finish<TM * TN, NT>(a, tile, split, BM * BN, true, v)) return;
   }
-  const float alpha = FMT == qgemm::FMT_INT4 ? 1.0f : *a.alpha;
+  const float alpha = qgemm::int_weights(FMT) ? 1.0f : *a.alpha;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int nb = (n0 >> 4) + TN * wn + j;
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * TM * wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < a.M) store_out(a, m, n, FMT == qgemm::FMT_INT4 ? v[TN * i + j][r] : v[TN * i + j][r] * alpha, bv);
+        if (m < a.M) store_out(a, m, n, qgemm::int_weights(FMT) ? v[TN * i + j][r] : v[TN * i + j][r] * alpha, bv);
       }
   }
 }
@@ -254,7 +254,7 @@ struct PrefillLauncher {
   }
 };
 
-// Instances for every group size the format has (INT4: 32, 64, 128, 256; FP8 / FP4: none).
+// Instances for every group size the format has (INT4, INT2: 32, 64, 128, 256; FP8 / FP4: none).
 template <template <int, int> class L>
 hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
   switch (pl.fmt) {
@@ -264,6 +264,14 @@ hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t
         case 64: return L<FMT_INT4, 64>::run(pl, a, stream);
         case 128: return L<FMT_INT4, 128>::run(pl, a, stream);
         case 256: return L<FMT_INT4, 256>::run(pl, a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    case FMT_INT2:
+      switch (group_size) {
+        case 32: return L<FMT_INT2, 32>::run(pl, a, stream);
+        case 64: return L<FMT_INT2, 64>::run(pl, a, stream);
+        case 128: return L<FMT_INT2, 128>::run(pl, a, stream);
+        case 256: return L<FMT_INT2, 256>::run(pl, a, stream);
         default: return hipErrorInvalidValue;
       }
     case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);

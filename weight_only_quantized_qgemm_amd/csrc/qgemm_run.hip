@@ -22,15 +22,15 @@ extern "C" qgemm_status_t qgemm_run_bias(const qgemm_problem_t* p, const void* A
   if (!A) return fail(QGEMM_ERR_INVALID_ARGUMENT, "A is NULL");
   if (!w_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_packed is NULL");
   if (!out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "out is NULL");
-  if (!fp8_weights(fmt) && !s_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "s_packed is NULL (needed for INT4 and FP4)");
-  if (fmt != FMT_INT4 && !alpha) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha is NULL (needed for FP8 and FP4)");
+  if (!fp8_weights(fmt) && !s_packed) return fail(QGEMM_ERR_INVALID_ARGUMENT, "s_packed is NULL (needed for INT4, INT2 and FP4)");
+  if (!int_weights(fmt) && !alpha) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha is NULL (needed for FP8 and FP4)");
   if (!aligned(A, 16)) return fail(QGEMM_ERR_MISALIGNED, "A must be 16-byte aligned");
   if (!aligned(w_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "w_packed must be 16-byte aligned");
   if (s_packed && !fp8_weights(fmt) && !aligned(s_packed, 16)) return fail(QGEMM_ERR_MISALIGNED, "s_packed must be 16-byte aligned");
   // a bias takes the alignment the FlashInfer fix requires of it (PR #7495 analysis,
   // section 3(a): 16 bytes when a bias is given, 4 for the scalar alpha)
   if (bias && !aligned(bias, 16)) return fail(QGEMM_ERR_MISALIGNED, "bias must be 16-byte aligned");
-  if (alpha && fmt != FMT_INT4 && !aligned(alpha, 4)) return fail(QGEMM_ERR_MISALIGNED, "alpha must be 4-byte aligned");
+  if (alpha && !int_weights(fmt) && !aligned(alpha, 4)) return fail(QGEMM_ERR_MISALIGNED, "alpha must be 4-byte aligned");
   if (!aligned(out, 16)) return fail(QGEMM_ERR_MISALIGNED, "out must be 16-byte aligned");
 
   Plan pl;
