@@ -19,6 +19,8 @@ INT4 (w_dtype INT4) and FP4 (w_dtype FP4_E2M1) weights
     for nibble slot s = 0..7 (slot s = bits 4s .. 4s+3 of the little-endian dword).
       INT4: J = (0, 2, 4, 6, 1, 3, 5, 7)
       FP4 : J = (0, 1, 2, 3, 4, 5, 6, 7)
+      NF4 : J = (0, 4, 1, 5, 2, 6, 3, 7)  (byte b: k offsets b and b + 4, the order in which
+            a byte-wise table lookup yields fp16 pairs (k, k+1) with one byte shuffle)
 INT2 (w_dtype INT2) weights
     block (nb, kb) = columns 16*nb .. 16*nb+15, k = 128*kb .. 128*kb+127, 512 bytes, block
     index nb * (K/128) + kb.  Lane l owns bytes [8*l, 8*l + 8): dword d (d = 0..1) holds 16
@@ -31,6 +33,9 @@ FP8 weights
     block (nb, kb) = 16 columns x 64 k, 1024 bytes, block index nb * (K/64) + kb;
     lane l owns 16 bytes: byte 8*t + j (t = 0..1, j = 0..7) is column 16*nb + (l & 15),
     k = 64*kb + 32*t + 8*(l >> 4) + j.
+NF4 scales
+    a 256-byte header, then the INT4 scale layout.  Header byte c (0..15) = low byte of the
+    fp16 code-book entry T[c], byte 16 + c = its high byte, bytes 32..255 = 0.
 INT4 and INT2 scales (fp16)
     span = max(G, 128); T = max(1, 128 / G) scales per (column, span).
     Element index ((nb * (K/span) + kb) * 16 + c) * T + t holds the scale of column
@@ -44,6 +49,8 @@ import numpy as np
 
 J_INT4 = (0, 2, 4, 6, 1, 3, 5, 7)
 J_FP4 = (0, 1, 2, 3, 4, 5, 6, 7)
+J_NF4 = (0, 4, 1, 5, 2, 6, 3, 7)
+LUT_HEADER_BYTES = 256
 
 
 def _nibble_positions(N, K, J):
@@ -193,3 +200,21 @@ def device_fp4_scales(sf_codes, N, K):
     n = 16 * nb + c + 0 * (kb + h + t)
     blk = 8 * kb + 2 * t + h + 0 * (nb + c)
     return sf_codes[n, blk].reshape(-1)
+
+
+def device_nf4_weights(codes):
+    return _nibble_layout(codes, J_NF4)
+
+
+def device_nf4_weights_inverse(packed, N, K):
+    return _nibble_unlayout(packed, N, K, J_NF4)
+
+
+def device_nf4_scales(book_bits, scale_bits, N, K, G):
+    """book_bits uint16 [16], scale_bits uint16 [K/G, N] -> packed bytes per the NF4 scale spec."""
+    book = np.asarray(book_bits, dtype=np.uint16)
+    head = np.zeros(LUT_HEADER_BYTES, np.uint8)
+    head[:16] = book & 0xFF
+    head[16:32] = book >> 8
+    body = device_int4_scales(scale_bits, N, K, G).astype("<u2").view(np.uint8)
+    return np.concatenate([head, body])

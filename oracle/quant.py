@@ -11,7 +11,7 @@ Readings where the pages are silent (each is listed in the design notes):
 * the quantizer divides by the *stored* (already rounded) scale, so that dequantizing
   the stored codes and scales is self-consistent;
 * an all-zero INT4 group gets scale 0 and codes 8 (signed 0), an all-zero INT2 group scale 0
-  and codes 2; an all-zero FP4 block gets scale code 0 and codes 0; an all-zero FP8 tensor
+  and codes 2, an all-zero NF4 group scale 0 and the code of the book's 0; an all-zero FP4 block gets scale code 0 and codes 0; an all-zero FP8 tensor
   gets alpha 0 and codes 0.
 """
 import numpy as np
@@ -71,6 +71,54 @@ def quantize_int2(wt, group_size):
     codes = (q + 2).astype(np.uint8).reshape(N, K)
     scale_bits = codecs.f16_bits(s).T.copy()            # [K/G, N]
     return codes, scale_bits
+
+
+# ----------------------------------------------------------------------------- NF4
+NF4_DELTA = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0))
+
+
+def nf4_codebook():
+    """The NormalFloat-4 code book as fp16 values (float64 [16], ascending).
+
+    Low Bit Triton Kernels (lecture 034) names NF4 as the non-uniform choice of the 16
+    values a 4-bit weight can take, read through a table held in registers; the pages give
+    no values.  Reading: QLoRA's construction -- quantiles of the standard normal at evenly
+    spaced probabilities, 8 for the positive half (from delta down to, not including, 1/2)
+    and 7 for the negative half, plus an exact zero, divided by the largest so the book
+    spans [-1, 1]; delta = ((1 - 1/30) + (1 - 1/32)) / 2 lies between the outermost quantile
+    estimates of a 15- and a 16-point grid.  Each value is then rounded to fp16, the type
+    the book is stored in.
+    """
+    from scipy.special import ndtri
+    pos = ndtri(np.linspace(NF4_DELTA, 0.5, 9)[:-1])      # 8 values, largest first
+    neg = -ndtri(np.linspace(NF4_DELTA, 0.5, 8)[:-1])     # 7 values, most negative first
+    v = np.sort(np.concatenate([neg, [0.0], pos]))
+    return codecs.f16_round(v / v.max())
+
+
+def quantize_nf4(wt, group_size, book=None):
+    """NF4 per (K-group, column): s = RNE_fp16(absmax) (the book spans [-1, 1]), code = index
+    of the book entry nearest to w / s, ties to the lower index; all-zero group: s = 0 and
+    the code of the entry 0 (7 in the NF4 book).
+
+    wt: float32 [N, K]; book: fp16 values [16] (default: nf4_codebook()).
+    Returns (codes uint8 [N, K] in 0..15, scale_bits uint16 [K/G, N], book_bits uint16 [16]).
+    """
+    wt = np.asarray(wt, dtype=np.float32)
+    N, K = wt.shape
+    G = int(group_size)
+    if K % G:
+        raise ValueError("K must be a multiple of group_size")
+    book = nf4_codebook() if book is None else np.asarray(book, dtype=np.float64)
+    zero_code = int(np.argmin(np.abs(book)))
+    w = wt.astype(np.float64).reshape(N, K // G, G)
+    s = codecs.f16_round(np.abs(w).max(axis=2))           # [N, K/G]
+    safe = np.where(s == 0, 1.0, s)
+    x = w / safe[:, :, None]
+    codes = np.argmin(np.abs(x[..., None] - book), axis=-1)   # first minimum: lower index
+    codes = np.where(s[:, :, None] == 0, zero_code, codes)
+    return (codes.astype(np.uint8).reshape(N, K), codecs.f16_bits(s).T.copy(),
+            codecs.f16_bits(book).astype(np.uint16))
 
 
 # ----------------------------------------------------------------------------- FP8

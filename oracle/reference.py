@@ -47,6 +47,25 @@ def dequant_int2(codes, scale_bits, group_size):
     return (q * s_nk).astype(np.float32)
 
 
+def dequant_nf4(codes, scale_bits, group_size, book_bits):
+    """T[code] * s in float32, exact (two fp16 values: at most 22 significant bits).
+
+    codes [N, K] in 0..15, scale_bits uint16 [K/G, N], book_bits uint16 [16] (the fp16 code
+    book).  The non-uniform 4-bit grid of Low Bit Triton Kernels (lecture 034): the code
+    indexes the book, the group scale multiplies the entry.  Returns float32 [N, K].
+    """
+    t = codecs.f16_from_bits(book_bits)[np.asarray(codes, dtype=np.int64)]
+    s = codecs.f16_from_bits(scale_bits)               # [K/G, N]
+    s_nk = np.repeat(s.T, group_size, axis=1)          # [N, K]
+    return (t * s_nk).astype(np.float32)
+
+
+def dequant_nf4_f16(codes, scale_bits, group_size, book_bits):
+    """The fp16 operand of an NF4 tile: RNE_fp16(T[code] * s), as INT4's RNE_fp16((n - 8) s).
+    Returns float64 values of fp16 numbers, [N, K]."""
+    return codecs.f16_round(dequant_nf4(codes, scale_bits, group_size, book_bits).astype(np.float64))
+
+
 def dequant_fp8(codes):
     """e4m3 code -> value (exact); alpha is NOT applied here.  Returns float32 [N, K].
 

@@ -119,3 +119,33 @@ def test_int2_closed_forms_and_identity():
     assert np.array_equal(reference.gemm_fp64(np.eye(K), dq), dq.T.astype(np.float64))
     # the products are exact in fp16 too: the 16-bit operand equals the exact value
     assert np.array_equal(codecs.f16_round(dq.astype(np.float64)), dq.astype(np.float64))
+
+
+def test_nf4_closed_forms_and_identity():
+    M, N, K, G = 3, 32, 256, 128
+    a = np.random.default_rng(19).standard_normal((M, K)).astype(np.float16).astype(np.float64)
+    one = codecs.f16_bits(np.ones((K // G, N)))
+    book_bits = codecs.f16_bits(quant.nf4_codebook())
+    book = codecs.f16_from_bits(book_bits)
+    for c in range(16):
+        codes = np.full((N, K), c, np.uint8)
+        r = reference.gemm_fp64(a, reference.dequant_nf4(codes, one, G, book_bits))
+        assert np.allclose(r, (book[c] * a.sum(axis=1))[:, None], rtol=0, atol=1e-12)
+    # one nonzero group: s * (A_group . book[q_group])
+    codes = np.full((N, K), 7, np.uint8)
+    q = np.random.default_rng(20).integers(0, 16, G)
+    codes[4, G:2 * G] = q
+    sb = np.zeros((K // G, N), np.uint16)
+    sb[1, 4] = 0x3555                                       # an fp16 scale with a full mantissa
+    r = reference.gemm_fp64(a, reference.dequant_nf4(codes, sb, G, book_bits))
+    s = float(codecs.f16_from_bits(np.array([0x3555], np.uint16))[0])
+    want = s * (a[:, G:2 * G] @ book[q])
+    assert np.allclose(r[:, 4], want, rtol=1e-14, atol=0) and not np.any(np.delete(r, 4, axis=1))
+    # identity A returns the dequantized weights; the fp16 operand is their RNE_fp16
+    wt = (np.random.default_rng(21).standard_normal((N, K)) * 0.02).astype(np.float32)
+    codes, sb, bb = quant.quantize_nf4(wt, 32)
+    dq = reference.dequant_nf4(codes, sb, 32, bb)
+    assert np.array_equal(reference.gemm_fp64(np.eye(K), dq), dq.T.astype(np.float64))
+    f16 = reference.dequant_nf4_f16(codes, sb, 32, bb)
+    assert np.array_equal(f16, codecs.f16_round(dq.astype(np.float64)))
+    assert np.max(np.abs(f16 - dq)) <= np.max(np.abs(dq)) * 2.0 ** -11

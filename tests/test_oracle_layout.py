@@ -117,3 +117,37 @@ def test_int2_single_hot(n, k, byte, shift):
 def test_int2_round_trip():
     c = np.random.default_rng(4).integers(0, 4, (48, 384)).astype(np.uint8)
     assert np.array_equal(layout.device_int2_weights_inverse(layout.device_int2_weights(c), 48, 384), c)
+
+
+@pytest.mark.parametrize("n,k,byte,shift", [
+    # NF4, N=32, K=256: J = (0,4,1,5,2,6,3,7), so byte b of a dword holds k offsets b (low
+    # nibble) and b + 4 (high nibble)
+    (0, 0, 0, 0),
+    (0, 1, 1, 0),                      # offset 1 -> slot 2 -> byte 1 low
+    (0, 4, 0, 4),                      # offset 4 -> slot 1 -> byte 0 high
+    (0, 7, 3, 4),                      # offset 7 -> slot 7 -> byte 3 high
+    (5, 14, 16 * 21 + 2, 4),           # lane 21, t0, offset 6 -> slot 5 -> byte 2 high
+    (17, 131, 3072 + 16 + 3, 0),       # block 3, lane 1, offset 3 -> slot 6 -> byte 3 low
+    # n=31 k=255: block 3; k' = 127 = 32*3 + 8*3 + 7 -> t3, lane 63, offset 7 -> byte 3 high
+    (31, 255, 3072 + 16 * 63 + 12 + 3, 4),
+])
+def test_nf4_single_hot(n, k, byte, shift):
+    codes = np.zeros((32, 256), np.uint8)
+    codes[n, k] = 0xD
+    p = layout.device_nf4_weights(codes)
+    assert list(np.flatnonzero(p)) == [byte]
+    assert p[byte] == 0xD << shift
+
+
+def test_nf4_round_trip_and_scale_header():
+    c = np.random.default_rng(5).integers(0, 16, (48, 384)).astype(np.uint8)
+    assert np.array_equal(layout.device_nf4_weights_inverse(layout.device_nf4_weights(c), 48, 384), c)
+    N, K, G = 32, 256, 64
+    book = (0x1234 + 0x0101 * np.arange(16)).astype(np.uint16)
+    s = np.arange((K // G) * N, dtype=np.uint16).reshape(K // G, N)
+    p = layout.device_nf4_scales(book, s, N, K, G)
+    assert p.size == 256 + 2 * s.size
+    assert list(p[:16]) == [0x34 + i for i in range(16)]    # low bytes of the book
+    assert list(p[16:32]) == [0x12 + i for i in range(16)]  # high bytes
+    assert not p[32:256].any()
+    assert np.array_equal(p[256:].view("<u2"), layout.device_int4_scales(s, N, K, G))

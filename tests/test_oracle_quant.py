@@ -179,3 +179,86 @@ def test_int2_brute_force_nearest_and_invariants():
     assert np.all(codes[5, 128:192] == 2) and s[2, 5] == 0
     err = np.abs(wt - reference.dequant_int2(codes, sbits, G))
     assert np.all(err <= s_nk / 2 * (1 + 1e-6) + 1e-12)
+
+
+def _phi_inverse_by_bisection(p):
+    """Standard normal quantile from math.erf alone (independent of scipy's ndtri)."""
+    import math
+    lo, hi = -10.0, 10.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if 0.5 * (1.0 + math.erf(mid / math.sqrt(2.0))) < p:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def test_nf4_codebook_definition():
+    book = quant.nf4_codebook()
+    assert book.shape == (16,)
+    assert np.all(np.diff(book) > 0)                        # strictly ascending
+    assert book[0] == -1.0 and book[7] == 0.0 and book[15] == 1.0
+    assert np.sum(book < 0) == 7 and np.sum(book > 0) == 8  # asymmetric: exact zero, 8 positive
+    assert np.array_equal(codecs.f16_round(book), book)     # stored in fp16
+    # the quantile construction, recomputed with a different routine, gives the same fp16 book
+    d = ((1 - 1 / 30) + (1 - 1 / 32)) / 2
+    top = _phi_inverse_by_bisection(d)
+    pos = [_phi_inverse_by_bisection(d + (0.5 - d) * i / 8) / top for i in range(8)]
+    neg = [-_phi_inverse_by_bisection(d + (0.5 - d) * i / 7) / top for i in range(7)]
+    want = codecs.f16_round(np.sort(np.array(pos + neg + [0.0])))
+    assert np.array_equal(book, want)
+    # equal-probability spacing: Phi of consecutive positive quantiles differs by (d - 1/2) / 8
+    import math
+    phi = [0.5 * (1 + math.erf(p * top / math.sqrt(2))) for p in pos]
+    assert np.allclose(np.diff(phi), -(d - 0.5) / 8, rtol=0, atol=1e-12)
+
+
+def test_nf4_worked_example():
+    g = tagged("worked_nf4.txt")
+    wt = _w(g["w"])
+    codes, sbits, book_bits = quant.quantize_nf4(wt, 4)
+    for i, v in g["book"].items():
+        assert book_bits[i] == v[0]
+    want_s = np.array([g["scale"][i] for i in sorted(g["scale"])], np.uint16)
+    assert np.array_equal(sbits, want_s)
+    want_b = np.array([g["bytes"][i] for i in sorted(g["bytes"])], np.uint8)
+    assert np.array_equal(quant.pack_nibbles(codes), want_b)
+    a = np.array([g["a"][i] for i in sorted(g["a"])])
+    out = reference.gemm_fp64(a, reference.dequant_nf4(codes, sbits, 4, book_bits))
+    want = np.array([g["out"][i] for i in sorted(g["out"])])
+    assert np.array_equal(out, want)
+
+
+def test_nf4_brute_force_nearest_and_invariants():
+    G = 64
+    wt = (np.random.default_rng(18).standard_normal((16, 256)) * 0.02).astype(np.float32)
+    wt[3, 64:128] = 0.0                                     # an all-zero group
+    codes, sbits, book_bits = quant.quantize_nf4(wt, G)
+    book = codecs.f16_from_bits(book_bits)
+    s = codecs.f16_from_bits(sbits)                         # [K/G, N]
+    for n in range(16):
+        for k in range(256):
+            sk = s[k // G, n]
+            if sk == 0:
+                assert codes[n, k] == 7
+                continue
+            x = float(wt[n, k]) / float(sk)
+            best, bd = 0, abs(x - book[0])
+            for c in range(1, 16):                          # first strict minimum: lower index on ties
+                if abs(x - book[c]) < bd:
+                    best, bd = c, abs(x - book[c])
+            assert codes[n, k] == best
+    grp = np.abs(wt).reshape(16, -1, G)
+    hit = np.take_along_axis(codes.reshape(16, -1, G), grp.argmax(axis=2)[..., None], axis=2)[..., 0]
+    assert np.all(np.isin(hit[s.T > 0], (0, 15)))           # each group's absmax lands on -1 or +1
+    gap = np.max(np.diff(book))
+    err = np.abs(wt - reference.dequant_nf4(codes, sbits, G, book_bits))
+    assert np.all(err <= np.repeat(s.T, G, axis=1) * gap / 2 * (1 + 1e-6) + 1e-12)
+    # ties go to the lower index: a value exactly between two entries
+    w2 = np.zeros((1, 64), np.float32)
+    w2[0, 0] = 1.0
+    w2[0, 1] = np.float32((book[7] + book[8]) / 2)
+    c2, _, _ = quant.quantize_nf4(w2, 64)
+    if float(w2[0, 1]) == (book[7] + book[8]) / 2:
+        assert c2[0, 1] == 7
