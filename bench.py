@@ -42,6 +42,8 @@ def weight_bytes(fmt, N, K, G):
         return N * K // 2 + (K // G) * N * 2
     if fmt == "int2":
         return N * K // 4 + (K // G) * N * 2
+    if fmt == "nf4":                     # + the 256-byte code-book header of the scales
+        return N * K // 2 + (K // G) * N * 2 + 256
     if fmt in ("fp8", "fp8h"):
         return N * K
     return N * K // 2 + N * K // 16
@@ -53,9 +55,9 @@ class Gemm:
     def __init__(self, q, torch, fmt, M, N, K, G, key, min_rotate_bytes, with_bias=False):
         import synthetic
         self.fmt, self.M, self.N, self.K, self.G = fmt, M, N, K, G
-        self.p = q.problem(M, N, K, fmt, group_size=G if fmt in ("int4", "int2") else None)
-        pq = q.problem(1, N, K, fmt, group_size=G if fmt in ("int4", "int2") else None)
-        w = synthetic.weights(N, K, {"int4": 0.02, "int2": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}[fmt], key)
+        self.p = q.problem(M, N, K, fmt, group_size=G if fmt in q.GROUP_SCALED else None)
+        pq = q.problem(1, N, K, fmt, group_size=G if fmt in q.GROUP_SCALED else None)
+        w = synthetic.weights(N, K, 0.05 if fmt in ("fp8", "fp8h") else 0.02, key)
         codes, scales, alpha = q.quantize(pq, w)            # the library's own quantizer
         wpk, spk = q.pack(pq, codes, scales)
         self.wbytes = weight_bytes(fmt, N, K, G)
@@ -66,7 +68,7 @@ class Gemm:
         self.w = [w0] + [w0.clone() for _ in range(ncopies - 1)]
         self.s = [s0] + [None if s0 is None else s0.clone() for _ in range(ncopies - 1)]
         self.alpha = torch.tensor([alpha], dtype=torch.float32, device="cuda")
-        kind = "f16" if fmt in ("int4", "int2", "fp8h") else "bf16"
+        kind = "f16" if fmt in ("int4", "int2", "nf4", "fp8h") else "bf16"
         self.A = synthetic.activations(M, K, kind, key).cuda()
         odt = torch.float16 if kind == "f16" else torch.bfloat16
         self.out = torch.empty((M, N), dtype=odt, device="cuda")
@@ -78,7 +80,7 @@ class Gemm:
     def launch(self):
         c = self.i % len(self.w)
         self.i += 1
-        self.q.run(self.p, self.A, self.w[c], self.s[c], None if self.fmt in ("int4", "int2") else self.alpha,
+        self.q.run(self.p, self.A, self.w[c], self.s[c], None if self.fmt in self.q.GROUP_SCALED else self.alpha,
                    self.out, self.ws, bias=self.bias)
 
     @property
@@ -303,7 +305,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.all:
-        for name in ("fp8", "fp4", "fp8h", "int2"):
+        for name in ("fp8", "fp4", "fp8h", "int2", "nf4"):
             wk = synthetic.WORKLOADS[name]
             wix = synthetic.WORKLOAD_INDEX[name]
             for si, (M, N, K) in enumerate(wk["shapes"]):

@@ -22,6 +22,10 @@
  *   F16      INT2           GROUP_F16 (G=32..256) F16 or F32    Bitblas lecture 033, exercises
  *                                                               (the W2A16 combination), with
  *                                                               the INT4 recipe at 2 bits
+ *   F16      NF4            GROUP_F16_LUT16       F16 or F32    Low Bit Triton Kernels (GPU MODE
+ *                           (G=32..256)                         lecture 034), 4-bit value choice:
+ *                                                               a non-uniform 16-value grid read
+ *                                                               through a register table
  *
  * Value semantics (what the kernels compute):
  *   INT4 : w[k][n] = RNE_fp16((nibble - 8) * s[k / G][n]) -- the 16-bit operand the
@@ -32,6 +36,9 @@
  *   FP4  : w = e2m1(code) * e4m3(s_b) (exact in bf16) with one scale per 16 consecutive
  *          K of a column; alpha multiplies the fp32 accumulator in the epilogue.
  *   INT2 : w[k][n] = (code - 2) * s[k / G][n] (exact in fp16), accumulated in fp32.
+ *   NF4  : w[k][n] = RNE_fp16(T[code] * s[k / G][n]) with T the 16-entry fp16 code book
+ *          that travels with the scales (qgemm_quantize writes the NormalFloat-4 book),
+ *          accumulated in fp32.  No alpha.
  *   Bias (qgemm_run_bias): bias[n] is added in fp32 after alpha.
  *   The 16-bit output is the round-to-nearest-even cast of the fp32 result, so a call
  *   with out_dtype F32 yields exactly the values a 16-bit call rounds.
@@ -68,13 +75,15 @@ typedef enum qgemm_dtype {
   QGEMM_DT_INT4 = 3,
   QGEMM_DT_FP8_E4M3 = 4,   /* OCP e4m3 ("fn"): max 448, code S.1111.111 is NaN        */
   QGEMM_DT_FP4_E2M1 = 5,   /* e2m1: +-{0, .5, 1, 1.5, 2, 3, 4, 6}                      */
-  QGEMM_DT_INT2 = 6        /* signed 2-bit integer in [-2, 1], stored + 2               */
+  QGEMM_DT_INT2 = 6,       /* signed 2-bit integer in [-2, 1], stored + 2               */
+  QGEMM_DT_NF4 = 7         /* 4-bit index into a 16-entry fp16 code book                */
 } qgemm_dtype_t;
 
 typedef enum qgemm_scale_layout {
   QGEMM_SCALE_GROUP_F16 = 0,     /* INT4: fp16 scale per (group of G consecutive K, column) */
   QGEMM_SCALE_TENSOR_F32 = 1,    /* FP8 : no weight scales; one fp32 alpha (device pointer) */
-  QGEMM_SCALE_BLOCK16_E4M3 = 2   /* FP4 : e4m3 scale per (16 consecutive K, column) + alpha */
+  QGEMM_SCALE_BLOCK16_E4M3 = 2,  /* FP4 : e4m3 scale per (16 consecutive K, column) + alpha */
+  QGEMM_SCALE_GROUP_F16_LUT16 = 3 /* NF4: 16 fp16 code-book entries, then GROUP_F16 scales   */
 } qgemm_scale_layout_t;
 
 /* kernel_hint values (testing and tuning; 0 is the right choice for applications) */
@@ -89,7 +98,7 @@ typedef enum qgemm_scale_layout {
  *   M >= 0 (any value; M = 0 is an empty product: qgemm_run validates the descriptor and
  *   enqueues nothing, ignoring the pointers); N % 16 == 0; K % 128 == 0; for INT4 also
  *   K % group_size == 0.  Each of M, N, K is at most 2^24.
- *   group_size: INT4 and INT2, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
+ *   group_size: INT4, INT2 and NF4, one of 32, 64, 128, 256; FP4 requires 16; FP8 requires 0.
  *   FP8 weights take a_dtype BF16 (mm_bf16_fp8) or F16 (mm_fp16_fp8); the packed weights
  *   are the same for both.
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
@@ -122,12 +131,19 @@ typedef struct qgemm_problem {
  *   INT2: codes_canonical uint8[N][K/4], byte j of row n = code(4j) | code(4j+1) << 2 |
  *         code(4j+2) << 4 | code(4j+3) << 6, code = clamp(rint(w / s), -2, 1) + 2; scales
  *         as INT4 with s = RNE_fp16(absmax_group / 1) (the INT4 recipe at 2 bits).
+ *   NF4 : codes uint8[N][K/2] (nibble order as INT4) = the index c of the code-book entry
+ *         nearest to w / s (ties to the lower index; c = 7, the entry 0, when s = 0);
+ *         scales_canonical fp16 [16 + (K/G) N]: first the code book T[0..15], the
+ *         NormalFloat-4 values (QLoRA's construction: the 8 positive and 7 negative
+ *         quantiles of N(0,1) at evenly spaced probabilities from 1/2 to
+ *         delta = ((1 - 1/30) + (1 - 1/32)) / 2, plus 0, divided by the largest; rounded
+ *         to fp16), then [K/G][N] scales s = RNE_fp16(absmax_group).
  *   FP4 : codes uint8[N][K/2] (nibble order as INT4) = e2m1(clamp(w / (s_b alpha), +-6)),
  *         scales_canonical e4m3 uint8[N][K/16] = e4m3(min(absmax_b / (6 alpha), 448)),
  *         alpha = absmax / (6 * 448) (fp32).
  * Rounding is round-half-even; divisions are done in double and rounded once.  An
- * all-zero group / block / tensor gets scale 0 and signed code 0.  alpha_out receives
- * alpha (FP8, FP4) or 1.0 (INT4); it may be NULL for INT4.
+ * all-zero group / block / tensor gets scale 0 and signed code 0 (NF4: code 7).  alpha_out
+ * receives alpha (FP8, FP4) or 1.0 (INT4, INT2, NF4); it may be NULL for those three.
  */
 qgemm_status_t qgemm_quantize(const qgemm_problem_t* problem, const float* w_nk,
                               void* codes_canonical, void* scales_canonical, float* alpha_out);
@@ -143,6 +159,8 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* problem, const float* w_nk,
  *     index nb*(K/128) + kb; dword t (0..3) of lane l holds column 16nb + (l & 15) at
  *     k = 128kb + 32t + 8(l >> 4) + J[s] in nibble s (bits 4s..4s+3), with
  *     J = (0,2,4,6,1,3,5,7) for INT4 and J = (0,1,...,7) for FP4.
+ *   NF4 weights: as INT4 with J = (0,4,1,5,2,6,3,7) (byte b of a dword holds k offsets b
+ *     and b + 4, the order of the byte-table lookup).
  *   INT2 weights: block (nb, kb) = 16 columns x 128 k = 512 bytes, index nb*(K/128) + kb;
  *     lane l owns bytes [8 l, 8 l + 8); bits 16h + 8b + 2f (h, b = 0..1, f = 0..3) of its
  *     dword d hold column 16nb + (l & 15), k = 128kb + 32(2d + b) + 8(l >> 4) + 2f + h.
@@ -150,6 +168,9 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* problem, const float* w_nk,
  *     (t = 0..1, j = 0..7) of lane l is column 16nb + (l & 15), k = 64kb + 32t + 8(l>>4) + j.
  *   INT4 and INT2 scales (fp16): span = max(G, 128), T = max(1, 128/G); element
  *     ((nb*(K/span) + kb)*16 + c)*T + t = scale of column 16nb + c, group kb*(span/G) + t.
+ *   NF4 scales: a 256-byte header, then the INT4 scale layout.  Header dword q (0..3) holds
+ *     the low bytes of T[4q..4q+3] (T[4q] in bits 0..7), dword 4 + q their high bytes; the
+ *     rest of the header is zero.
  *   FP4 scales (e4m3): byte ((nb*(K/128) + kb)*16 + c)*8 + 4h + t = scale of column
  *     16nb + c, 16-k block 8kb + 2t + h.
  * Size query: pass w_packed == NULL and/or s_packed == NULL to receive the sizes only.
@@ -175,8 +196,9 @@ qgemm_status_t qgemm_workspace_bytes(const qgemm_problem_t* problem, size_t* byt
  * qgemm_run -- enqueue out = A . dequant(W) (* alpha) on `stream`.
  *   A        device, row-major [M][K] of a_dtype, 16-byte aligned.
  *   w_packed device, qgemm_pack output, 16-byte aligned.
- *   s_packed device, qgemm_pack scale output (INT4, FP4; NULL for FP8), 16-byte aligned.
- *   alpha    device pointer to one fp32 (FP8, FP4; NULL for INT4); 4-byte alignment only
+ *   s_packed device, qgemm_pack scale output (INT4, INT2, NF4, FP4; NULL for FP8),
+ *            16-byte aligned.
+ *   alpha    device pointer to one fp32 (FP8, FP4; NULL for INT4, INT2, NF4); 4-byte alignment only
  *            (FlashInfer PR #7495 analysis, section 3(a): scalar pointers must not be
  *            assumed 16-byte aligned).
  *   out      device, row-major [M][N] of out_dtype, 16-byte aligned.

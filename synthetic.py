@@ -5,9 +5,9 @@ casts activations to their 16-bit type with torch's own cast.  Quantization, pac
 the GEMM live in the library (GPU path) and, independently, in the oracle.
 
 Workloads (LLM linear layers; no dataset or trained weights are involved):
-  A ~ N(0, 1) cast to fp16 (INT4 and INT2 shapes, FP8 with fp16 activations) or bf16
+  A ~ N(0, 1) cast to fp16 (INT4, INT2 and NF4 shapes, FP8 with fp16 activations) or bf16
   (FP8 / FP4 shapes);
-  W ~ N(0, sigma) in fp32, sigma = 0.02 (INT4, INT2, FP4) or 0.05 (FP8), drawn in the
+  W ~ N(0, sigma) in fp32, sigma = 0.02 (INT4, INT2, NF4, FP4) or 0.05 (FP8), drawn in the
   "nt" orientation [N, K] (row n = output column n).
   a bias (the bias argument of mm_bf16_fp8 / mm_fp16_fp8) ~ N(0, 0.1) per output column,
   cast to the output's 16-bit type.
@@ -36,6 +36,9 @@ WORKLOADS = {
     # W2A16: the INT4 decode and prefill layer shapes with 2-bit weights
     "int2": dict(fmt="int2", shapes=[(1, 4096, 4096), (16, 4096, 4096), (4096, 4096, 4096)],
                  group_sizes=[128], sigma=0.02),
+    # NF4 (4-bit code-book index): the same shapes, so its table lookup is priced against INT4
+    "nf4": dict(fmt="nf4", shapes=[(1, 4096, 4096), (16, 4096, 4096), (4096, 4096, 4096)],
+                group_sizes=[128], sigma=0.02),
 }
 WORKLOAD_INDEX = {name: i for i, name in enumerate(WORKLOADS)}
 

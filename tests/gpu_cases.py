@@ -8,8 +8,9 @@ import numpy as np
 import synthetic
 from oracle import codecs, quant, reference, tolerance
 
-FMT_ACT = {"int4": "f16", "int2": "f16", "fp8": "bf16", "fp8h": "f16", "fp4": "bf16"}
-SIGMA = {"int4": 0.02, "int2": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}
+FMT_ACT = {"int4": "f16", "int2": "f16", "nf4": "f16", "fp8": "bf16", "fp8h": "f16", "fp4": "bf16"}
+SIGMA = {"int4": 0.02, "int2": 0.02, "nf4": 0.02, "fp8": 0.05, "fp8h": 0.05, "fp4": 0.02}
+GROUPED = ("int4", "int2", "nf4")        # formats with a group size (fp16 group scales, no alpha)
 
 
 def say(msg):
@@ -27,6 +28,10 @@ def oracle_weights(fmt, N, K, G, key):
     if fmt == "int2":
         codes, sbits = quant.quantize_int2(w, G)
         return quant.pack_crumbs(codes), sbits, 1.0, reference.dequant_int2(codes, sbits, G)
+    if fmt == "nf4":                     # canonical scales: the code book, then [K/G][N]
+        codes, sbits, book = quant.quantize_nf4(w, G)
+        return (quant.pack_nibbles(codes), np.concatenate([book, sbits.reshape(-1)]), 1.0,
+                reference.dequant_nf4(codes, sbits, G, book))
     if fmt in ("fp8", "fp8h"):           # one quantization for both activation types
         codes, alpha = quant.quantize_fp8(w)
         return codes, None, alpha, reference.dequant_fp8(codes)
@@ -48,7 +53,7 @@ class Prepared:
         self.fmt, self.N, self.K, self.G = fmt, N, K, G
         canon, scales, alpha, self.wdq = oracle_weights(fmt, N, K, G, key)
         self.alpha = alpha if alpha_override is None else alpha_override
-        p = q.problem(1, N, K, fmt, group_size=G if fmt in ("int4", "int2") else None)
+        p = q.problem(1, N, K, fmt, group_size=G if fmt in GROUPED else None)
         wpk, spk = q.pack(p, canon, scales)
         self.w = torch.from_numpy(wpk).cuda()
         self.s = None if spk is None else torch.from_numpy(spk).cuda()
@@ -62,7 +67,7 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     an exact widening), through qgemm_run_bias."""
     import torch
     M, K = A16.shape
-    p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt in ("int4", "int2") else None,
+    p = q.problem(M, prep.N, prep.K, prep.fmt, group_size=prep.G if prep.fmt in GROUPED else None,
                   out_dtype=out_dtype, kernel_hint=kernel_hint, split_k_hint=split_k_hint,
                   tile_hint=tile_hint)
     tdt = {q.DT_F32: torch.float32, q.DT_F16: torch.float16, q.DT_BF16: torch.bfloat16}[out_dtype]
@@ -71,7 +76,7 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     if workspace is None:
         workspace = q.alloc_workspace(p)
     b = None if bias is None else bias.to(tdt).cuda()
-    q.run(p, A, prep.w, prep.s, None if prep.fmt in ("int4", "int2") else prep.alpha_t, out, workspace, bias=b)
+    q.run(p, A, prep.w, prep.s, None if prep.fmt in GROUPED else prep.alpha_t, out, workspace, bias=b)
     torch.cuda.synchronize()
     o = out.cpu()
     if out_dtype == q.DT_F32:
@@ -85,7 +90,7 @@ def ref_rows(prep, A16, rows, bias=None):
 
 
 def out16_kind(fmt):
-    return "f16" if fmt in ("int4", "int2", "fp8h") else "bf16"
+    return "f16" if fmt in ("int4", "int2", "nf4", "fp8h") else "bf16"
 
 
 def out16_dtype(q, fmt):

@@ -49,6 +49,9 @@ BAD = [
     (dict(M=1, N=256, K=512, fmt="int4", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "INT4 weights need"),
     (dict(M=1, N=256, K=512, fmt="int2", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "INT2 weights need"),
     (dict(M=1, N=256, K=512, fmt="int2", group_size=16), q.ERR_UNSUPPORTED, "INT2 group_size"),
+    (dict(M=1, N=256, K=512, fmt="nf4", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "NF4 weights need"),
+    (dict(M=1, N=256, K=512, fmt="nf4", group_size=16), q.ERR_UNSUPPORTED, "NF4 group_size"),
+    (dict(M=1, N=256, K=640, fmt="nf4", group_size=256), q.ERR_INVALID_ARGUMENT, "multiple of group_size"),
     (dict(M=1, N=256, K=512, fmt="fp8", out_dtype=q.DT_F16), q.ERR_UNSUPPORTED, "FP8_E4M3 weights need"),
     (dict(M=1, N=256, K=512, fmt="fp8h", out_dtype=q.DT_BF16), q.ERR_UNSUPPORTED, "FP8_E4M3 weights need"),
     (dict(M=1, N=256, K=512, fmt="fp8", group_size=128), q.ERR_INVALID_ARGUMENT, "group_size 0"),
@@ -72,7 +75,7 @@ def test_validation_errors(kw, status, text):
 def test_empty_product_needs_nothing_and_launches_nothing():
     # M = 0: no workspace; qgemm_run validates the descriptor and returns without touching
     # (or checking) any pointer, so it needs no GPU.
-    for fmt in ("int4", "int2", "fp8", "fp8h", "fp4"):
+    for fmt in ("int4", "int2", "nf4", "fp8", "fp8h", "fp4"):
         p = q.problem(0, 256, 512, fmt)
         assert q.workspace_bytes(p) == 0
         assert q.run_raw(p, None, None, None, None, None, None, 0, None) == q.OK
@@ -116,7 +119,7 @@ def test_null_and_misaligned_pointers_fail_before_launch():
 def test_bias_needs_16_byte_alignment():
     # the FlashInfer fix (PR #7495 analysis, section 3(a)): a bias is 16-byte aligned, the
     # scalar alpha only 4; a misaligned bias fails before anything is enqueued
-    for fmt in ("int4", "int2", "fp8", "fp8h", "fp4"):
+    for fmt in ("int4", "int2", "nf4", "fp8", "fp8h", "fp4"):
         p = q.problem(1, 256, 512, fmt)
         st = q.run_bias_raw(p, 0x1000, 0x2000, 0x3000, 0x4004, 0x6008, 0x5000, None, 0, None)
         assert st == q.ERR_MISALIGNED and "bias must be 16-byte aligned" in q.last_error()
@@ -164,3 +167,20 @@ def test_pack_size_query():
     assert q.packed_sizes(q.problem(1, 256, 512, "fp8")) == (256 * 512, 0)
     assert q.packed_sizes(q.problem(1, 256, 512, "fp4")) == (256 * 256, 256 * 32)
     assert q.packed_sizes(q.problem(1, 256, 512, "int2")) == (256 * 128, 256 * 4 * 2)
+    assert q.packed_sizes(q.problem(1, 256, 512, "nf4", group_size=64)) == (256 * 256, 256 + 256 * 8 * 2)
+
+
+def test_nf4_needs_its_scale_layout():
+    # NF4 scales carry the code book: the plain group layout is refused, and INT4 does not
+    # take the code-book layout
+    p = q.problem(1, 256, 512, "nf4")
+    p.scale_layout = q.SCALE_GROUP_F16
+    assert _valid_run_status(p) == q.ERR_UNSUPPORTED and "GROUP_F16_LUT16" in q.last_error()
+    p = q.problem(1, 256, 512, "int4")
+    p.scale_layout = q.SCALE_GROUP_F16_LUT16
+    assert _valid_run_status(p) == q.ERR_UNSUPPORTED
+    p = q.problem(1, 256, 512, "nf4")
+    assert _valid_run_status(p, S=None) == q.ERR_INVALID_ARGUMENT
+    assert _valid_run_status(p, S=0x3008) == q.ERR_MISALIGNED
+    p.scale_layout = 4
+    assert _valid_run_status(p) == q.ERR_INVALID_ARGUMENT

@@ -25,7 +25,7 @@ def q():
 
 def _g(fmt):
     """Group size of the format in the generic cases (128 for the integer formats)."""
-    return 128 if fmt in ("int4", "int2") else 0
+    return 128 if fmt in ("int4", "int2", "nf4") else 0
 
 
 def _act(fmt, M, K, key):
@@ -44,15 +44,19 @@ def _identity_rows(fmt, rows, K):
 def _dequant_16bit_values(fmt, prep):
     """The 16-bit operand the method feeds the MFMA, [N, K] float64."""
     canon, scales, _, wdq = oracle_weights(fmt, prep.N, prep.K, prep.G, (7, prep.N, prep.K))
+    from oracle import quant
     if fmt == "int4":
-        from oracle import quant
         return reference.dequant_int4_f16(quant.unpack_nibbles(canon), scales, prep.G)
+    if fmt == "nf4":                                     # RNE_fp16(T[code] s)
+        return reference.dequant_nf4_f16(quant.unpack_nibbles(canon), scales[16:].reshape(-1, prep.N),
+                                         prep.G, scales[:16])
     # INT2: (code - 2) s is exact in fp16; FP8 (alpha not applied), FP4: exact in 16 bits
     return wdq.astype(np.float64)
 
 
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 64), ("int4", 128), ("int4", 256),
                                    ("int2", 32), ("int2", 64), ("int2", 128), ("int2", 256),
+                                   ("nf4", 32), ("nf4", 64), ("nf4", 128), ("nf4", 256),
                                    ("fp8", None), ("fp8h", None), ("fp4", None)])
 @pytest.mark.parametrize("hint,step", [(1, 16), (1, 4), (1, 1), (2, None)],
                          ids=["decode-M16", "decode-M4", "decode-M1", "prefill"])
@@ -99,6 +103,9 @@ CONFIGS = [
     ("int2", 0, (1, 4096, 4096), 128, None),
     ("int2", 1, (16, 4096, 4096), 128, None),
     ("int2", 2, (4096, 4096, 4096), 128, 96),
+    ("nf4", 0, (1, 4096, 4096), 128, None),
+    ("nf4", 1, (16, 4096, 4096), 128, None),
+    ("nf4", 2, (4096, 4096, 4096), 128, 96),
     ("fp4", 0, (1, 8192, 8192), None, None),
     ("fp4", 1, (128, 8192, 8192), None, None),
     ("fp4", 2, (8192, 8192, 8192), None, 64),
@@ -125,7 +132,7 @@ def test_workload_parity(q, name, si, shape, G, nrows):
 
 
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int4", 256), ("int2", 64), ("int2", 256),
-                                   ("fp8", None), ("fp8h", None), ("fp4", None)])
+                                   ("nf4", 32), ("nf4", 256), ("fp8", None), ("fp8h", None), ("fp4", None)])
 @pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 33, 127, 128, 129])
 def test_m_sweep_ragged(q, fmt, G, M):
     N, K = 272, 768          # N: 17 column blocks (ragged against 128-wide tiles); K: 6 k blocks
@@ -135,7 +142,7 @@ def test_m_sweep_ragged(q, fmt, G, M):
     check_against_oracle(q, prep, A)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "nf4", "fp8", "fp4"])
 @pytest.mark.parametrize("M,hint,split,tile", [(16, 1, 2, 0), (16, 1, 3, 1), (16, 1, 7, 2), (16, 1, 14, 4),
                                                (4, 1, 1, 4), (4, 1, 5, 1), (16, 1, 1, 3), (16, 1, 4, 3),
                                                (3, 1, 2, 3), (16, 2, 1, 0), (16, 2, 2, 0),
@@ -148,7 +155,7 @@ def test_split_k_and_kernel_hints(q, fmt, M, hint, split, tile):
     check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, tile_hint=tile)
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 64), ("int2", 128), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("fmt,G", [("int4", 64), ("int2", 128), ("nf4", 32), ("fp8", None), ("fp4", None)])
 @pytest.mark.parametrize("M,N,K", [(1, 256, 128 * 44), (3, 512, 128 * 60), (16, 256, 128 * 60), (16, 8192, 128 * 44),
                                    (9, 4352, 128 * 23)])
 def test_decode_multi_run(q, fmt, G, M, N, K):
@@ -160,7 +167,8 @@ def test_decode_multi_run(q, fmt, G, M, N, K):
     check_against_oracle(q, prep, A)
 
 
-@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int2", 32), ("fp8", None), ("fp4", None)])
+@pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int2", 32), ("nf4", 64), ("fp8", None),
+                                   ("fp4", None)])
 @pytest.mark.parametrize("tile,split", [(128, 1), (128, 3), (256, 1), (256, 3)])
 def test_prefill_tile_shapes(q, fmt, G, tile, split):
     # Both prefill workgroup shapes on every format: 600 rows are ragged against 128- and
@@ -172,7 +180,7 @@ def test_prefill_tile_shapes(q, fmt, G, tile, split):
     check_against_oracle(q, prep, A, kernel_hint=2, split_k_hint=split, tile_hint=tile)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "nf4", "fp8", "fp4"])
 @pytest.mark.parametrize("M", [16, 256])
 def test_deterministic_and_counters_reset(q, fmt, M):
     N, K = 512, 4096
@@ -192,7 +200,7 @@ def test_deterministic_and_counters_reset(q, fmt, M):
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "nf4", "fp8", "fp4"])
 def test_minimum_shape_and_zero_weights(q, fmt):
     import torch as T
     N, K = 16, 128
@@ -231,7 +239,7 @@ def test_int4_closed_form_equal_nibbles_unit_scales(q):
             tolerance.check_e1_e2(y, want)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "nf4", "fp8", "fp4"])
 def test_empty_m_enqueues_nothing(q, fmt):
     # M = 0 is an empty product: the call succeeds and writes nothing (the output buffer
     # handed over here has a row of sentinels that must survive).
@@ -242,7 +250,7 @@ def test_empty_m_enqueues_nothing(q, fmt):
     A = torch.zeros((1, K), dtype=dt, device="cuda")
     out = torch.full((1, N), 7.0, dtype=dt, device="cuda")
     p = q.problem(0, N, K, fmt, group_size=_g(fmt) or None)
-    q.run(p, A, prep.w, prep.s, None if fmt in ("int4", "int2") else prep.alpha_t, out)
+    q.run(p, A, prep.w, prep.s, None if fmt in ("int4", "int2", "nf4") else prep.alpha_t, out)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
 
@@ -259,7 +267,7 @@ def test_long_k(q, fmt, G, M, N, K):
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int2", "fp8", "fp8h", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int2", "nf4", "fp8", "fp8h", "fp4"])
 @pytest.mark.parametrize("M,hint,split", [(1, 0, 0), (16, 0, 3), (33, 0, 0), (300, 2, 2)])
 def test_bias_epilogue(q, fmt, M, hint, split):
     # qgemm_run_bias: out = A . dequant(W) (* alpha) + bias[n], the bias added in fp32 after
@@ -295,3 +303,32 @@ def test_bias_null_is_plain_run_bitwise(q):
     assert st == q.OK, q.last_error()
     T.cuda.synchronize()
     assert T.equal(o1, o2)
+
+
+@pytest.mark.parametrize("hint,M", [(1, 1), (1, 4), (1, 16), (2, 64)])
+def test_nf4_any_code_book_bit_exact(q, hint, M):
+    # The kernels read the code book from the packed scales: with a random book (every entry
+    # its own sign and magnitude), random codes and random scales, identity activations must
+    # return RNE_fp16(T[code] * s) exactly for every code in every nibble slot.
+    import torch as T
+    from oracle import quant
+    N, K, G = 64, 512, 64
+    say(f"case nf4-any-book hint={hint} M={M}")
+    g = np.random.default_rng([59, hint, M])
+    mag = np.exp2(g.uniform(-4, 2, 16))
+    book = codecs.f16_bits(codecs.f16_round(mag * g.choice([-1.0, 1.0], 16)))
+    codes = g.integers(0, 16, (N, K)).astype(np.uint8)
+    sbits = codecs.f16_bits(codecs.f16_round(np.exp2(g.uniform(-8, 1, (K // G, N)))))
+    p = q.problem(M, N, K, "nf4", group_size=G, out_dtype=q.DT_F32, kernel_hint=hint)
+    wpk, spk = q.pack(p, quant.pack_nibbles(codes), np.concatenate([book, sbits.reshape(-1)]))
+    want = reference.dequant_nf4_f16(codes, sbits, G, book)          # [N, K]
+    w_d, s_d = T.from_numpy(wpk).cuda(), T.from_numpy(spk).cuda()
+    ws = q.alloc_workspace(p)
+    for k0 in range(0, K, M):
+        rows = list(range(k0, min(k0 + M, K)))
+        A = _identity_rows("nf4", rows, K)
+        pr = q.problem(len(rows), N, K, "nf4", group_size=G, out_dtype=q.DT_F32, kernel_hint=hint)
+        out = T.full((len(rows), N), float("nan"), dtype=T.float32, device="cuda")
+        q.run(pr, A.cuda(), w_d, s_d, None, out, ws)
+        T.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), want[:, rows].T), f"rows {k0}.."

@@ -110,3 +110,36 @@ def test_int2_pack_every_code_position():
     wpk, _ = q.pack(q.problem(1, N, K, "int2"), quant.pack_crumbs(codes), sb)
     assert np.array_equal(wpk, layout.device_int2_weights(codes))
     assert np.array_equal(layout.device_int2_weights_inverse(wpk, N, K), codes)
+
+
+@pytest.mark.parametrize("N,K,G", [(16, 128, 32), (16, 128, 128), (16, 256, 256), (48, 384, 64),
+                                   (256, 512, 128), (64, 1024, 32)])
+def test_nf4_quantize_and_pack_match_oracle(N, K, G):
+    w = _w(N, K, 0.02, 11 * N + K + G)
+    w[2, G:2 * G] = 0.0                                 # an all-zero group
+    p = q.problem(1, N, K, "nf4", group_size=G)
+    codes_b, scales_b, alpha = q.quantize(p, w)
+    codes_o, sbits_o, book_o = quant.quantize_nf4(w, G)
+    assert alpha == 1.0
+    # the library derives the code book on its own (bisection on erfc); the oracle uses scipy
+    assert np.array_equal(scales_b[:16], book_o)
+    assert np.array_equal(scales_b[16:].reshape(K // G, N), sbits_o)
+    assert np.array_equal(codes_b, quant.pack_nibbles(codes_o))
+    wpk, spk = q.pack(p, codes_b, scales_b)
+    assert wpk.size == N * K // 2 and spk.size == 256 + 2 * (K // G) * N
+    assert np.array_equal(wpk, layout.device_nf4_weights(codes_o))
+    assert np.array_equal(spk, layout.device_nf4_scales(book_o, sbits_o, N, K, G))
+
+
+def test_nf4_pack_every_code_and_any_book():
+    # every code at every position, and a code book that is not NF4's: the packer copies the
+    # caller's book into the header unchanged
+    N, K, G = 64, 512, 128
+    codes = np.random.default_rng(10).integers(0, 16, (N, K)).astype(np.uint8)
+    book = np.random.default_rng(12).integers(0, 0x7C00, 16).astype(np.uint16)
+    sb = np.full((K // G, N), 0x3C00, np.uint16)
+    scales = np.concatenate([book, sb.reshape(-1)])
+    wpk, spk = q.pack(q.problem(1, N, K, "nf4"), quant.pack_nibbles(codes), scales)
+    assert np.array_equal(wpk, layout.device_nf4_weights(codes))
+    assert np.array_equal(layout.device_nf4_weights_inverse(wpk, N, K), codes)
+    assert np.array_equal(spk, layout.device_nf4_scales(book, sb, N, K, G))

@@ -31,8 +31,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # ----------------------------------------------------------------------------- enums
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(6)
-DT_F16, DT_BF16, DT_F32, DT_INT4, DT_FP8_E4M3, DT_FP4_E2M1, DT_INT2 = range(7)
-SCALE_GROUP_F16, SCALE_TENSOR_F32, SCALE_BLOCK16_E4M3 = range(3)
+DT_F16, DT_BF16, DT_F32, DT_INT4, DT_FP8_E4M3, DT_FP4_E2M1, DT_INT2, DT_NF4 = range(8)
+SCALE_GROUP_F16, SCALE_TENSOR_F32, SCALE_BLOCK16_E4M3, SCALE_GROUP_F16_LUT16 = range(4)
 KERNEL_AUTO, KERNEL_DECODE, KERNEL_PREFILL = range(3)
 
 
@@ -84,16 +84,18 @@ _FORMATS = {
     "fp8h": (DT_F16, DT_FP8_E4M3, SCALE_TENSOR_F32, DT_F16),      # FP8 weights, fp16 activations
     "fp4": (DT_BF16, DT_FP4_E2M1, SCALE_BLOCK16_E4M3, DT_BF16),
     "int2": (DT_F16, DT_INT2, SCALE_GROUP_F16, DT_F16),             # W2A16
+    "nf4": (DT_F16, DT_NF4, SCALE_GROUP_F16_LUT16, DT_F16),         # 4-bit code-book index
 }
+GROUP_SCALED = ("int4", "int2", "nf4")
 
 
 def problem(M, N, K, fmt, group_size=None, out_dtype=None, kernel_hint=KERNEL_AUTO, split_k_hint=0,
             tile_hint=0):
-    """Problem descriptor for one of the formats 'int4', 'int2', 'fp8' (bf16 activations),
-    'fp8h' (fp16 activations), 'fp4'."""
+    """Problem descriptor for one of the formats 'int4', 'int2', 'nf4', 'fp8' (bf16
+    activations), 'fp8h' (fp16 activations), 'fp4'."""
     a, w, sl, o = _FORMATS[fmt]
     if group_size is None:
-        group_size = {"int4": 128, "int2": 128, "fp8": 0, "fp8h": 0, "fp4": 16}[fmt]
+        group_size = {"int4": 128, "int2": 128, "nf4": 128, "fp8": 0, "fp8h": 0, "fp4": 16}[fmt]
     if out_dtype is not None:
         o = out_dtype
     return Problem(M, N, K, a, w, o, group_size, sl, kernel_hint, split_k_hint, tile_hint)
@@ -102,7 +104,7 @@ def problem(M, N, K, fmt, group_size=None, out_dtype=None, kernel_hint=KERNEL_AU
 def fmt_of(p):
     if p.w_dtype == DT_FP8_E4M3:
         return "fp8h" if p.a_dtype == DT_F16 else "fp8"
-    return {DT_INT4: "int4", DT_INT2: "int2", DT_FP4_E2M1: "fp4"}[p.w_dtype]
+    return {DT_INT4: "int4", DT_INT2: "int2", DT_NF4: "nf4", DT_FP4_E2M1: "fp4"}[p.w_dtype]
 
 
 def _ptr(x):
@@ -115,7 +117,9 @@ def _ptr(x):
 
 # ----------------------------------------------------------------------------- host calls
 def quantize(p, w_nk):
-    """fp32 [N, K] weights -> (canonical codes uint8, canonical scales or None, alpha)."""
+    """fp32 [N, K] weights -> (canonical codes uint8, canonical scales or None, alpha).
+
+    NF4 scales are one flat fp16 (uint16) array: the 16 code-book entries, then [K/G][N]."""
     w = np.ascontiguousarray(w_nk, dtype=np.float32)
     N, K = int(p.N), int(p.K)
     assert w.shape == (N, K)
@@ -124,6 +128,8 @@ def quantize(p, w_nk):
     scales = None
     if f in ("int4", "int2"):
         scales = np.empty((K // p.group_size, N), np.uint16)
+    elif f == "nf4":
+        scales = np.empty(16 + (K // p.group_size) * N, np.uint16)
     elif f == "fp4":
         scales = np.empty((N, K // 16), np.uint8)
     alpha = ctypes.c_float(0.0)

@@ -1,6 +1,6 @@
 """Builds the HIP library (libqgemm.so) in-tree for gfx950 with hipcc.
 
-Each source compiles to its own object (in parallel), then hipcc links the shared library.
+Each source compiles to its own objects in parallel (the kernel sources once per weight format), then hipcc links the shared library.
 """
 import os
 import subprocess
@@ -11,7 +11,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = ["qgemm_host.cpp", "qgemm_run.hip", "qgemm_decode.hip", "qgemm_prefill.hip"]
+# Weight formats (the Format enum of csrc/qgemm_internal.h).  Each kernel source is compiled
+# once per format (-DQGEMM_FMT_UNIT), so the many kernel instances build in parallel.
+N_FORMATS = 6
+UNITS = ([("qgemm_host.cpp", []), ("qgemm_run.hip", [])]
+         + [(k, [f"-DQGEMM_FMT_UNIT={f}"]) for k in ("qgemm_decode.hip", "qgemm_prefill.hip")
+            for f in range(N_FORMATS)])
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -34,14 +39,16 @@ def build(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     inc = ["-I", os.path.join(ROOT, "include")]
     with tempfile.TemporaryDirectory(prefix="qgemm_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
-        cmds = [[hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-        with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+        objs = [os.path.join(tmpdir, f"{i}_{s}.o") for i, (s, _) in enumerate(UNITS)]
+        cmds = [[hipcc, *HIPCC_FLAGS, *defs, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+                for (s, defs), o in zip(UNITS, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
             results = list(ex.map(_run, cmds))
         msgs = []
-        for s, (rc, lines) in zip(SOURCES, results):
+        for (s, defs), (rc, lines) in zip(UNITS, results):
             if rc != 0:
-                raise RuntimeError(f"hipcc failed on {s}:\n" + "\n".join(lines))
+                raise RuntimeError(f"hipcc failed on {s} {' '.join(defs)}:\n" + "\n".join(lines))
             msgs += lines
         tmp = LIB + ".tmp"
         rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])

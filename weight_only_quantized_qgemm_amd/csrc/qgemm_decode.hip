@@ -59,6 +59,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   // LDS (layout shared with the launch plan): one private region per wavefront ([its A share:
   // M rows of share x 128 + 8 halves][its scales: CB x SW bytes]), then the wave tiles of the
   // final reduction.
+  Lut lut;                                           // NF4 code book (wavefront-uniform)
+  load_lut<FMT>(a, lut);
   const int ldw = share * 128 + 8;                   // LDS A row stride (halves)
   const int aw_bytes = qgemm::dec_a_bytes(a.M, share, ASTAGE);
   const int SW = HAS_S ? qgemm::dec_scale_span(FMT, G, share) : 0;   // scale bytes of a share, per column block
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const u32x4 av = al[t];
-            acc[c][DEC_ACC2 ? (t & 1) : 0] = mfma<FMT>(av, bfrag<FMT, G>(wf[u][c], t, fs), acc[c][DEC_ACC2 ? (t & 1) : 0]);
+            acc[c][DEC_ACC2 ? (t & 1) : 0] = mfma<FMT>(av, bfrag<FMT, G>(wf[u][c], t, fs, lut), acc[c][DEC_ACC2 ? (t & 1) : 0]);
           }
         }
       }
@@ -238,13 +240,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
     if (!splitk_finish<1, NT>(a, group, split, CB * 256, active, v)) return;
   }
   if (!active || nb0 + c >= NB) return;
-  const float alpha = qgemm::int_weights(FMT) ? 1.0f : *a.alpha;
+  const float alpha = qgemm::group_scaled(FMT) ? 1.0f : *a.alpha;
   const int n = (nb0 + c) * 16 + (ln & 15);
   const float bv = bias_of(a, n);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * (ln >> 4) + r;
-    if (m < a.M) store_out(a, m, n, qgemm::int_weights(FMT) ? v[0][r] : v[0][r] * alpha, bv);
+    if (m < a.M) store_out(a, m, n, qgemm::group_scaled(FMT) ? v[0][r] : v[0][r] * alpha, bv);
   }
 }
 
@@ -290,37 +292,30 @@ struct DecodeLauncher {
   }
 };
 
-// Instances for every group size the format has (INT4, INT2: 32, 64, 128, 256; FP8 / FP4: none).
-template <template <int, int> class L>
-hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
-  switch (pl.fmt) {
-    case FMT_INT4:
-      switch (group_size) {
-        case 32: return L<FMT_INT4, 32>::run(pl, a, stream);
-        case 64: return L<FMT_INT4, 64>::run(pl, a, stream);
-        case 128: return L<FMT_INT4, 128>::run(pl, a, stream);
-        case 256: return L<FMT_INT4, 256>::run(pl, a, stream);
-        default: return hipErrorInvalidValue;
-      }
-    case FMT_INT2:
-      switch (group_size) {
-        case 32: return L<FMT_INT2, 32>::run(pl, a, stream);
-        case 64: return L<FMT_INT2, 64>::run(pl, a, stream);
-        case 128: return L<FMT_INT2, 128>::run(pl, a, stream);
-        case 256: return L<FMT_INT2, 256>::run(pl, a, stream);
-        default: return hipErrorInvalidValue;
-      }
-    case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);
-    case FMT_FP8H: return L<FMT_FP8H, 0>::run(pl, a, stream);
-    default: return L<FMT_FP4, 0>::run(pl, a, stream);
+}  // namespace
+
+// The instances of one format (QGEMM_FMT_UNIT): every group size it has (INT4, INT2, NF4:
+// 32, 64, 128, 256; FP8 / FP4: none).  The source is compiled once per format, so that the
+// many instances build in parallel; launch_decode dispatches to the format's unit.
+template <int FMT>
+hipError_t launch_decode_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  if constexpr (qgemm::group_scaled(FMT)) {
+    switch (group_size) {
+      case 32: return DecodeLauncher<FMT, 32>::run(pl, a, stream);
+      case 64: return DecodeLauncher<FMT, 64>::run(pl, a, stream);
+      case 128: return DecodeLauncher<FMT, 128>::run(pl, a, stream);
+      case 256: return DecodeLauncher<FMT, 256>::run(pl, a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return DecodeLauncher<FMT, 0>::run(pl, a, stream);
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
-  return by_format<DecodeLauncher>(pl, group_size, a, stream);
-}
+#ifndef QGEMM_FMT_UNIT
+#error "compile once per format with -DQGEMM_FMT_UNIT=<format>"
+#endif
+template hipError_t launch_decode_format<QGEMM_FMT_UNIT>(const Plan&, int, const KArgs&, hipStream_t);
 
 }  // namespace dev
 }  // namespace qgemm

@@ -24,6 +24,11 @@
 //   FP4 : v_cvt_scalef32_pk_f32_fp4 with scale 1.0, times the e4m3 block scale in fp32
 //         (exact), then RNE to bf16 (exact).  The scale operand of the scalef32 converts
 //         only honours its exponent, so it cannot carry an e4m3 block scale.
+//   NF4 : the nibble indexes a 16-entry fp16 code book held in registers as byte tables
+//         (v_perm_b32 looks up four bytes at once), and the entry is multiplied by the fp16
+//         group scale: RNE_fp16(T[code] * s).  Low Bit Triton Kernels (lecture 034) weighs
+//         this against INT4: the table must live in registers and the unpack is about twice
+//         as long.
 //
 // Split-K (when the output tiles alone cannot fill 256 compute units): each K slice writes
 // an fp32 partial tile to the workspace, then takes a ticket; the workgroup that draws the
@@ -54,7 +59,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct KArgs {
   const uint16_t* A;          // [M][K] 16-bit
   const uint8_t* W;           // packed weights
-  const void* S;              // packed scales (INT4: fp16, FP4: e4m3 bytes)
+  const void* S;              // packed scales (INT4 / INT2 / NF4: fp16, FP4: e4m3 bytes)
+  const unsigned* lut;        // NF4: code-book header (low-byte tables, then high-byte tables)
   const float* alpha;         // FP8 / FP4: device scalar
   void* out;                  // [M][N]
   const void* bias;           // [N] of out_dtype, added after alpha; NULL for none
@@ -119,6 +125,55 @@ __device__ __forceinline__ u32x4 dq_int2(unsigned w, int b, unsigned s2) {
                __builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p1) - b1) * s),
                __builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p2) - b2) * s),
                __builtin_bit_cast(unsigned, (__builtin_bit_cast(f16x2, p3) - b3) * s)};
+}
+
+// NF4 code book as byte tables: lo[q] byte j = low byte of T[4q + j], hi[q] the high bytes.
+struct Lut {
+  unsigned lo[4], hi[4];
+};
+template <int FMT>
+__device__ __forceinline__ void load_lut(const KArgs& a, Lut& t) {
+  if constexpr (FMT == qgemm::FMT_NF4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      t.lo[q] = a.lut[q];
+      t.hi[q] = a.lut[4 + q];
+    }
+  }
+}
+
+// Byte j of the result = byte sel_j of the 16-byte table t3:t2:t1:t0 (sel_j in 0..15).
+// v_perm_b32 selects among 8 bytes, so entries 0..7 and 8..15 are looked up separately and
+// bit 3 of each index picks one (hm: 0xFF in the bytes whose index has bit 3 set).
+__device__ __forceinline__ unsigned lut16(unsigned t0, unsigned t1, unsigned t2, unsigned t3, unsigned sel,
+                                          unsigned hm) {
+  const unsigned a = __builtin_amdgcn_perm(t1, t0, sel);
+  const unsigned b = __builtin_amdgcn_perm(t3, t2, sel);
+  return (b & hm) | (a & ~hm);
+}
+
+// Dword w holds 8 nibbles; byte b carries the codes of k offsets b (low nibble) and b + 4
+// (high nibble).  Returns the four fp16 pairs (k 0,1), (2,3), (4,5), (6,7), each times s.
+__device__ __forceinline__ u32x4 dq_nf4(unsigned w, unsigned s2, const Lut& t) {
+  const unsigned w4 = w >> 4;
+  const unsigned sa = w & 0x07070707u, sb = w4 & 0x07070707u;
+  // bytes 0xFF where bit 3 (sa) or bit 7 (sb) of the byte is set: the sign-replicating
+  // selectors 8..11 of v_perm_b32 read bit 7 of bytes 1, 3, 5, 7 of {x << 8, x}
+  const unsigned ha = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);
+  const unsigned hb = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+  const unsigned la = lut16(t.lo[0], t.lo[1], t.lo[2], t.lo[3], sa, ha);   // low bytes, k 0..3
+  const unsigned ua = lut16(t.hi[0], t.hi[1], t.hi[2], t.hi[3], sa, ha);   // high bytes, k 0..3
+  const unsigned lb = lut16(t.lo[0], t.lo[1], t.lo[2], t.lo[3], sb, hb);   // k 4..7
+  const unsigned ub = lut16(t.hi[0], t.hi[1], t.hi[2], t.hi[3], sb, hb);
+  const f16x2 s = __builtin_bit_cast(f16x2, s2);
+  const unsigned p0 = __builtin_amdgcn_perm(ua, la, 0x05010400u);   // fp16 of k 0 | k 1 << 16
+  const unsigned p1 = __builtin_amdgcn_perm(ua, la, 0x07030602u);   // k 2, 3
+  const unsigned p2 = __builtin_amdgcn_perm(ub, lb, 0x05010400u);   // k 4, 5
+  const unsigned p3 = __builtin_amdgcn_perm(ub, lb, 0x07030602u);   // k 6, 7
+  return u32x4{__builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, p0) * s),
+               __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, p1) * s),
+               __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, p2) * s),
+               __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, p3) * s)};
 }
 
 __device__ __forceinline__ u32x4 dq_fp8(unsigned lo, unsigned hi) {
@@ -207,7 +262,7 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
   }
   if constexpr (!SCALES) {
     return;
-  } else if constexpr (qgemm::int_weights(FMT)) {
+  } else if constexpr (qgemm::group_scaled(FMT)) {
     const uint16_t* S = static_cast<const uint16_t*>(a.S);
     const int c = lane & 15;
     if constexpr (G <= 128) {
@@ -237,14 +292,14 @@ __device__ __forceinline__ void load_wfrag(const KArgs& a, int nb, int kb, int l
 // column block's scales.  FP8 has none.
 template <int FMT, int G>
 __device__ __forceinline__ int sc_rel(int kb) {
-  if constexpr (qgemm::int_weights(FMT)) return G <= 128 ? kb * 32 * (128 / G) : (kb >> 1) * 32;
+  if constexpr (qgemm::group_scaled(FMT)) return G <= 128 ? kb * 32 * (128 / G) : (kb >> 1) * 32;
   else if constexpr (FMT == qgemm::FMT_FP4) return kb * 128;
   else return 0;
 }
 // End of the scale bytes that cover k blocks up to kb_end (exclusive); a group of 256 is kept whole.
 template <int FMT, int G>
 __device__ __forceinline__ int sc_end(int kb_end) {
-  return sc_rel<FMT, G>(qgemm::int_weights(FMT) && G > 128 ? kb_end + 1 : kb_end);
+  return sc_rel<FMT, G>(qgemm::group_scaled(FMT) && G > 128 ? kb_end + 1 : kb_end);
 }
 
 // Scales of k block kb for this lane's column, from an LDS copy of one column block's packed
@@ -253,7 +308,7 @@ template <int FMT, int G>
 __device__ __forceinline__ void read_staged_scales(const unsigned char* s, int kb, int kb_begin, int lane,
                                                    WFrag<FMT>& f) {
   const unsigned char* p = s + (sc_rel<FMT, G>(kb) - sc_rel<FMT, G>(kb_begin));
-  if constexpr (qgemm::int_weights(FMT)) {
+  if constexpr (qgemm::group_scaled(FMT)) {
     constexpr int T = G <= 128 ? 128 / G : 1;
     p += (lane & 15) * T * 2;
     if constexpr (T == 4) {
@@ -282,9 +337,11 @@ __device__ __forceinline__ unsigned int4_scale_pair(const unsigned (&s)[2], int 
 
 // The B operand (dequantized weights) of K step t.
 template <int FMT, int G>
-__device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (&fs)[4]) {
+__device__ __forceinline__ u32x4 bfrag(const WFrag<FMT>& f, int t, const float (&fs)[4], const Lut& lut) {
   if constexpr (FMT == qgemm::FMT_INT4) {
     return dq_int4(f.w[0][t], int4_scale_pair<G>(f.s, t));
+  } else if constexpr (FMT == qgemm::FMT_NF4) {
+    return dq_nf4(f.w[0][t], int4_scale_pair<G>(f.s, t), lut);
   } else if constexpr (FMT == qgemm::FMT_INT2) {
     return dq_int2(f.w[0][t >> 1], t & 1, int4_scale_pair<G>(f.s, t));
   } else if constexpr (FMT == qgemm::FMT_FP8) {
@@ -378,6 +435,11 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
 // Launch the kernel instance the plan names on `stream`; return hipGetLastError().
 hipError_t launch_decode(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
+// The same for one format; each kernel source instantiates these for one format per object.
+template <int FMT>
+hipError_t launch_decode_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
+template <int FMT>
+hipError_t launch_prefill_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
 
 }  // namespace dev
 }  // namespace qgemm

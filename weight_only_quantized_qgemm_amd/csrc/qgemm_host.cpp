@@ -36,6 +36,7 @@ static const char* dtype_name(int d) {
     case QGEMM_DT_FP8_E4M3: return "FP8_E4M3";
     case QGEMM_DT_FP4_E2M1: return "FP4_E2M1";
     case QGEMM_DT_INT2: return "INT2";
+    case QGEMM_DT_NF4: return "NF4";
     default: return "?";
   }
 }
@@ -43,6 +44,7 @@ static const char* dtype_name(int d) {
 Format format_of(const qgemm_problem_t* p) {
   if (p->w_dtype == QGEMM_DT_INT4) return FMT_INT4;
   if (p->w_dtype == QGEMM_DT_INT2) return FMT_INT2;
+  if (p->w_dtype == QGEMM_DT_NF4) return FMT_NF4;
   if (p->w_dtype == QGEMM_DT_FP8_E4M3) return p->a_dtype == QGEMM_DT_F16 ? FMT_FP8H : FMT_FP8;
   return FMT_FP4;
 }
@@ -54,9 +56,9 @@ static const int64_t kMaxDim = int64_t(1) << 24;
 qgemm_status_t validate_problem(const qgemm_problem_t* p) {
   if (!p) return fail(QGEMM_ERR_INVALID_ARGUMENT, "problem is NULL");
   for (int d : {p->a_dtype, p->w_dtype, p->out_dtype})
-    if (d < QGEMM_DT_F16 || d > QGEMM_DT_INT2)
+    if (d < QGEMM_DT_F16 || d > QGEMM_DT_NF4)
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "dtype value %d is not a qgemm_dtype_t", d);
-  if (p->scale_layout < QGEMM_SCALE_GROUP_F16 || p->scale_layout > QGEMM_SCALE_BLOCK16_E4M3)
+  if (p->scale_layout < QGEMM_SCALE_GROUP_F16 || p->scale_layout > QGEMM_SCALE_GROUP_F16_LUT16)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "scale_layout %d is not a qgemm_scale_layout_t", p->scale_layout);
   if (p->M < 0 || p->M > kMaxDim)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "M must be in [0, %lld], got %lld", (long long)kMaxDim, (long long)p->M);
@@ -68,11 +70,13 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
                 (long long)kMaxDim, (long long)p->K);
 
   const int a = p->a_dtype, w = p->w_dtype, o = p->out_dtype, sl = p->scale_layout, g = p->group_size;
-  if (w == QGEMM_DT_INT4 || w == QGEMM_DT_INT2) {
+  if (w == QGEMM_DT_INT4 || w == QGEMM_DT_INT2 || w == QGEMM_DT_NF4) {
     const char* wn = dtype_name(w);
-    if (a != QGEMM_DT_F16 || sl != QGEMM_SCALE_GROUP_F16 || (o != QGEMM_DT_F16 && o != QGEMM_DT_F32))
-      return fail(QGEMM_ERR_UNSUPPORTED, "%s weights need a_dtype F16, scale_layout GROUP_F16 and out_dtype F16 or F32; "
-                  "got a=%s out=%s scale_layout=%d", wn, dtype_name(a), dtype_name(o), sl);
+    const int want = w == QGEMM_DT_NF4 ? QGEMM_SCALE_GROUP_F16_LUT16 : QGEMM_SCALE_GROUP_F16;
+    if (a != QGEMM_DT_F16 || sl != want || (o != QGEMM_DT_F16 && o != QGEMM_DT_F32))
+      return fail(QGEMM_ERR_UNSUPPORTED, "%s weights need a_dtype F16, scale_layout %s and out_dtype F16 or F32; "
+                  "got a=%s out=%s scale_layout=%d", wn, w == QGEMM_DT_NF4 ? "GROUP_F16_LUT16" : "GROUP_F16",
+                  dtype_name(a), dtype_name(o), sl);
     if (g != 32 && g != 64 && g != 128 && g != 256)
       return fail(QGEMM_ERR_UNSUPPORTED, "%s group_size must be 32, 64, 128 or 256, got %d", wn, g);
     if (p->K % g) return fail(QGEMM_ERR_INVALID_ARGUMENT, "K (%lld) must be a multiple of group_size (%d)", (long long)p->K, g);
@@ -88,7 +92,7 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
                   "got a=%s out=%s scale_layout=%d", dtype_name(a), dtype_name(o), sl);
     if (g != 16) return fail(QGEMM_ERR_INVALID_ARGUMENT, "FP4_E2M1 takes group_size 16 (one e4m3 scale per 16 K), got %d", g);
   } else {
-    return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, INT2, FP8_E4M3, FP4_E2M1)", dtype_name(w));
+    return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, INT2, NF4, FP8_E4M3, FP4_E2M1)", dtype_name(w));
   }
 
   if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL)
@@ -184,7 +188,8 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     };
     auto fits_twice = [&](int k) {
       const int wregs = fp8_weights(pl->fmt) ? 8 : 5;
-      return 2 * k * ((pl->astage ? 0 : 16) + pl->cb * wregs) <= 210;
+      const int budget = pl->fmt == FMT_NF4 ? 202 : 210;     // NF4 keeps its code book in 8 registers
+      return 2 * k * ((pl->astage ? 0 : 16) + pl->cb * wregs) <= budget;
     };
     pl->kpw = 1;
     for (int k : kRuns)
@@ -264,6 +269,36 @@ static uint16_t f16_bits_of(double v) {   // v already an fp16 value (finite)
   return (uint16_t)(s | ((e + 15) << 10) | m);
 }
 
+// Standard normal quantile: bisection on Phi(x) = erfc(-x / sqrt 2) / 2 to double precision.
+static double normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int i = 0; i < 200 && hi - lo > 0.0; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p) lo = mid;
+    else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// The NormalFloat-4 code book (QLoRA's construction), in fp16: quantiles of N(0,1) at 8
+// evenly spaced probabilities from delta down to (not including) 1/2 for the positive
+// values and at 7 for the negative ones, plus an exact 0, sorted and divided by the largest.
+// delta = ((1 - 1/30) + (1 - 1/32)) / 2 sits between the outermost quantile estimates of a
+// 15- and a 16-point grid.
+static void nf4_codebook(double (&t)[16]) {
+  const double delta = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+  double neg[7], pos[8];
+  for (int i = 0; i < 7; ++i) neg[i] = -normal_quantile(delta + (0.5 - delta) * i / 7.0);   // -q .. nearest 0
+  for (int i = 0; i < 8; ++i) pos[i] = normal_quantile(delta + (0.5 - delta) * i / 8.0);    // q .. nearest 0
+  const double top = pos[0];
+  int n = 0;
+  for (int i = 0; i < 7; ++i) t[n++] = neg[i] / top;
+  t[n++] = 0.0;
+  for (int i = 7; i >= 0; --i) t[n++] = pos[i] / top;
+  for (int i = 0; i < 16; ++i) t[i] = round_format(t[i], 10, -14);
+}
+
 static uint8_t e4m3_code_of(double v) {   // v already an e4m3 value, |v| <= 448
   if (v == 0.0) return 0;
   uint8_t s = std::signbit(v) ? 0x80 : 0;
@@ -337,12 +372,57 @@ qgemm_status_t qgemm_quantize(const qgemm_problem_t* p, const float* w_nk, void*
   if (!w_nk || !codes_canonical) return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk and codes_canonical must not be NULL");
   const Format fmt = format_of(p);
   if (!fp8_weights(fmt) && !scales_canonical)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical must not be NULL for INT4 / INT2 / FP4");
-  if (!int_weights(fmt) && !alpha_out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha_out must not be NULL for FP8 / FP4");
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "scales_canonical must not be NULL for INT4 / INT2 / NF4 / FP4");
+  if (!group_scaled(fmt) && !alpha_out) return fail(QGEMM_ERR_INVALID_ARGUMENT, "alpha_out must not be NULL for FP8 / FP4");
   const int64_t N = p->N, K = p->K;
   uint8_t* codes = static_cast<uint8_t*>(codes_canonical);
 
-  if (int_weights(fmt)) {
+  if (fmt == FMT_NF4) {
+    // s = RNE_fp16(absmax) per (group, column): the code book spans [-1, 1]; code = index of
+    // the book entry nearest to w / s, ties to the lower index; 7 (the entry 0) when s = 0
+    double book[16];
+    nf4_codebook(book);
+    const int G = p->group_size;
+    uint16_t* sc = static_cast<uint16_t*>(scales_canonical);   // [16] book, then [K/G][N]
+    for (int c = 0; c < 16; ++c) sc[c] = f16_bits_of(book[c]);
+    sc += 16;
+    std::vector<uint8_t> q(K);
+    for (int64_t n = 0; n < N; ++n) {
+      const float* row = w_nk + n * K;
+      for (int64_t g = 0; g < K / G; ++g) {
+        double amax = 0.0;
+        for (int i = 0; i < G; ++i) {
+          const double v = std::fabs((double)row[g * G + i]);
+          if (!std::isfinite(v))
+            return fail(QGEMM_ERR_INVALID_ARGUMENT, "w_nk[%lld] is not finite", (long long)(n * K + g * G + i));
+          amax = v > amax ? v : amax;
+        }
+        const double s = round_format(amax, 10, -14);
+        if (!(s <= 65504.0))
+          return fail(QGEMM_ERR_INVALID_ARGUMENT, "column %lld group %lld: absmax %g overflows the fp16 scale",
+                      (long long)n, (long long)g, amax);
+        sc[g * N + n] = f16_bits_of(s);
+        for (int i = 0; i < G; ++i) {
+          int best = 7;
+          if (s != 0.0) {
+            const double x = (double)row[g * G + i] / s;
+            double bd = std::fabs(x - book[0]);
+            best = 0;
+            for (int c = 1; c < 16; ++c) {
+              const double d = std::fabs(x - book[c]);
+              if (d < bd) { bd = d; best = c; }
+            }
+          }
+          q[g * G + i] = (uint8_t)best;
+        }
+      }
+      for (int64_t j = 0; j < K / 2; ++j) codes[n * (K / 2) + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+    }
+    if (alpha_out) *alpha_out = 1.0f;
+    return QGEMM_OK;
+  }
+
+  if (group_scaled(fmt)) {
     // symmetric absmax per (group, column): s = RNE_fp16(absmax / qmax), code = clamp(rint(w / s),
     // -qmax-1, qmax) + qmax + 1 with qmax = 7 (INT4) or 1 (INT2)
     const bool i2 = fmt == FMT_INT2;
@@ -440,7 +520,7 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
   const int64_t N = p->N, K = p->K, NB = N / 16;
   const size_t need_w = fp8_weights(fmt) ? (size_t)(N * K) : fmt == FMT_INT2 ? (size_t)(N * K / 4) : (size_t)(N * K / 2);
   size_t need_s = 0;
-  if (int_weights(fmt)) need_s = (size_t)(N * (K / p->group_size)) * 2;
+  if (group_scaled(fmt)) need_s = (size_t)(N * (K / p->group_size)) * 2 + (fmt == FMT_NF4 ? kLutHeaderBytes : 0);
   if (fmt == FMT_FP4) need_s = (size_t)(N * (K / 16));
   const size_t cap_w = *w_packed_bytes, cap_s = *s_packed_bytes;
   *w_packed_bytes = need_w;
@@ -496,7 +576,8 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
       // of column l & 15 at k = 32t + 8(l >> 4) + J[slot].
       static const int J_INT4[8] = {0, 2, 4, 6, 1, 3, 5, 7};
       static const int J_FP4[8] = {0, 1, 2, 3, 4, 5, 6, 7};
-      const int* J = fmt == FMT_INT4 ? J_INT4 : J_FP4;
+      static const int J_NF4[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+      const int* J = fmt == FMT_INT4 ? J_INT4 : fmt == FMT_NF4 ? J_NF4 : J_FP4;
       const int64_t KB = K / 128;
       for (int64_t nb = 0; nb < NB; ++nb)
         for (int64_t kb = 0; kb < KB; ++kb) {
@@ -519,13 +600,23 @@ qgemm_status_t qgemm_pack(const qgemm_problem_t* p, const void* w_canonical, con
   }
 
   if (s_packed && need_s) {
-    if (int_weights(fmt)) {
+    if (group_scaled(fmt)) {
       const int G = p->group_size;
       const int span = G > 128 ? G : 128;
       const int T = G < 128 ? 128 / G : 1;
       const int64_t KS = K / span, NG = K / G;
       const uint16_t* src = static_cast<const uint16_t*>(scales_canonical);   // [K/G][N]
       uint16_t* dst = static_cast<uint16_t*>(s_packed);
+      if (fmt == FMT_NF4) {   // header: code-book low bytes in dwords 0..3, high bytes in 4..7
+        uint8_t* h = static_cast<uint8_t*>(s_packed);
+        std::memset(h, 0, kLutHeaderBytes);
+        for (int c = 0; c < 16; ++c) {
+          h[c] = (uint8_t)(src[c] & 0xFF);
+          h[16 + c] = (uint8_t)(src[c] >> 8);
+        }
+        src += 16;
+        dst += kLutHeaderBytes / 2;
+      }
       for (int64_t nb = 0; nb < NB; ++nb)
         for (int64_t ks = 0; ks < KS; ++ks)
           for (int c = 0; c < 16; ++c)

@@ -38,10 +38,14 @@ constexpr int kDecodeStageS = kDecodeMaxScales / (16 * 64 * kDecodeWaves);
 // Kernel formats.  FMT_FP8H is FP8 weights with fp16 activations (mm_fp16_fp8): the weight
 // layout, quantization and alpha are FP8's, the MFMA is the fp16 one.  FMT_INT2 (W2A16)
 // shares INT4's fp16 group scales and their layout; its weight blocks are 512 bytes.
-enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2, FMT_FP8H = 3, FMT_INT2 = 4 };
+// FMT_NF4 has INT4's block size and scale layout, behind a 256-byte code-book header.
+enum Format : int { FMT_INT4 = 0, FMT_FP8 = 1, FMT_FP4 = 2, FMT_FP8H = 3, FMT_INT2 = 4, FMT_NF4 = 5 };
 constexpr bool fp8_weights(int fmt) { return fmt == FMT_FP8 || fmt == FMT_FP8H; }
-constexpr bool int_weights(int fmt) { return fmt == FMT_INT4 || fmt == FMT_INT2; }
-constexpr bool f16_mfma(int fmt) { return fmt == FMT_INT4 || fmt == FMT_FP8H || fmt == FMT_INT2; }
+// fp16 scale per (group of G k, column), no alpha
+constexpr bool group_scaled(int fmt) { return fmt == FMT_INT4 || fmt == FMT_INT2 || fmt == FMT_NF4; }
+constexpr bool f16_mfma(int fmt) { return fmt == FMT_INT4 || fmt == FMT_FP8H || fmt == FMT_INT2 || fmt == FMT_NF4; }
+// Bytes in front of the NF4 scales: the code book split into low- and high-byte tables.
+constexpr int kLutHeaderBytes = 256;
 
 // ---- Decode LDS layout, shared by the launch plan (which sizes the allocation) and the kernel.
 // Packed scale bytes of one column block that nkb consecutive k blocks read, at most (an INT4

@@ -98,6 +98,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
+  Lut lut;                                           // NF4 code book (wavefront-uniform)
+  load_lut<FMT>(a, lut);
   const int tile = blockIdx.x, split = blockIdx.y;
   int tm, tn;
   pf_tile_of(tile, gridDim.x, a.tiles_n, tm, tn);
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     };
     u32x4 b[2][TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[0][j] = bfrag<FMT, G>(wf[j], 0, fs[j]);
+    for (int j = 0; j < TN; ++j) b[0][j] = bfrag<FMT, G>(wf[j], 0, fs[j], lut);
 #pragma unroll
     for (int u = 0; u < LA && u < NU; ++u) read_unit(u, af[u]);
     __builtin_amdgcn_sched_barrier(0);
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
       __builtin_amdgcn_sched_barrier(0);   // later units' reads go out before this unit's MFMAs
       if (i0 + RU == TM && t < 3) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[(t + 1) & 1][j] = bfrag<FMT, G>(wf[j], t + 1, fs[j]);
+        for (int j = 0; j < TN; ++j) b[(t + 1) & 1][j] = bfrag<FMT, G>(wf[j], t + 1, fs[j], lut);
       }
 #pragma unroll
       for (int r = 0; r < RU; ++r)
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   if (a.splits > 1) {
     if (!splitk_finish<TM * TN, NT>(a, tile, split, BM * BN, true, v)) return;
   }
-  const float alpha = qgemm::int_weights(FMT) ? 1.0f : *a.alpha;
+  const float alpha = qgemm::group_scaled(FMT) ? 1.0f : *a.alpha;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int nb = (n0 >> 4) + TN * wn + j;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * TM * wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < a.M) store_out(a, m, n, qgemm::int_weights(FMT) ? v[TN * i + j][r] : v[TN * i + j][r] * alpha, bv);
+        if (m < a.M) store_out(a, m, n, qgemm::group_scaled(FMT) ? v[TN * i + j][r] : v[TN * i + j][r] * alpha, bv);
       }
   }
 }
@@ -254,37 +256,30 @@ struct PrefillLauncher {
   }
 };
 
-// Instances for every group size the format has (INT4, INT2: 32, 64, 128, 256; FP8 / FP4: none).
-template <template <int, int> class L>
-hipError_t by_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
-  switch (pl.fmt) {
-    case FMT_INT4:
-      switch (group_size) {
-        case 32: return L<FMT_INT4, 32>::run(pl, a, stream);
-        case 64: return L<FMT_INT4, 64>::run(pl, a, stream);
-        case 128: return L<FMT_INT4, 128>::run(pl, a, stream);
-        case 256: return L<FMT_INT4, 256>::run(pl, a, stream);
-        default: return hipErrorInvalidValue;
-      }
-    case FMT_INT2:
-      switch (group_size) {
-        case 32: return L<FMT_INT2, 32>::run(pl, a, stream);
-        case 64: return L<FMT_INT2, 64>::run(pl, a, stream);
-        case 128: return L<FMT_INT2, 128>::run(pl, a, stream);
-        case 256: return L<FMT_INT2, 256>::run(pl, a, stream);
-        default: return hipErrorInvalidValue;
-      }
-    case FMT_FP8: return L<FMT_FP8, 0>::run(pl, a, stream);
-    case FMT_FP8H: return L<FMT_FP8H, 0>::run(pl, a, stream);
-    default: return L<FMT_FP4, 0>::run(pl, a, stream);
+}  // namespace
+
+// The instances of one format (QGEMM_FMT_UNIT): every group size it has (INT4, INT2, NF4:
+// 32, 64, 128, 256; FP8 / FP4: none).  The source is compiled once per format, so that the
+// many instances build in parallel; launch_prefill dispatches to the format's unit.
+template <int FMT>
+hipError_t launch_prefill_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  if constexpr (qgemm::group_scaled(FMT)) {
+    switch (group_size) {
+      case 32: return PrefillLauncher<FMT, 32>::run(pl, a, stream);
+      case 64: return PrefillLauncher<FMT, 64>::run(pl, a, stream);
+      case 128: return PrefillLauncher<FMT, 128>::run(pl, a, stream);
+      case 256: return PrefillLauncher<FMT, 256>::run(pl, a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return PrefillLauncher<FMT, 0>::run(pl, a, stream);
   }
 }
 
-}  // namespace
-
-hipError_t launch_prefill(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
-  return by_format<PrefillLauncher>(pl, group_size, a, stream);
-}
+#ifndef QGEMM_FMT_UNIT
+#error "compile once per format with -DQGEMM_FMT_UNIT=<format>"
+#endif
+template hipError_t launch_prefill_format<QGEMM_FMT_UNIT>(const Plan&, int, const KArgs&, hipStream_t);
 
 }  // namespace dev
 }  // namespace qgemm
