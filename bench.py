@@ -9,8 +9,12 @@ The K timed steps are one HIP-graph replay; `value` is the effective weight band
 (packed weight + scale bytes / time) over them.
 
 Also reported: a `roofline` object for the decode kernel, `secondary` numbers (per-shape
-decode timings and the M = 4096 prefill TFLOP/s over the group-size sweep), and the CPU
-oracle timed on the host as `cpu_baseline`.
+decode timings and the M = 4096 prefill TFLOP/s over the group-size sweep), the CPU
+oracle timed on the host as `cpu_baseline`, and `comparators`: on the same shapes, the
+vendor 16-bit GEMM (hipBLASLt through torch) on a resident 16-bit weight and the cast-copy
+path (whole weight dequantized into HBM by torch ops, then that GEMM) -- context, not
+target.  `--all` adds the FP8, FP4, FP8-with-fp16-activations, INT2 and NF4 workloads (and
+comparators for the FP8 / FP4 shapes and the INT4 prefill).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
 """
@@ -112,6 +116,46 @@ def time_graph(torch, g, reps=1):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps        # ms
+
+
+def comparator_row(q, torch, fmt, M, N, K, G, key, rot_bytes, qgemm_us):
+    """Vendor paths on one shape, timed like the library (graphs over rotating copies):
+    the 16-bit GEMM on a resident 16-bit weight, and the cast-copy path (dequantize the whole
+    weight into HBM, then the same GEMM).  qgemm_us is the library's time on the shape."""
+    import comparators
+    import synthetic
+    pq = q.problem(1, N, K, fmt, group_size=G if fmt in q.GROUP_SCALED else None)
+    w = synthetic.weights(N, K, 0.05 if fmt in ("fp8", "fp8h") else 0.02, key)
+    codes, scales, alpha = q.quantize(pq, w)
+    cbytes = codes.nbytes + (0 if scales is None else scales.nbytes)
+    cc = [comparators.CastCopy(torch, fmt, N, K, G, codes, scales, alpha)
+          for _ in range(max(2, -(-rot_bytes // cbytes)))]
+    w16 = cc[0].dequantize()
+    dense = [w16] + [w16.clone() for _ in range(max(2, -(-rot_bytes // (w16.numel() * 2))) - 1)]
+    kind = "f16" if w16.dtype == torch.float16 else "bf16"
+    A = synthetic.activations(M, K, kind, key).cuda()
+    n = 10 if M >= 128 else 64
+    st = {"i": 0, "j": 0}
+
+    def run_dense():
+        comparators.dense_gemm(torch, A, dense[st["i"] % len(dense)])
+        st["i"] += 1
+
+    def run_cast():
+        cc[st["j"] % len(cc)].run(A)
+        st["j"] += 1
+
+    g1 = graph_of(torch, run_dense, n)
+    us_dense = time_graph(torch, g1, 3) * 1e3 / n
+    del g1
+    g2 = graph_of(torch, run_cast, n)
+    us_cast = time_graph(torch, g2, 3) * 1e3 / n
+    del g2, cc, dense, w16
+    torch.cuda.empty_cache()
+    return {"gemm": f"{fmt} M={M} N={N} K={K}" + (f" G={G}" if fmt in q.GROUP_SCALED else ""),
+            "qgemm_us": round(qgemm_us, 3), "vendor_16bit_gemm_us": round(us_dense, 3),
+            "cast_copy_us": round(us_cast, 3), "speedup_vs_16bit": round(us_dense / qgemm_us, 2),
+            "speedup_vs_cast_copy": round(us_cast / qgemm_us, 2)}
 
 
 KERNEL_SOURCES = {"decode": ["qgemm_device.h", "qgemm_decode.hip"],
@@ -292,6 +336,12 @@ def main():
     del gemms
     torch.cuda.empty_cache()
 
+    # vendor comparators on the decode shapes (hipBLASLt through torch; context, not target)
+    comps = []
+    for si, (M, N, K) in enumerate(DECODE_SHAPES):
+        comps.append(comparator_row(q, torch, "int4", M, N, K, 128, (wi, si), rot // 2,
+                                    secondary[si]["us_per_launch"]))
+
     # prefill M = 4096 over the group-size sweep (TFLOP/s)
     wi2 = synthetic.WORKLOAD_INDEX["int4_prefill"]
     for G in PREFILL_G:
@@ -301,6 +351,8 @@ def main():
         tf = g.flops / (ms * 1e-3) / 1e12
         secondary.append({"gemm": f"int4 M=4096 N=4096 K=4096 G={G}", "us_per_launch": round(ms * 1e3, 2),
                           "TFLOPs": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+        if args.all and G == 128:
+            comps.append(comparator_row(q, torch, "int4", 4096, 4096, 4096, G, (wi2, 0), 64 << 20, ms * 1e3))
         del gg, g
         torch.cuda.empty_cache()
 
@@ -323,6 +375,9 @@ def main():
                                   "weight_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
                 del gg, g
                 torch.cuda.empty_cache()
+                if name in ("fp8", "fp4", "fp8h"):
+                    comps.append(comparator_row(q, torch, name, M, N, K, 0, (wix, si),
+                                                (64 << 20) if big else rot, ms * 1e3))
 
     cpu = None if args.no_cpu else cpu_baseline()
 
@@ -340,6 +395,7 @@ def main():
                      "algorithmic_bytes_per_launch": avg_bytes},
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "comparators": comps,
     }
     print(json.dumps(line), flush=True)
 
