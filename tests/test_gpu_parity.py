@@ -332,3 +332,15 @@ def test_nf4_any_code_book_bit_exact(q, hint, M):
         q.run(pr, A.cuda(), w_d, s_d, None, out, ws)
         T.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().astype(np.float64), want[:, rows].T), f"rows {k0}.."
+
+
+@pytest.mark.parametrize("fmt,G,M,N,K", [("int4", 128, 1000, 4048, 1024), ("fp8", None, 2000, 2560, 640),
+                                         ("int4", 64, 520, 4096, 2048), ("fp4", None, 1024, 2048, 2048)])
+def test_mid_m_auto_plan(q, fmt, G, M, N, K):
+    # Shapes between decode and the large tiles, where the planner's time model picks the tile
+    # (128 x 128 or 256 x 256) and the K split; every row is checked.
+    say(f"case mid-m fmt={fmt} G={G} M={M} N={N} K={K}")
+    prep = Prepared(q, fmt, N, K, G or 0, (61, N, K))
+    A = _act(fmt, M, K, (61, M))
+    st, _ = check_against_oracle(q, prep, A)
+    say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")

@@ -202,28 +202,38 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->tile_elems = pl->cb * 256;
   } else {
     pl->kind = KIND_PREFILL;
-    // The large tile once M fills at least two of its row tiles.
-    const bool large = p->tile_hint ? p->tile_hint == pf_bm(kPfLarge) : p->M >= 2 * pf_bm(kPfLarge);
-    const PfShape sh = large ? kPfLarge : kPfMedium;
-    pl->bm = pf_bm(sh);
-    pl->bn = pf_bn(sh);
-    // the A tile is addressed with 32-bit byte offsets
-    if ((int64_t)pl->bm * p->K * 2 > 0x7fffffffLL)
-      return fail(QGEMM_ERR_UNSUPPORTED, "the prefill kernel needs %d * K * 2 < 2^31 (K = %lld)", pl->bm,
-                  (long long)p->K);
-    const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
-    // K split: the count that minimises a step-count model of the launch, in units of one
-    // k block of one workgroup: rounds of the grid over the CUs x (k blocks per slice +
-    // pipeline fill and drain), plus, when split, the final workgroup's reads of one
-    // partial tile per slice.  Slices keep at least two k blocks.
-    const double kFill = 3.0, kPartialRead = 1.5;
-    int best = 1;
+    // Tile shape and K split: the pair that minimises a time model of the launch, in
+    // microseconds measured on MI355X: rounds of the grid over the CUs x (k blocks per slice
+    // + pipeline fill) x the tile's time per k block under full load, plus, when split, the
+    // fp32 partial tiles written and read back at HBM speed and one dependent partial read
+    // per slice by the workgroup that finishes each tile.  The medium tile does a quarter of
+    // the large tile's work per k block in about 0.38 of its time, so it wins whenever it
+    // fills the CUs and the large tile cannot (e.g. M = 512..1024 at N = 4096, or
+    // M = 2048 at N = 10240); the large one wins once both fill several rounds.
+    struct Cand { PfShape sh; double t_kb; };
+    const Cand cands[2] = {{kPfMedium, 1.3}, {kPfLarge, 3.4}};
+    const double kFill = 3.0, kPartialLatency = 1.5, kBytesPerUs = 5.0e6;
+    int best_c = -1, best = 1;
     double best_cost = 0.0;
-    for (int s = 1; s <= 64 && s <= kblocks / 2; ++s) {
-      const double rounds = (double)((mt * nt * s + kCUs - 1) / kCUs);
-      const double cost = rounds * (ceil_div(kblocks, s) + kFill) + (s > 1 ? kPartialRead * s : 0.0);
-      if (s == 1 || cost < best_cost) { best = s; best_cost = cost; }
+    for (int c = 0; c < 2; ++c) {
+      const PfShape sh = cands[c].sh;
+      if (p->tile_hint ? p->tile_hint != pf_bm(sh) : (c == 1 && p->M <= pf_bm(kPfMedium))) continue;
+      if ((int64_t)pf_bm(sh) * p->K * 2 > 0x7fffffffLL) continue;     // the A tile uses 32-bit offsets
+      const int64_t mt = (p->M + pf_bm(sh) - 1) / pf_bm(sh), nt = (p->N + pf_bn(sh) - 1) / pf_bn(sh);
+      for (int s = 1; s <= 64 && (s == 1 || s <= kblocks / 2); ++s) {
+        const double rounds = (double)((mt * nt * s + kCUs - 1) / kCUs);
+        const double partials = (double)(mt * nt * s) * pf_bm(sh) * pf_bn(sh) * 4 * 2 / kBytesPerUs;
+        const double cost = rounds * (ceil_div(kblocks, s) + kFill) * cands[c].t_kb +
+                            (s > 1 ? partials + kPartialLatency * s : 0.0);
+        if (best_c < 0 || cost < best_cost) { best_c = c; best = s; best_cost = cost; }
+      }
     }
+    if (best_c < 0)
+      return fail(QGEMM_ERR_UNSUPPORTED, "the prefill kernel needs %d * K * 2 < 2^31 (K = %lld)",
+                  p->tile_hint ? p->tile_hint : pf_bm(kPfMedium), (long long)p->K);
+    pl->bm = pf_bm(cands[best_c].sh);
+    pl->bn = pf_bn(cands[best_c].sh);
+    const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
     pl->splits = best;
     finish_split(pl, kblocks, p->split_k_hint);
     if (mt * nt > 0x7fffffffLL) return fail(QGEMM_ERR_UNSUPPORTED, "too many output tiles (%lld)", (long long)(mt * nt));
