@@ -239,8 +239,9 @@ def main():
                     help="for rocprofv3 --pmc: copy a MIB-sized device buffer 5 times (known traffic)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMM shards by "
-              "columns with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the GEMM would shard "
+              "by output columns, each rank holding its columns' packed weights, with no exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
