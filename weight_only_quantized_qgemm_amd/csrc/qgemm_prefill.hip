@@ -86,11 +86,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char As2[ST > 2 ? BM * ROWB : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char As3[ST > 3 ? BM * ROWB : 16];
   auto stage = [&](int i) -> unsigned char* { return i == 0 ? As0 : i == 1 ? As1 : i == 2 ? As2 : As3; };
+  // With three or more stages the first LA read units of the next block are read during
+  // the current one (after its own last reads), so a block starts with its A fragments in
+  // flight instead of behind the barrier; the unit ring must then line up across blocks.
+  constexpr bool XPF = ST >= 3 && NU % (LA + 1) == 0;
   // Vector-memory instructions per k block per wavefront: NDMA A loads and, per weight
   // column block, two (the fragment and its scales, or FP8's two fragment halves).  At the
-  // end of a step the next block must have landed while the ST - 2 blocks after it may
-  // still be in flight; loads complete in issue order, so that is this many pending.
-  constexpr int PEND = (ST - 2) * (NDMA + 2 * TN);
+  // end of a step the next block must have landed (with XPF: the next two, since the step
+  // after reads ahead into the second) while the blocks after them may still be in flight;
+  // loads complete in issue order, so that is this many pending.
+  constexpr int PEND = (ST - (XPF ? 3 : 2)) * (NDMA + 2 * TN);
   static_assert(PEND <= 63, "vmcnt counts at most 63 outstanding loads");
   // s_waitcnt immediate: vmcnt = PEND (bits 3:0 and 15:14), expcnt and lgkmcnt left open.
   // Through the builtin (not inline asm) the compiler's own wait insertion knows of it.
@@ -143,10 +148,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Computes one k block from As / wf while issuing the DMA loads of the next one (into
+  // A-fragment read units: unit u of a k block sits in slot u % (LA + 1); with XPF the
+  // first LA units of a block are read by the step before it.
+  u32x4 af[LA + 1][RU];
+  auto read_unit = [&](const unsigned char* As, int u, u32x4 (&dst)[RU]) {
+    const int t = u / TU, i0 = (u % TU) * RU;
+#pragma unroll
+    for (int r = 0; r < RU; ++r) dst[r] = *reinterpret_cast<const u32x4*>(As + aoff[t] + (i0 + r) * 16 * ROWB);
+  };
+
+  // Computes one k block from As / wf while issuing the DMA loads of a later one (into
   // Ad), DS read units apart: issued all at once they would fill the memory pipeline's
-  // queue and stall the wavefront's MFMAs behind it.
-  auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN], int kb_next, unsigned char* Ad) {
+  // queue and stall the wavefront's MFMAs behind it.  An is the stage of the next block.
+  auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN], int kb_next, unsigned char* Ad,
+                     const unsigned char* An) {
     float fs[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -154,22 +169,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
       for (int t = 0; t < 4; ++t) fs[j][t] = 0.f;
       if constexpr (FMT == qgemm::FMT_FP4) fp4_scales(wf[j].s[0], fs[j]);
     }
-    u32x4 af[LA + 1][RU];
-    auto read_unit = [&](int u, u32x4 (&dst)[RU]) {
-      const int t = u / TU, i0 = (u % TU) * RU;
-#pragma unroll
-      for (int r = 0; r < RU; ++r) dst[r] = *reinterpret_cast<const u32x4*>(As + aoff[t] + (i0 + r) * 16 * ROWB);
-    };
     u32x4 b[2][TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[0][j] = bfrag<FMT, G>(wf[j], 0, fs[j], lut);
+    if constexpr (!XPF) {
 #pragma unroll
-    for (int u = 0; u < LA && u < NU; ++u) read_unit(u, af[u]);
+      for (int u = 0; u < LA && u < NU; ++u) read_unit(As, u, af[u]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int t = u / TU, i0 = (u % TU) * RU;
-      if (u + LA < NU) read_unit(u + LA, af[(u + LA) % (LA + 1)]);
+      if (u + LA < NU) read_unit(As, u + LA, af[(u + LA) % (LA + 1)]);
+      else if constexpr (XPF) read_unit(An, u + LA - NU, af[(u + LA) % (LA + 1)]);
       if (u % DS == 0 && u / DS < NDMA) load_a(kb_next, Ad, u / DS);
       __builtin_amdgcn_sched_barrier(0);   // later units' reads go out before this unit's MFMAs
       if (i0 + RU == TM && t < 3) {
@@ -196,6 +208,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(WAIT_PEND);
   barrier_no_fence();
+  if constexpr (XPF) {
+#pragma unroll
+    for (int u = 0; u < LA && u < NU; ++u) read_unit(stage(0), u, af[u]);
+  }
 
   for (int kb = kb_begin; kb < kb_end; kb += ST) {
 #pragma unroll
@@ -204,7 +220,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
       const int kn = min(kb + j + ST - 1, kb_end - 1);
       load_w(kn, w[sn]);
       __builtin_amdgcn_sched_barrier(0);
-      compute(stage(j), w[j], kn, stage(sn));
+      compute(stage(j), w[j], kn, stage(sn), stage((j + 1) % ST));
       __builtin_amdgcn_s_waitcnt(WAIT_PEND);
       barrier_no_fence();
       if (kb + j + 1 >= kb_end) break;
