@@ -250,24 +250,28 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(KArgs a) {
   }
 }
 
-template <int FMT, int G, int CB, int KPW, bool ASTAGE>
+template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE>
 void launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  const dim3 grid(pl.grid_x, pl.grid_y), block(64 * QGEMM_DEC_NW);
+  const dim3 grid(pl.grid_x, pl.grid_y), block(64 * NW);
   const size_t lds = pl.lds_bytes;
   switch (pl.nruns) {
-    case 2: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 2>), grid, block, lds, stream, a); break;
-    case 3: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 3>), grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 4>), grid, block, lds, stream, a); break;
-    default: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, QGEMM_DEC_NW, ASTAGE, 1>), grid, block, lds, stream, a);
+    case 2: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 2>), grid, block, lds, stream, a); break;
+    case 3: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 3>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 4>), grid, block, lds, stream, a); break;
+    default: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 1>), grid, block, lds, stream, a);
   }
 }
 
+// Staged A always runs kDecodeWaves wavefronts; unstaged A with two or more column blocks
+// runs kDecodeWavesWide (the plan's nw says which).
 template <int FMT, int G, int CB, int KPW>
 void launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {
   if (pl.astage)
-    launch_nr<FMT, G, CB, KPW, true>(pl, a, stream);
+    launch_nr<FMT, G, CB, KPW, kDecodeWaves, true>(pl, a, stream);
+  else if constexpr (CB >= 2)
+    launch_nr<FMT, G, CB, KPW, kDecodeWavesWide, false>(pl, a, stream);
   else
-    launch_nr<FMT, G, CB, KPW, false>(pl, a, stream);
+    launch_nr<FMT, G, CB, KPW, kDecodeWaves, false>(pl, a, stream);
 }
 
 template <int FMT, int G>

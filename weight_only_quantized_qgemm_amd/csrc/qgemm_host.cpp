@@ -151,6 +151,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       cb = 2;
     }
     pl->cb = p->tile_hint ? p->tile_hint : cb;
+    pl->nw = !pl->astage && pl->cb >= 2 ? kDecodeWavesWide : kDecodeWaves;
     const int groups = ceil_div(nblocks, pl->cb);
     // K is split only when needed to bound what a workgroup stages in LDS (its A slice and
     // its scales), or when the output alone gives fewer than 128 workgroups (a split-K
@@ -158,30 +159,30 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // one k block.
     // Each wavefront stages its own share (ceil(kb / waves) k blocks) of A and of the scales.
     auto staged_ok = [&](int kb) {
-      const int share = ceil_div(kb, kDecodeWaves);
-      return (!pl->astage || 2 * 128 * p->M * (int64_t)share * kDecodeWaves <= kDecodeMaxA) &&
+      const int share = ceil_div(kb, pl->nw);
+      return (!pl->astage || 2 * 128 * p->M * (int64_t)share * pl->nw <= kDecodeMaxA) &&
              (!pl->astage ||
-              (int64_t)pl->cb * dec_scale_span(pl->fmt, p->group_size, share) * kDecodeWaves <= kDecodeMaxScales);
+              (int64_t)pl->cb * dec_scale_span(pl->fmt, p->group_size, share) * pl->nw <= kDecodeMaxScales);
     };
     int max_kb = kblocks;
     while (max_kb > 1 && !staged_ok(max_kb)) --max_kb;
     int s = 1;
     while (ceil_div(kblocks, s) > max_kb) ++s;
-    while (groups * s < kCUs / 2 && kblocks / (s * 2) >= kDecodeWaves) s *= 2;
+    while (groups * s < kCUs / 2 && kblocks / (s * 2) >= pl->nw) s *= 2;
     pl->splits = s;
     finish_split(pl, kblocks, p->split_k_hint);
     if (pl->kb_per_split > max_kb)
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d leaves %d k blocks per slice; the decode kernel "
                   "stages at most %d at M=%lld", p->split_k_hint, pl->kb_per_split, max_kb, (long long)p->M);
-    pl->lds_bytes = dec_lds_bytes(pl->fmt, p->group_size, (int)p->M, ceil_div(pl->kb_per_split, kDecodeWaves),
-                                  pl->cb, pl->astage, kDecodeWaves);
+    pl->lds_bytes = dec_lds_bytes(pl->fmt, p->group_size, (int)p->M, ceil_div(pl->kb_per_split, pl->nw),
+                                  pl->cb, pl->astage, pl->nw);
     // Each wavefront owns ceil(kb_per_split / waves) consecutive k blocks, streamed in runs
     // of KPW (at most 8 weight blocks in flight per wavefront): the whole share in one run
     // when an instance exists for it, else the largest instance below.  A share longer
     // than one run alternates two register sets, each KPW x (4 A fragments unless A is
     // staged + CB weight fragments of 5 registers, FP8 8); the run is shortened until both
     // sets fit in 210 registers (measured: more spills).
-    const int share = ceil_div(pl->kb_per_split, kDecodeWaves);
+    const int share = ceil_div(pl->kb_per_split, pl->nw);
     static const int kRuns[] = {8, 5, 4, 2, 1};            // instantiated KPW values
     auto instantiated = [&](int k) {
       return k * pl->cb <= 8 && (k != 5 || pl->cb == 1) && (k != 8 || pl->cb == 1);

@@ -23,11 +23,15 @@ constexpr PfShape kPfLarge{QGEMM_PF_LARGE};    // 256 x 256 output tile
 constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 128 output tile
 constexpr int pf_bm(PfShape s) { return 16 * s.wgm * s.tm; }
 constexpr int pf_bn(PfShape s) { return 16 * s.wgn * s.tn; }
-// Decode kernel: wavefronts per workgroup.
+// Decode kernel: wavefronts per workgroup (with A staged in LDS, and whenever a workgroup
+// owns a single column block), and the smaller count for wider workgroups of unstaged A:
+// half the wavefronts with twice the K share each pipeline longer runs (M = 16: N = 11008
+// 9.58 -> 9.00 us, FP8 N = 10240 14.5 -> 12.8 us; with one column block 6.9 -> 7.8 us).
 #ifndef QGEMM_DEC_NW
 #define QGEMM_DEC_NW 8
 #endif
 constexpr int kDecodeWaves = QGEMM_DEC_NW;
+constexpr int kDecodeWavesWide = 4;
 // Decode staging pass (A slice and scales into LDS): the largest staged A slice and scale
 // range per workgroup, and the 16-byte chunks per thread they take at most.
 constexpr int kDecodeMaxA = 32 * 1024;
@@ -89,6 +93,7 @@ struct Plan {
   // decode: column blocks (16 columns each) per workgroup, k blocks per wavefront run
   int cb, kpw;
   bool astage;            // decode: stage the A slice in LDS (small M)
+  int nw;                 // decode: wavefronts per workgroup
   int nruns;              // decode: runs per wavefront share, pipelined when 2..4 (else 1)
   int lds_bytes;          // decode: dynamic LDS per workgroup (staged A, staged scales, wave tiles)
   // prefill: workgroup tile (bm == pf_bm(kPfLarge) selects the large shape)
