@@ -335,7 +335,9 @@ def test_nf4_any_code_book_bit_exact(q, hint, M):
 
 
 @pytest.mark.parametrize("fmt,G,M,N,K", [("int4", 128, 1000, 4048, 1024), ("fp8", None, 2000, 2560, 640),
-                                         ("int4", 64, 520, 4096, 2048), ("fp4", None, 1024, 2048, 2048)])
+                                         ("int4", 64, 520, 4096, 2048), ("fp4", None, 1024, 2048, 2048),
+                                         ("int4", 256, 200, 2048, 1024), ("fp8h", None, 300, 4112, 512),
+                                         ("nf4", 128, 257, 1024, 2048)])
 def test_mid_m_auto_plan(q, fmt, G, M, N, K):
     # Shapes between decode and the large tiles, where the planner's time model picks the tile
     # (128 x 128 or 256 x 256) and the K split; every row is checked.
