@@ -1,0 +1,37 @@
+"""Host-side pieces of the benchmark (no GPU): the one-GPU guard, the algorithmic byte counts
+against the packer's sizes, and the recorded-traffic lookup."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import weight_only_quantized_qgemm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("fmt,N,K,G", [("int4", 4096, 4096, 128), ("int4", 11008, 4096, 32), ("int2", 4096, 4096, 128),
+                                       ("nf4", 4096, 4096, 64), ("fp8", 10240, 5120, 0), ("fp8h", 10240, 5120, 0),
+                                       ("fp4", 8192, 8192, 16)])
+def test_weight_bytes_are_the_packed_sizes(fmt, N, K, G):
+    # the algorithmic bytes behind every GB/s figure are exactly what the packer produces
+    p = q.problem(1, N, K, fmt, group_size=G if fmt in q.GROUP_SCALED else None)
+    wb, sb = q.packed_sizes(p)
+    assert bench.weight_bytes(fmt, N, K, G) == wb + sb
+
+
+def test_recorded_traffic_follows_the_kernel_sources(monkeypatch):
+    t = bench.recorded_traffic()
+    assert t is None or (isinstance(t, int) and t > bench.weight_bytes("int4", 4096, 4096, 128))
+    # a different decode source hash makes the recorded counters stale
+    monkeypatch.setattr(bench, "kernel_sha", lambda kind: "0" * 16)
+    assert bench.recorded_traffic() is None
