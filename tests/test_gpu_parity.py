@@ -346,3 +346,34 @@ def test_mid_m_auto_plan(q, fmt, G, M, N, K):
     A = _act(fmt, M, K, (61, M))
     st, _ = check_against_oracle(q, prep, A)
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
+
+
+def test_split_k_under_concurrent_load(q):
+    # Split-K must not rely on its workgroups being resident together (FlashInfer PR #7495
+    # analysis, section 3(d)): with a long GEMM occupying compute units from another stream,
+    # split-K decode and prefill launches still finish and give bitwise the results of an
+    # isolated run.
+    import torch as T
+    say("case split-k under concurrent load")
+    cases = [("int4", 1, 256, 128 * 64, 128, 1, 16), ("fp4", 128, 2048, 8192, 0, 2, 4),
+             ("fp8", 16, 512, 128 * 40, 0, 1, 5)]
+    preps = []
+    for fmt, M, N, K, G, hint, split in cases:
+        prep = Prepared(q, fmt, N, K, G, (62, N, K))
+        A = _act(fmt, M, K, (62, M))
+        y0, ws = run_gpu(q, prep, A, q.DT_F32, kernel_hint=hint, split_k_hint=split)
+        preps.append((prep, A, hint, split, y0, ws))
+    x = T.randn((8192, 8192), dtype=T.float16, device="cuda")
+    y = T.randn((8192, 8192), dtype=T.float16, device="cuda")
+    side = T.cuda.Stream()                       # default priority
+    side.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(side):
+        for _ in range(8):
+            z = T.mm(x, y)
+    for _ in range(3):
+        for prep, A, hint, split, y0, ws in preps:
+            y1, _ = run_gpu(q, prep, A, q.DT_F32, kernel_hint=hint, split_k_hint=split, workspace=ws)
+            assert np.array_equal(y1, y0)
+            assert not ws[:256].cpu().numpy().any()
+    side.synchronize()
+    del z
