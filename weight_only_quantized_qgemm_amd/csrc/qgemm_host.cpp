@@ -141,13 +141,15 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // distinct and fragments are loaded directly.
     pl->astage = p->M <= 4;
     // Column blocks per workgroup.  Every workgroup reads all M x K of A once, so wider
-    // workgroups cut A traffic; narrower ones put more compute units to work.  M = 1: A is
-    // negligible, one block each.  M <= 4: two.  Larger M: the fewest blocks (1 to 4)
-    // that keep the grid within one workgroup per compute unit.
+    // workgroups cut A traffic; narrower ones put more compute units to work.  M <= 4 (A
+    // staged per wavefront): one block each up to three workgroups per compute unit, two
+    // beyond (M = 4: N = 4096 5.4 vs 6.2 us, N = 11008 8.4 vs 9.3 us, N = 14336 10.7 vs
+    // 9.8 us).  Larger M: the fewest blocks (1 to 4) that keep the grid within one
+    // workgroup per compute unit.
     int cb = 1;
     if (p->M > 4) {
       while (cb < 4 && ceil_div(nblocks, cb) > kCUs) ++cb;
-    } else if (p->M > 1) {
+    } else if (p->M > 1 && nblocks > 3 * kCUs) {
       cb = 2;
     }
     pl->cb = p->tile_hint ? p->tile_hint : cb;
