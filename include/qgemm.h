@@ -104,9 +104,10 @@ typedef enum qgemm_scale_layout {
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
  *   slices (1..64) the chosen kernel uses; tile_hint: 0 = automatic, else for the decode
  *   kernel the number of 16-column blocks per workgroup (1 to 4), for the prefill
- *   kernel its square workgroup tile (128: 128 x 128, 256: 256 x 256).  Hints only change the work split and the reduction order of the fp32
- *   accumulation, never the packed layout; the automatic choice depends only on M, N, K
- *   and the formats (never on out_dtype or pointers).
+ *   kernel the rows of its workgroup tile (64: 64 x 128, 128: 128 x 128, 256: 256 x 256).
+ *   Hints only change the work split and the reduction order of the fp32 accumulation,
+ *   never the packed layout; the automatic choice depends only on M, N, K and the formats
+ *   (never on out_dtype or pointers).
  */
 typedef struct qgemm_problem {
   int64_t M, N, K;

@@ -41,7 +41,8 @@ BAD = [
     (dict(M=(1 << 24) + 1, N=256, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "M must be"),
     (dict(M=1, N=(1 << 24) + 16, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "N must be"),
     (dict(M=1, N=256, K=(1 << 24) + 128, fmt="int4"), q.ERR_INVALID_ARGUMENT, "K must be"),
-    (dict(M=4096, N=256, K=1 << 23, fmt="int4"), q.ERR_UNSUPPORTED, "prefill kernel needs"),
+    (dict(M=4096, N=256, K=1 << 24, fmt="int4"), q.ERR_UNSUPPORTED, "prefill kernel needs"),
+    (dict(M=4096, N=256, K=1 << 23, fmt="int4", tile_hint=128), q.ERR_UNSUPPORTED, "prefill kernel needs"),
     (dict(M=1, N=250, K=512, fmt="int4"), q.ERR_INVALID_ARGUMENT, "N must be"),
     (dict(M=1, N=256, K=500, fmt="int4"), q.ERR_INVALID_ARGUMENT, "K must be"),
     (dict(M=1, N=256, K=640, fmt="int4", group_size=256), q.ERR_INVALID_ARGUMENT, "multiple of group_size"),
@@ -159,6 +160,18 @@ def test_workspace_sizes_do_not_depend_on_out_dtype():
             a = q.workspace_bytes(q.problem(M, 8192, 8192, fmt))
             b = q.workspace_bytes(q.problem(M, 8192, 8192, fmt, out_dtype=o))
             assert a == b
+
+
+def test_prefill_tile_workspace_sizes():
+    # A split prefill needs one ticket per output tile (rounded to 256 bytes) plus one fp32
+    # partial tile per tile and slice; each tile shape gives its own count.
+    M, N, K = 600, 784, 1024
+    for tile, bn in ((64, 128), (128, 128), (256, 256)):
+        p = q.problem(M, N, K, "int4", kernel_hint=2, split_k_hint=3, tile_hint=tile)
+        tiles = -(-M // tile) * -(-N // bn)
+        assert q.workspace_bytes(p) == -(-tiles * 4 // 256) * 256 + tiles * 3 * tile * bn * 4, tile
+        p.split_k_hint = 1
+        assert q.workspace_bytes(p) == 0
 
 
 def test_pack_size_query():

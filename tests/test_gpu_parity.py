@@ -169,10 +169,11 @@ def test_decode_multi_run(q, fmt, G, M, N, K):
 
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int2", 32), ("nf4", 64), ("fp8", None),
                                    ("fp4", None)])
-@pytest.mark.parametrize("tile,split", [(128, 1), (128, 3), (256, 1), (256, 3)])
+@pytest.mark.parametrize("tile,split", [(64, 1), (64, 3), (128, 1), (128, 3), (256, 1), (256, 3)])
 def test_prefill_tile_shapes(q, fmt, G, tile, split):
-    # Both prefill workgroup shapes on every format: 600 rows are ragged against 128- and
-    # 256-row tiles, 784 columns (49 column blocks) against 256-column tiles; 8 k blocks.
+    # The three prefill workgroup shapes on every format: 600 rows are ragged against 64-,
+    # 128- and 256-row tiles, 784 columns (49 column blocks) against 128- and 256-column
+    # tiles; 8 k blocks.
     M, N, K = 600, 784, 1024
     say(f"case prefill-tile fmt={fmt} G={G} tile={tile} split={split}")
     prep = Prepared(q, fmt, N, K, G or 0, (53, N, K))
@@ -337,10 +338,12 @@ def test_nf4_any_code_book_bit_exact(q, hint, M):
 @pytest.mark.parametrize("fmt,G,M,N,K", [("int4", 128, 1000, 4048, 1024), ("fp8", None, 2000, 2560, 640),
                                          ("int4", 64, 520, 4096, 2048), ("fp4", None, 1024, 2048, 2048),
                                          ("int4", 256, 200, 2048, 1024), ("fp8h", None, 300, 4112, 512),
-                                         ("nf4", 128, 257, 1024, 2048)])
+                                         ("nf4", 128, 257, 1024, 2048), ("int4", 128, 17, 4096, 4096),
+                                         ("fp4", None, 64, 8192, 2048), ("int2", 32, 100, 2064, 1024),
+                                         ("fp8", None, 128, 3072, 1536)])
 def test_mid_m_auto_plan(q, fmt, G, M, N, K):
     # Shapes between decode and the large tiles, where the planner's time model picks the tile
-    # (128 x 128 or 256 x 256) and the K split; every row is checked.
+    # (64 x 128, 128 x 128 or 256 x 256) and the K split; every row is checked.
     say(f"case mid-m fmt={fmt} G={G} M={M} N={N} K={K}")
     prep = Prepared(q, fmt, N, K, G or 0, (61, N, K))
     A = _act(fmt, M, K, (61, M))

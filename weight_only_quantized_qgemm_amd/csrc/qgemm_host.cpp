@@ -107,9 +107,10 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
   const bool decode = p->kernel_hint == QGEMM_KERNEL_DECODE || (p->kernel_hint == QGEMM_KERNEL_AUTO && p->M <= 16);
   if (decode && (p->tile_hint < 0 || p->tile_hint > 4))
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the decode kernel must be 0 to 4, got %d", p->tile_hint);
-  if (!decode && p->tile_hint != 0 && p->tile_hint != pf_bm(kPfMedium) && p->tile_hint != pf_bm(kPfLarge))
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the prefill kernel must be 0, %d or %d, got %d",
-                pf_bm(kPfMedium), pf_bm(kPfLarge), p->tile_hint);
+  if (!decode && p->tile_hint != 0 && p->tile_hint != pf_bm(kPfSmall) && p->tile_hint != pf_bm(kPfMedium) &&
+      p->tile_hint != pf_bm(kPfLarge))
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "tile_hint for the prefill kernel must be 0, %d, %d or %d, got %d",
+                pf_bm(kPfSmall), pf_bm(kPfMedium), pf_bm(kPfLarge), p->tile_hint);
   return QGEMM_OK;
 }
 
@@ -212,15 +213,19 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // per slice by the workgroup that finishes each tile.  The medium tile does a quarter of
     // the large tile's work per k block in about 0.38 of its time, so it wins whenever it
     // fills the CUs and the large tile cannot (e.g. M = 512..1024 at N = 4096, or
-    // M = 2048 at N = 10240); the large one wins once both fill several rounds.
+    // M = 2048 at N = 10240); the large one wins once both fill several rounds.  The small
+    // tile does half the medium tile's work in about 0.62 of its time (the weight fragments
+    // it dequantizes are the same), so it wins where rows are few: M <= 64 always, and up to
+    // a few hundred rows when the medium tile would leave CUs idle or need a deep split.
+    // A tile is only a candidate when M exceeds the next smaller tile's rows.
     struct Cand { PfShape sh; double t_kb; };
-    const Cand cands[2] = {{kPfMedium, 1.3}, {kPfLarge, 3.4}};
+    const Cand cands[3] = {{kPfSmall, 0.8}, {kPfMedium, 1.3}, {kPfLarge, 3.4}};
     const double kFill = 3.0, kPartialLatency = 1.5, kBytesPerUs = 5.0e6;
     int best_c = -1, best = 1;
     double best_cost = 0.0;
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 3; ++c) {
       const PfShape sh = cands[c].sh;
-      if (p->tile_hint ? p->tile_hint != pf_bm(sh) : (c == 1 && p->M <= pf_bm(kPfMedium))) continue;
+      if (p->tile_hint ? p->tile_hint != pf_bm(sh) : (c > 0 && p->M <= pf_bm(cands[c - 1].sh))) continue;
       if ((int64_t)pf_bm(sh) * p->K * 2 > 0x7fffffffLL) continue;     // the A tile uses 32-bit offsets
       const int64_t mt = (p->M + pf_bm(sh) - 1) / pf_bm(sh), nt = (p->N + pf_bn(sh) - 1) / pf_bn(sh);
       for (int s = 1; s <= 64 && (s == 1 || s <= kblocks / 2); ++s) {
@@ -233,7 +238,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     }
     if (best_c < 0)
       return fail(QGEMM_ERR_UNSUPPORTED, "the prefill kernel needs %d * K * 2 < 2^31 (K = %lld)",
-                  p->tile_hint ? p->tile_hint : pf_bm(kPfMedium), (long long)p->K);
+                  p->tile_hint ? p->tile_hint : pf_bm(kPfSmall), (long long)p->K);
     pl->bm = pf_bm(cands[best_c].sh);
     pl->bn = pf_bn(cands[best_c].sh);
     const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;

@@ -11,7 +11,8 @@ namespace qgemm {
 // Prefill workgroup shapes: one row of eight wavefronts (two per SIMD), each owning
 // TM x TN MFMA tiles of 16 x 16.  The large shape amortises every dequantized weight
 // fragment over 16 row tiles; the medium one (small M) has a quarter of the area, so its
-// k steps are short and it keeps four A stages in flight instead of two.
+// k steps are short and it keeps four A stages in flight instead of two; the small one
+// (M up to a few hundred) halves the medium tile's rows again, doubling the workgroups.
 // RU: row tiles per LDS read unit; LA: units read ahead of the MFMAs that consume them;
 // ST: A stages in LDS (ST - 1 k blocks are loaded ahead of the one being computed).
 struct PfShape { int wgm, wgn, tm, tn, ru, la, st; };
@@ -19,8 +20,12 @@ struct PfShape { int wgm, wgn, tm, tn, ru, la, st; };
 #define QGEMM_PF_LARGE 1, 8, 16, 2, 4, 1, 2
 #define QGEMM_PF_MEDIUM 1, 8, 8, 1, 8, 1, 4
 #endif
+#ifndef QGEMM_PF_SMALL
+#define QGEMM_PF_SMALL 1, 8, 4, 1, 4, 1, 4
+#endif
 constexpr PfShape kPfLarge{QGEMM_PF_LARGE};    // 256 x 256 output tile
 constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 128 output tile
+constexpr PfShape kPfSmall{QGEMM_PF_SMALL};    // 64 x 128 output tile
 constexpr int pf_bm(PfShape s) { return 16 * s.wgm * s.tm; }
 constexpr int pf_bn(PfShape s) { return 16 * s.wgn * s.tn; }
 // Decode kernel: wavefronts per workgroup (with A staged in LDS, and whenever a workgroup
@@ -96,7 +101,7 @@ struct Plan {
   int nw;                 // decode: wavefronts per workgroup
   int nruns;              // decode: runs per wavefront share, pipelined when 2..4 (else 1)
   int lds_bytes;          // decode: dynamic LDS per workgroup (staged A, staged scales, wave tiles)
-  // prefill: workgroup tile (bm == pf_bm(kPfLarge) selects the large shape)
+  // prefill: workgroup tile (bm selects the shape: pf_bm of kPfSmall, kPfMedium or kPfLarge)
   int bm, bn;
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
   int splits;

@@ -263,9 +263,11 @@ void launch_shape(const Plan& pl, const KArgs& a, hipStream_t stream) {
 template <int FMT, int G>
 struct PrefillLauncher {
   static hipError_t run(const Plan& pl, const KArgs& a, hipStream_t stream) {
-    constexpr PfShape L = kPfLarge, S = kPfMedium;
+    constexpr PfShape L = kPfLarge, M = kPfMedium, S = kPfSmall;
     if (pl.bm == pf_bm(L))
       launch_shape<FMT, G, L.wgm, L.wgn, L.tm, L.tn, L.ru, L.la, L.st>(pl, a, stream);
+    else if (pl.bm == pf_bm(M))
+      launch_shape<FMT, G, M.wgm, M.wgn, M.tm, M.tn, M.ru, M.la, M.st>(pl, a, stream);
     else
       launch_shape<FMT, G, S.wgm, S.wgn, S.tm, S.tn, S.ru, S.la, S.st>(pl, a, stream);
     return hipGetLastError();
