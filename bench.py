@@ -10,7 +10,9 @@ The K timed steps are one HIP-graph replay; `value` is the effective weight band
 
 Also reported: a `roofline` object for the decode kernel, `secondary` numbers (per-shape
 decode timings and the M = 4096 prefill TFLOP/s over the group-size sweep), the CPU
-oracle timed on the host as `cpu_baseline`, and `comparators`: on the same shapes, the
+oracle timed on the host as `cpu_baseline`, `hbm_context` (torch's copy and a read-mostly
+elementwise kernel at the decode weight sizes and at 2 GiB: the HBM rate plain streaming
+kernels reach at those sizes), and `comparators`: on the same shapes, the
 vendor 16-bit GEMM (hipBLASLt through torch) on a resident 16-bit weight and the cast-copy
 path (whole weight dequantized into HBM by torch ops, then that GEMM) -- context, not
 target.  `--all` adds the FP8, FP4, FP8-with-fp16-activations, INT2 and NF4 workloads (and
@@ -109,6 +111,7 @@ def graph_of(torch, fn, n):
 
 def time_graph(torch, g, reps=1):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()                        # untimed: the first replay uploads the graph and first-touches buffers
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
@@ -116,6 +119,42 @@ def time_graph(torch, g, reps=1):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps        # ms
+
+
+def hbm_context(torch, sizes, rot_bytes):
+    """Achievable-HBM context for the decode figures: two torch elementwise kernels over
+    rotating buffers of the given byte counts, graph-timed like the GEMMs -- a copy (writes as
+    many bytes as it reads) and a nonzero test of int64 words into a bool mask (writes one byte
+    per eight read).  GB/s counts the bytes read.  These are vendor kernels, not the library's;
+    at a few MB they show how much of the spec peak launch and first-byte latency leave.  (No
+    reduction is used: torch's multi-block reductions record memsets, which stay out of graphs.)"""
+    res = []
+    for nbytes in sizes:
+        ncopies = max(2, -(-rot_bytes // nbytes))
+        src = [torch.ones(nbytes // 8, dtype=torch.int64, device="cuda") for _ in range(ncopies)]
+        dst = torch.empty_like(src[0])
+        mask = torch.empty(nbytes // 8, dtype=torch.bool, device="cuda")
+        row = {"bytes": nbytes}
+        for kind in ("copy", "read8"):
+            i = [0]
+
+            def fn():
+                x = src[i[0] % ncopies]
+                i[0] += 1
+                if kind == "copy":
+                    dst.copy_(x)
+                else:
+                    torch.ne(x, 0, out=mask)
+            n = 8 if nbytes > (256 << 20) else 64
+            gg = graph_of(torch, fn, n)
+            us = time_graph(torch, gg, 3) * 1e3 / n
+            row[f"{kind}_us"] = round(us, 3)
+            row[f"{kind}_read_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            del gg
+        res.append(row)
+        del src, dst, mask
+        torch.cuda.empty_cache()
+    return res
 
 
 def comparator_row(q, torch, fmt, M, N, K, G, key, rot_bytes, qgemm_us):
@@ -334,8 +373,10 @@ def main():
                           "weight_GBps": round(g.wbytes / (us * 1e-6) / 1e9, 1),
                           "frac_hbm": round(g.wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
         del gg
+    wsizes = sorted({g.wbytes for g in gemms})
     del gemms
     torch.cuda.empty_cache()
+    hbm = hbm_context(torch, [-(-b // 4096) * 4096 for b in wsizes] + [2 << 30], rot // 2)
 
     # vendor comparators on the decode shapes (hipBLASLt through torch; context, not target)
     comps = []
@@ -395,6 +436,7 @@ def main():
                      "kernel": "qgemm_decode (int4)", "avg_launch_us": round(avg_launch_us, 3),
                      "algorithmic_bytes_per_launch": avg_bytes},
         "cpu_baseline": cpu,
+        "hbm_context": hbm,
         "secondary": secondary,
         "comparators": comps,
     }
