@@ -23,6 +23,10 @@ namespace {
 // ahead) and dequantizes each once per K step, reusing it for its TM row tiles; the
 // dequantization of K step t + 1 is issued with the MFMAs of step t.  A fragments are
 // read from LDS in units of RU row tiles, LA units ahead of the MFMAs that consume them.
+// The weights enter each MFMA as its first operand and A as its second (both fragments
+// have the same lane map), so the MFMA computes the transposed 16 x 16 tile: lane l holds
+// output row l & 15, columns 4 (l >> 4) .. 4 (l >> 4) + 3, and the epilogue writes them
+// with one 8-byte (16-bit output) or 16-byte (fp32) store.
 // One barrier per k block: step k issues the weight loads of block k + 1, computes block k
 // while spreading the A DMA loads of block k + 1 over its first read units, waits for its
 // own loads and meets the other wavefronts at the barrier.  The
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
 #pragma unroll
       for (int r = 0; r < RU; ++r)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i0 + r][j] = mfma<FMT>(af[u % (LA + 1)][r], b[t & 1][j], acc[i0 + r][j]);
+        for (int j = 0; j < TN; ++j) acc[i0 + r][j] = mfma<FMT>(b[t & 1][j], af[u % (LA + 1)][r], acc[i0 + r][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -242,15 +246,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   for (int j = 0; j < TN; ++j) {
     const int nb = (n0 >> 4) + TN * wn + j;
     if (nb >= NB) continue;
-    const int n = nb * 16 + (lane & 15);
-    const float bv = bias_of(a, n);
+    const int n = nb * 16 + 4 * (lane >> 4);
+    const f32x4 bv = bias4_of(a, n);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * TM * wm + 16 * i + 4 * (lane >> 4) + r;
-        if (m < a.M) store_out(a, m, n, qgemm::group_scaled(FMT) ? v[TN * i + j][r] : v[TN * i + j][r] * alpha, bv);
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + 16 * TM * wm + 16 * i + (lane & 15);
+      f32x4 x = v[TN * i + j];
+      if constexpr (!qgemm::group_scaled(FMT)) {
+        x[0] *= alpha;
+        x[1] *= alpha;
+        x[2] *= alpha;
+        x[3] *= alpha;
       }
+      if (m < a.M) store_out4(a, m, n, x, bv);
+    }
   }
 }
 
