@@ -377,22 +377,28 @@ __device__ __forceinline__ f32x4 bias4_of(const KArgs& a, int n) {
   return f32x4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
 }
 
+// Four fp32 results (alpha already applied) plus their biases in fp32, each rounded once to
+// the 16-bit output type, packed in column order.
+__device__ __forceinline__ u32x2 pack4_out16(const KArgs& a, f32x4 v, f32x4 bias) {
+  const float v0 = v[0] + bias[0], v1 = v[1] + bias[1], v2 = v[2] + bias[2], v3 = v[3] + bias[3];
+  if (a.out_dtype == QGEMM_DT_F16) {
+    const f16x2 lo = {(_Float16)v0, (_Float16)v1}, hi = {(_Float16)v2, (_Float16)v3};
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  }
+  const bf16x2 lo = {(__bf16)v0, (__bf16)v1}, hi = {(__bf16)v2, (__bf16)v3};
+  return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
 // Columns n .. n + 3 of row m (n a multiple of 4; N is a multiple of 16 and out 16-byte
 // aligned, so the store is aligned): each fp32 result (alpha already applied) plus its bias
 // in fp32, rounded once to the output type, written with one 16- or 8-byte store.
 __device__ __forceinline__ void store_out4(const KArgs& a, int m, int n, f32x4 v, f32x4 bias) {
-  const float v0 = v[0] + bias[0], v1 = v[1] + bias[1], v2 = v[2] + bias[2], v3 = v[3] + bias[3];
   const size_t i = (size_t)m * a.N + n;
   if (a.out_dtype == QGEMM_DT_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + i) = f32x4{v0, v1, v2, v3};
-  } else if (a.out_dtype == QGEMM_DT_F16) {
-    const f16x2 lo = {(_Float16)v0, (_Float16)v1}, hi = {(_Float16)v2, (_Float16)v3};
-    *reinterpret_cast<u32x2*>(static_cast<_Float16*>(a.out) + i) =
-        u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + i) =
+        f32x4{v[0] + bias[0], v[1] + bias[1], v[2] + bias[2], v[3] + bias[3]};
   } else {
-    const bf16x2 lo = {(__bf16)v0, (__bf16)v1}, hi = {(__bf16)v2, (__bf16)v3};
-    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.out) + i) =
-        u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + i) = pack4_out16(a, v, bias);
   }
 }
 

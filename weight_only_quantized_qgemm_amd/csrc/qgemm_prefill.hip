@@ -242,24 +242,65 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     if (!splitk_finish<TM * TN, NT>(a, tile, split, BM * BN, true, v)) return;
   }
   const float alpha = qgemm::group_scaled(FMT) ? 1.0f : *a.alpha;
+  auto scaled = [&](f32x4 x) {
+    if constexpr (!qgemm::group_scaled(FMT)) {
+      x[0] *= alpha;
+      x[1] *= alpha;
+      x[2] *= alpha;
+      x[3] *= alpha;
+    }
+    return x;
+  };
+  if (a.out_dtype == QGEMM_DT_F32) {                 // fp32 output: 16-byte stores from the fragments
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int nb = (n0 >> 4) + TN * wn + j;
+      if (nb >= NB) continue;
+      const int n = nb * 16 + 4 * (lane >> 4);
+      const f32x4 bv = bias4_of(a, n);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + 16 * TM * wm + 16 * i + (lane & 15);
+        if (m < a.M) store_out4(a, m, n, scaled(v[TN * i + j]), bv);
+      }
+    }
+    return;
+  }
+
+  // 16-bit output: the tile goes through the (now idle) A stages in LDS, row-major, so that
+  // each store instruction writes whole rows.  Tile row R sits in stage R / RPA at row
+  // R % RPA; its 16-byte chunk c at position c ^ (R & 15), which keeps both the fragment
+  // writes (16 rows per instruction) and the row reads free of bank conflicts.
+  constexpr int OROW = BN * 2;                       // bytes of one output row of the tile
+  constexpr int OCH = OROW / 16;                     // 16-byte chunks per row
+  constexpr int RPA = BM * ROWB / OROW;              // tile rows per stage
+  constexpr int RPP = NT / OCH;                      // tile rows per store pass
+  static_assert(OCH >= 16 && RPA % 16 == 0 && (BM + RPA - 1) / RPA <= ST && BM % RPP == 0,
+                "the output tile must fit the A stages in whole swizzled rows");
+  __syncthreads();                                   // every wavefront is done reading A
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int nb = (n0 >> 4) + TN * wn + j;
-    if (nb >= NB) continue;
-    const int n = nb * 16 + 4 * (lane >> 4);
-    const f32x4 bv = bias4_of(a, n);
+    if (nb >= NB) continue;                          // never stored
+    const f32x4 bv = bias4_of(a, nb * 16 + 4 * (lane >> 4));
+    const int c = 2 * (TN * wn + j) + (lane >> 5);   // chunk of columns 4 (lane >> 4) ..
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = m0 + 16 * TM * wm + 16 * i + (lane & 15);
-      f32x4 x = v[TN * i + j];
-      if constexpr (!qgemm::group_scaled(FMT)) {
-        x[0] *= alpha;
-        x[1] *= alpha;
-        x[2] *= alpha;
-        x[3] *= alpha;
-      }
-      if (m < a.M) store_out4(a, m, n, x, bv);
+      const int R = 16 * TM * wm + 16 * i + (lane & 15);
+      unsigned char* row = stage(R / RPA) + (R % RPA) * OROW;
+      *reinterpret_cast<u32x2*>(row + 16 * (c ^ (R & 15)) + 8 * ((lane >> 4) & 1)) =
+          pack4_out16(a, scaled(v[TN * i + j]), bv);
     }
+  }
+  __syncthreads();
+  const int c = threadIdx.x % OCH;
+  const bool col_ok = (n0 >> 4) + (c >> 1) < NB;     // a 16-column block is two chunks
+  unsigned char* out = static_cast<unsigned char*>(a.out) + (size_t)n0 * 2 + 16 * c;
+#pragma unroll
+  for (int p = 0; p < BM / RPP; ++p) {
+    const int R = p * RPP + threadIdx.x / OCH;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(stage(R / RPA) + (R % RPA) * OROW + 16 * (c ^ (R & 15)));
+    if (col_ok && m0 + R < a.M) *reinterpret_cast<u32x4*>(out + (size_t)(m0 + R) * a.N * 2) = x;
   }
 }
 
