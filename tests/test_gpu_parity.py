@@ -240,6 +240,29 @@ def test_int4_closed_form_equal_nibbles_unit_scales(q):
             tolerance.check_e1_e2(y, want)
 
 
+@pytest.mark.parametrize("fmt", ["int4", "fp8"])
+@pytest.mark.parametrize("M,hint,tile,split", [(5, 1, 0, 1), (16, 1, 0, 3), (100, 2, 64, 1), (100, 2, 128, 2),
+                                               (300, 2, 256, 1), (300, 2, 64, 3)])
+@pytest.mark.parametrize("f32", [False, True])
+def test_writes_stay_inside_the_output(q, fmt, M, hint, tile, split, f32):
+    # The output handed over is the first M rows of a larger buffer whose remaining rows hold
+    # sentinels: no kernel (decode, each prefill tile, split or not, 16-bit or fp32 output)
+    # may write past row M - 1; N = 272 is ragged against every column tile.
+    N, K = 272, 1024
+    say(f"case bounds fmt={fmt} M={M} hint={hint} tile={tile} split={split} f32={f32}")
+    prep = Prepared(q, fmt, N, K, _g(fmt), (63, N, K))
+    A = _act(fmt, M, K, (63, M)).cuda()
+    dt = torch.float32 if f32 else (torch.float16 if out16_kind(fmt) == "f16" else torch.bfloat16)
+    odt = q.DT_F32 if f32 else out16_dtype(q, fmt)
+    buf = torch.full((M + 80, N), -3.0, dtype=dt, device="cuda")
+    p = q.problem(M, N, K, fmt, group_size=_g(fmt) or None, out_dtype=odt, kernel_hint=hint,
+                  split_k_hint=split, tile_hint=tile)
+    q.run(p, A, prep.w, prep.s, None if fmt == "int4" else prep.alpha_t, buf[:M], q.alloc_workspace(p))
+    torch.cuda.synchronize()
+    assert bool((buf[M:] == -3.0).all())
+    assert bool(torch.isfinite(buf[:M]).all()) and not bool((buf[:M] == -3.0).all())
+
+
 @pytest.mark.parametrize("fmt", ["int4", "nf4", "fp8", "fp4"])
 def test_empty_m_enqueues_nothing(q, fmt):
     # M = 0 is an empty product: the call succeeds and writes nothing (the output buffer
@@ -269,21 +292,23 @@ def test_long_k(q, fmt, G, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["int4", "int2", "nf4", "fp8", "fp8h", "fp4"])
-@pytest.mark.parametrize("M,hint,split", [(1, 0, 0), (16, 0, 3), (33, 0, 0), (300, 2, 2)])
-def test_bias_epilogue(q, fmt, M, hint, split):
+@pytest.mark.parametrize("M,hint,split,tile", [(1, 0, 0, 0), (16, 0, 3, 0), (33, 0, 0, 0), (300, 2, 2, 0),
+                                              (600, 2, 1, 256), (200, 2, 3, 64)])
+def test_bias_epilogue(q, fmt, M, hint, split, tile):
     # qgemm_run_bias: out = A . dequant(W) (* alpha) + bias[n], the bias added in fp32 after
     # alpha and rounded once with the rest (mm_bf16_fp8 / mm_fp16_fp8 bias argument).
+    # N = 272 columns are ragged against the 128- and 256-column prefill tiles.
     import torch as T
     N, K = 272, 1024
-    say(f"case bias fmt={fmt} M={M} hint={hint} split={split}")
+    say(f"case bias fmt={fmt} M={M} hint={hint} split={split} tile={tile}")
     prep = Prepared(q, fmt, N, K, _g(fmt), (57, N, K))
     A = _act(fmt, M, K, (57, M))
     b = synthetic.bias(N, out16_kind(fmt), (57, N))
-    check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, bias=b)
+    check_against_oracle(q, prep, A, kernel_hint=hint, split_k_hint=split, tile_hint=tile, bias=b)
     # zero activations: the output is exactly the bias in every row (both output types)
-    y32, _ = run_gpu(q, prep, T.zeros_like(A), q.DT_F32, hint, split, bias=b)
+    y32, _ = run_gpu(q, prep, T.zeros_like(A), q.DT_F32, hint, split, bias=b, tile_hint=tile)
     assert np.array_equal(y32, np.tile(b.to(T.float64).numpy(), (M, 1)))
-    y16, _ = run_gpu(q, prep, T.zeros_like(A), out16_dtype(q, fmt), hint, split, bias=b)
+    y16, _ = run_gpu(q, prep, T.zeros_like(A), out16_dtype(q, fmt), hint, split, bias=b, tile_hint=tile)
     assert np.array_equal(y16, np.tile(b.view(T.int16).numpy().view(np.uint16), (M, 1)))
 
 
