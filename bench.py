@@ -241,25 +241,38 @@ def cpu_baseline(budget_s=12.0):
         threads = 1
     wi = synthetic.WORKLOAD_INDEX["int4_decode"]
     prepared = []
+    quant_s = 0.0
     for si, (M, N, K) in enumerate(DECODE_SHAPES):
         w = synthetic.weights(N, K, 0.02, (wi, si))
+        tq = time.perf_counter()
         codes, sbits = quant.quantize_int4(w, 128)
+        quant_s += time.perf_counter() - tq
         a = synthetic.activations(M, K, "f16", (wi, si)).float().numpy()
-        prepared.append((codes, sbits, a, weight_bytes("int4", N, K, 128)))
+        prepared.append((codes, sbits, a, weight_bytes("int4", N, K, 128), 2.0 * M * N * K))
     t0 = time.perf_counter()
-    done_bytes, steps = 0, 0
+    done_bytes, done_flops, steps = 0, 0.0, 0
     while True:
-        for codes, sbits, a, nb in prepared:
+        for codes, sbits, a, nb, fl in prepared:
             wdq = reference.dequant_int4(codes, sbits, 128)
             reference.gemm_fp64(a, wdq)
             done_bytes += nb
+            done_flops += fl
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 20:
             break
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} full decode steps (4 GEMMs each: fp32 dequant + fp64 matmul), "
-                      f"{el:.1f} s, host cores available {len(os.sched_getaffinity(0))}"}
+                      f"{el:.1f} s, host cores available {len(os.sched_getaffinity(0))}",
+            "seconds": round(el, 3), "gflops": round(done_flops / el / 1e9, 3), "blas_threads": int(threads),
+            "cpu_model": model, "quantize_s": round(quant_s, 3),
+            "quantize_note": "oracle INT4 quantizer (absmax/7, group 128) over the four weights, outside the timed loop"}
 
 
 def main():
