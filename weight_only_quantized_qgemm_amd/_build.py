@@ -23,6 +23,8 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments (up to 16 SGPRs) arrive preloaded in registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
 ]
 
