@@ -174,6 +174,16 @@ def test_prefill_tile_workspace_sizes():
         assert q.workspace_bytes(p) == 0
 
 
+def test_prefill_rows_up_to_64_use_the_64_row_tile():
+    # With M <= 64 only the 64 x 128 tile is a candidate (a taller one would compute padding
+    # rows only): the split workspace has that tile's geometry for any format and split.
+    for fmt, M, N, K in (("int4", 17, 4096, 4096), ("fp8", 64, 10240, 5120), ("fp4", 33, 8192, 8192)):
+        for s in (2, 5):
+            p = q.problem(M, N, K, fmt, kernel_hint=2, split_k_hint=s)
+            tiles = -(-N // 128)
+            assert q.workspace_bytes(p) == -(-tiles * 4 // 256) * 256 + tiles * s * 64 * 128 * 4, (fmt, M, s)
+
+
 def test_pack_size_query():
     assert q.packed_sizes(q.problem(1, 256, 512, "int4")) == (256 * 256, 256 * 4 * 2)
     assert q.packed_sizes(q.problem(1, 256, 512, "int4", group_size=32)) == (256 * 256, 256 * 16 * 2)
