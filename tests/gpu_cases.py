@@ -84,11 +84,6 @@ def run_gpu(q, prep, A16, out_dtype, kernel_hint=0, split_k_hint=0, workspace=No
     return o.view(torch.int16).numpy().view(np.uint16), workspace
 
 
-def ref_rows(prep, A16, rows, bias=None):
-    b = None if bias is None else a_values(bias)
-    return reference.gemm_fp64_rows(a_values(A16), prep.wdq, rows, prep.alpha, b)
-
-
 def out16_kind(fmt):
     return "f16" if fmt in ("int4", "int2", "nf4", "fp8h") else "bf16"
 
@@ -101,14 +96,32 @@ def out16_values(bits, fmt):
     return codecs.f16_from_bits(bits) if out16_kind(fmt) == "f16" else codecs.bf16_from_bits(bits)
 
 
-def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0, tile_hint=0, bias=None):
-    """E1/E2 on the fp32 output, E2 on the 16-bit output, E3 between them."""
+def check_against_oracle(q, prep, A16, rows=None, kernel_hint=0, split_k_hint=0, tile_hint=0, bias=None,
+                         chunk=2048):
+    """E1/E2 on the fp32 output, E2 on the 16-bit output, E3 between them, over every row
+    (or the given rows): the fp64 reference is formed in row chunks and the chunk
+    statistics are combined, so full-size outputs are compared element by element.  E3
+    also requires every element of both outputs to be finite (outputs start as NaN, so an
+    output tile that no workgroup wrote fails here)."""
     M = A16.shape[0]
     rows = np.arange(M) if rows is None else np.asarray(rows)
     y32, ws = run_gpu(q, prep, A16, q.DT_F32, kernel_hint, split_k_hint, tile_hint=tile_hint, bias=bias)
-    r = ref_rows(prep, A16, rows, bias)
-    st = tolerance.check_e1_e2(y32[rows], r)
     y16, _ = run_gpu(q, prep, A16, out16_dtype(q, prep.fmt), kernel_hint, split_k_hint, ws, tile_hint, bias=bias)
     tolerance.check_e3(y16, y32.astype(np.float32), out16_kind(prep.fmt))
-    tolerance.check_e2(out16_values(y16[rows], prep.fmt), r)
+    a = a_values(A16)
+    w = np.asarray(prep.wdq, dtype=np.float64)
+    b = None if bias is None else a_values(bias)
+    parts32, parts16 = [], []
+    for i in range(0, len(rows), chunk):
+        rr = rows[i:i + chunk]
+        r = reference.gemm_fp64(a[rr], w, prep.alpha, b)
+        parts32.append(tolerance.error_stats(y32[rr], r))
+        parts16.append(tolerance.error_stats(out16_values(y16[rr], prep.fmt), r))
+    st = tolerance.combine_stats(parts32)
+    if not tolerance.gates_pass(st):
+        raise AssertionError(f"tolerance gates failed on the fp32 output: {st}")
+    st16 = tolerance.combine_stats(parts16)
+    if st16["nonfinite"] or st16["E2_fail_count"]:
+        raise AssertionError(f"E2 failed on the 16-bit output: {st16}")
+    st["rows_checked"] = int(len(rows))
     return st, y32

@@ -14,8 +14,8 @@ import pytest
 
 import comparators
 import synthetic
-from gpu_cases import Prepared, oracle_weights, out16_dtype, out16_values, ref_rows, run_gpu, say
-from oracle import tolerance
+from gpu_cases import Prepared, a_values, oracle_weights, out16_dtype, out16_values, run_gpu, say
+from oracle import reference, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -51,8 +51,7 @@ def test_kernel_error_within_tol_mult_of_cast_copy(q, name, fmt, si, shape, G):
     prep = Prepared(q, fmt, N, K, G, (wi, si))
     kind = "f16" if fmt in ("int4", "fp8h") else "bf16"
     A = synthetic.activations(M, K, kind, (wi, si))
-    rows = np.arange(M)
-    r = ref_rows(prep, A, rows)
+    r = reference.gemm_fp64(a_values(A), prep.wdq, prep.alpha)
     y16, _ = run_gpu(q, prep, A, out16_dtype(q, fmt))
     yk = out16_values(y16, fmt)
     canon, scales, alpha, _ = oracle_weights(fmt, N, K, G, (wi, si))
