@@ -227,10 +227,27 @@ qgemm_status_t qgemm_run_bias(const qgemm_problem_t* problem, const void* A, con
                               const void* s_packed, const float* alpha, const void* bias, void* out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static text for a status code. */
+/*
+ * qgemm_status_string -- static, NUL-terminated name of a status code ("QGEMM_OK",
+ * "QGEMM_ERR_MISALIGNED", ...; "QGEMM_ERR_UNKNOWN_STATUS" for a value outside the enum).
+ * The pointer is owned by the library and valid for the life of the process.  Status codes
+ * follow the FlashInfer PR #4466 analysis, section 2 (preparation and dispatch): a dtype or
+ * backend combination the kernels do not implement is refused explicitly
+ * (QGEMM_ERR_UNSUPPORTED, the analogue of its NotImplementedError) instead of falling back
+ * to another path, and section 1 (input validation): every shape, dtype and pointer check
+ * happens on the host before launch.
+ */
 const char* qgemm_status_string(qgemm_status_t status);
 
-/* Thread-local detail of the last error returned on this thread ("" if none). */
+/*
+ * qgemm_last_error -- detail text of the last error an entry point returned on the calling
+ * thread ("" after a call that succeeded).  The text names the offending argument, the
+ * value received and the value expected (e.g. which a_dtype / out_dtype a weight format
+ * needs), after the validation messages of the FlashInfer PR #4466 analysis, section 1,
+ * which name the expected dtype and the call that produces a correctly laid-out operand.
+ * The pointer is owned by the library (thread-local storage) and stays valid until the next
+ * qgemm_* call on the same thread.
+ */
 const char* qgemm_last_error(void);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
