@@ -3,20 +3,24 @@
 A step is one pass of the decode workload the headline metric is quoted on: W4A16 with
 fp16 activations, int4 weights in groups of 128 along K with fp16 scales, and the four
 GEMMs M in {1, 16} x (N, K) in {(4096, 4096), (11008, 4096)}.  Every launch reads a
-different copy of the packed weights (rotating copies, > 1 GB between two reads of the
-same copy), so the weight stream comes from HBM, not from the 256 MB last-level cache.
-The K timed steps are one HIP-graph replay; `value` is the effective weight bandwidth
-(packed weight + scale bytes / time) over them.
+different copy of the packed weights (rotating copies, >= 512 MB per shape, more than the
+256 MB last-level cache), so the weight stream comes from HBM.  The K timed steps are one
+HIP-graph replay; `value` is the effective weight bandwidth (packed weight + scale bytes /
+time) over them.
 
-Also reported: a `roofline` object for the decode kernel, `secondary` numbers (per-shape
-decode timings and the M = 4096 prefill TFLOP/s over the group-size sweep), the CPU
-oracle timed on the host as `cpu_baseline`, `hbm_context` (torch's copy and a read-mostly
-elementwise kernel at the decode weight sizes and at 2 GiB: the HBM rate plain streaming
-kernels reach at those sizes), and `comparators`: on the same shapes, the
-vendor 16-bit GEMM (hipBLASLt through torch) on a resident 16-bit weight and the cast-copy
-path (whole weight dequantized into HBM by torch ops, then that GEMM) -- context, not
-target.  `--all` adds the FP8, FP4, FP8-with-fp16-activations, INT2 and NF4 workloads (and
-comparators for the FP8 / FP4 shapes and the INT4 prefill).
+Also reported: a `roofline` object for the decode kernel; `secondary`, every other
+workload shape timed the same way (rotating >= 512 MB of weight copies): the INT4 prefill
+M = 4096 over the group-size sweep, the FP8 shapes (M = 1, 16, 8192 x 10240 x 5120,
+32768 x 3200 x 5120, 16384 x 12800 x 5120) and the FP4 shapes (M = 1, 128, 8192 x 8192 x 8192),
+each with TFLOP/s and weight GB/s as fractions of the MFMA and HBM peaks; the CPU oracle
+timed on the host as `cpu_baseline`; `hbm_context`, a hand-written streaming-read kernel
+(non-temporal 16-byte loads, no arithmetic) over the decode weight and scale byte counts
+and over 2 GiB, the time a kernel needs just to read those bytes; `host_overhead`, host
+time per qgemm_run call (validation, plan, launch); and `comparators`: on the decode
+shapes, the vendor 16-bit GEMM (hipBLASLt through torch) on a resident 16-bit weight and
+the cast-copy path (whole weight dequantized into HBM by torch ops, then that GEMM) --
+context, not target.  `--all` adds FP8 with fp16 activations and a bias, INT2 and NF4,
+and comparators for the FP8 / FP4 shapes and the INT4 prefill.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
 """
@@ -82,6 +86,8 @@ class Gemm:
         self.ws = q.alloc_workspace(self.p)
         self.i = 0
         self.q = q
+        self.label = (f"{fmt} M={M} N={N} K={K}" + (f" G={G}" if fmt in q.GROUP_SCALED else "")
+                      + (" +bias" if with_bias else ""))
 
     def launch(self):
         c = self.i % len(self.w)
@@ -92,6 +98,23 @@ class Gemm:
     @property
     def flops(self):
         return 2.0 * self.M * self.N * self.K
+
+
+def measure(torch, g, n):
+    """Graph of n launches of one GEMM (each on the next weight copy), timed over 3 replays
+    after a warm one: time per launch, TFLOP/s and weight GB/s with their fractions of the
+    MFMA and HBM peaks, and which of the two bounds the shape (the larger ideal time)."""
+    gg = graph_of(torch, g.launch, n)
+    us = time_graph(torch, gg, 3) * 1e3 / n
+    del gg
+    tf = g.flops / (us * 1e-6) / 1e12
+    gbs = g.wbytes / (us * 1e-6) / 1e9
+    t_mfma = g.flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    t_hbm = g.wbytes / (HBM_PEAK_GBS * 1e9)
+    return {"gemm": g.label, "us_per_launch": round(us, 3), "TFLOPs": round(tf, 1),
+            "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "weight_GBps": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bound": "mfma" if t_mfma > t_hbm else "hbm",
+            "frac_bound": round(max(t_mfma, t_hbm) / (us * 1e-6), 4), "weight_copies": len(g.w)}
 
 
 def graph_of(torch, fn, n):
@@ -121,40 +144,85 @@ def time_graph(torch, g, reps=1):
     return e0.elapsed_time(e1) / reps        # ms
 
 
-def hbm_context(torch, sizes, rot_bytes):
-    """Achievable-HBM context for the decode figures: two torch elementwise kernels over
-    rotating buffers of the given byte counts, graph-timed like the GEMMs -- a copy (writes as
-    many bytes as it reads) and a nonzero test of int64 words into a bool mask (writes one byte
-    per eight read).  GB/s counts the bytes read.  These are vendor kernels, not the library's;
-    at a few MB they show how much of the spec peak launch and first-byte latency leave.  (No
-    reduction is used: torch's multi-block reductions record memsets, which stay out of graphs.)"""
+def _probe_lib():
+    """The measurement helpers built next to libqgemm.so (streaming read, host time per call)."""
+    import ctypes
+    import weight_only_quantized_qgemm_amd as q
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(q.LIB_PATH), "libqgemm_probe.so"))
+    vp, ll = ctypes.c_void_p, ctypes.c_longlong
+    lib.qgemm_probe_stream.argtypes = [vp, ll, vp, ll, vp, ctypes.c_int, vp]
+    lib.qgemm_probe_stream.restype = ctypes.c_int
+    lib.qgemm_probe_stream_groups.argtypes = [ll, ctypes.c_int]
+    lib.qgemm_probe_stream_groups.restype = ll
+    lib.qgemm_probe_host_ns.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_double)]
+    lib.qgemm_probe_host_ns.restype = ctypes.c_int
+    return lib
+
+
+def hbm_context(torch, cases, rot_bytes):
+    """Achievable-HBM context for the decode figures: a hand-written streaming-read kernel
+    (non-temporal 16-byte loads, all of a thread's loads in flight before any is consumed,
+    one XOR per workgroup stored) over rotating buffers of the given byte counts, graph-timed
+    like the GEMMs.  cases: (label, weight bytes, scale bytes); with scale bytes > 0 the
+    kernel reads a second buffer of that size in the same launch, like the decode kernel's
+    scale stream.  Loads per thread U in {2, 4, 8} are each timed and the fastest is
+    reported.  GB/s counts the bytes read."""
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
     res = []
-    for nbytes in sizes:
+    for label, wbytes, sbytes in cases:
+        nbytes = wbytes + sbytes
         ncopies = max(2, -(-rot_bytes // nbytes))
-        src = [torch.ones(nbytes // 8, dtype=torch.int64, device="cuda") for _ in range(ncopies)]
-        dst = torch.empty_like(src[0])
-        mask = torch.empty(nbytes // 8, dtype=torch.bool, device="cuda")
-        row = {"bytes": nbytes}
-        for kind in ("copy", "read8"):
+        src = [torch.ones(wbytes // 8, dtype=torch.int64, device="cuda") for _ in range(ncopies)]
+        sc = [torch.ones(max(sbytes, 16) // 8, dtype=torch.int64, device="cuda") for _ in range(ncopies)]
+        sink = torch.empty(int(lib.qgemm_probe_stream_groups(wbytes // 16, 1)) + 64, dtype=torch.int32,
+                           device="cuda")
+        best = None
+        for U in (2, 4, 8):
             i = [0]
 
             def fn():
-                x = src[i[0] % ncopies]
+                c = i[0] % ncopies
                 i[0] += 1
-                if kind == "copy":
-                    dst.copy_(x)
-                else:
-                    torch.ne(x, 0, out=mask)
+                st = lib.qgemm_probe_stream(src[c].data_ptr(), wbytes, sc[c].data_ptr() if sbytes else None,
+                                            sbytes, sink.data_ptr(), U, torch.cuda.current_stream().cuda_stream)
+                assert st == 0, f"streaming probe failed: {st}"
             n = 8 if nbytes > (256 << 20) else 64
             gg = graph_of(torch, fn, n)
             us = time_graph(torch, gg, 3) * 1e3 / n
-            row[f"{kind}_us"] = round(us, 3)
-            row[f"{kind}_read_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
             del gg
-        res.append(row)
-        del src, dst, mask
+            if best is None or us < best[0]:
+                best = (us, U)
+        res.append({"case": label, "bytes": nbytes, "weight_bytes": wbytes, "scale_bytes": sbytes,
+                    "stream_us": round(best[0], 3), "loads_per_thread": best[1],
+                    "read_GBps": round(nbytes / (best[0] * 1e-6) / 1e9, 1)})
+        del src, sc, sink
         torch.cuda.empty_cache()
+    del stream
     return res
+
+
+def host_overhead(q, torch, gemms, iters=2000):
+    """Host microseconds per call, measured in C (no Python overhead): qgemm_workspace_bytes
+    (validation + launch plan) and qgemm_run (validation, plan and the kernel launch)."""
+    import ctypes
+    lib = _probe_lib()
+    rows = []
+    for g in gemms:
+        ns = (ctypes.c_double * 2)()
+        alpha = None if g.fmt in q.GROUP_SCALED else g.alpha.data_ptr()
+        ws = None if g.ws is None else g.ws.data_ptr()
+        wsb = 0 if g.ws is None else g.ws.numel()
+        n = iters if g.M <= 16 else 20
+        st = lib.qgemm_probe_host_ns(ctypes.addressof(g.p), g.A.data_ptr(), g.w[0].data_ptr(),
+                                     None if g.s[0] is None else g.s[0].data_ptr(), alpha, g.out.data_ptr(),
+                                     ws, wsb, torch.cuda.current_stream().cuda_stream, n, ns)
+        torch.cuda.synchronize()
+        assert st == 0, q.last_error()
+        rows.append({"gemm": g.label, "validate_plan_us": round(ns[0] / 1e3, 3),
+                     "qgemm_run_us": round(ns[1] / 1e3, 3), "calls": n})
+    return rows
 
 
 def comparator_row(q, torch, fmt, M, N, K, G, key, rot_bytes, qgemm_us):
@@ -281,7 +349,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true",
-                    help="also time the FP8, FP4, FP8-with-fp16-activations (+bias) and INT2 workloads")
+                    help="also time the FP8-with-fp16-activations (+bias), INT2 and NF4 workloads and the "
+                         "comparators of the FP8 / FP4 shapes and the INT4 prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--counter-pass", nargs="?", const="decode", choices=("decode", "prefill"),
@@ -320,7 +389,7 @@ def main():
         for name, si, G in (("int4_prefill", 0, 128), ("fp8", 2, 0), ("fp4", 2, 0)):
             wk = synthetic.WORKLOADS[name]
             M, N, K = wk["shapes"][si]
-            g = Gemm(q, torch, wk["fmt"], M, N, K, G, (synthetic.WORKLOAD_INDEX[name], si), 64 << 20)
+            g = Gemm(q, torch, wk["fmt"], M, N, K, G, (synthetic.WORKLOAD_INDEX[name], si), rot // 2)
             for _ in range(3):
                 g.launch()
             torch.cuda.synchronize()
@@ -376,20 +445,14 @@ def main():
     del graph
 
     # per-shape breakdown (graphs of one GEMM repeated; not part of the timed steps)
-    secondary = []
-    for g in gemms:
-        n = 64
-        gg = graph_of(torch, g.launch, n)
-        ms = time_graph(torch, gg, 3)
-        us = ms * 1e3 / n
-        secondary.append({"gemm": f"int4 M={g.M} N={g.N} K={g.K} G=128", "us_per_launch": round(us, 3),
-                          "weight_GBps": round(g.wbytes / (us * 1e-6) / 1e9, 1),
-                          "frac_hbm": round(g.wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
-        del gg
-    wsizes = sorted({g.wbytes for g in gemms})
+    secondary = [measure(torch, g, 64) for g in gemms]
+    host = host_overhead(q, torch, gemms[:2], iters=500)
+    hcases = [(f"int4 N={g.N} K={g.K}", g.wbytes - g.s[0].numel(), g.s[0].numel()) for g in gemms[::2]]
+    hcases = [(lab + " weights", w, 0) for lab, w, _ in hcases] + [(lab + " weights+scales", w, sb)
+                                                                   for lab, w, sb in hcases]
     del gemms
     torch.cuda.empty_cache()
-    hbm = hbm_context(torch, [-(-b // 4096) * 4096 for b in wsizes] + [2 << 30], rot // 2)
+    hbm = hbm_context(torch, hcases + [("2 GiB", 2 << 30, 0)], rot // 2)
 
     # vendor comparators on the decode shapes (hipBLASLt through torch; context, not target)
     comps = []
@@ -397,42 +460,34 @@ def main():
         comps.append(comparator_row(q, torch, "int4", M, N, K, 128, (wi, si), rot // 2,
                                     secondary[si]["us_per_launch"]))
 
-    # prefill M = 4096 over the group-size sweep (TFLOP/s)
+    # every other workload shape, each on >= rot / 2 bytes of rotating weight copies: the INT4
+    # prefill over the group-size sweep, the FP8 and FP4 layer shapes (and with --all the FP8
+    # fp16-activation + bias, INT2 and NF4 workloads)
     wi2 = synthetic.WORKLOAD_INDEX["int4_prefill"]
     for G in PREFILL_G:
-        g = Gemm(q, torch, "int4", 4096, 4096, 4096, G, (wi2, 0), 64 << 20)
-        gg = graph_of(torch, g.launch, 20)
-        ms = time_graph(torch, gg, 3) / 20
-        tf = g.flops / (ms * 1e-3) / 1e12
-        secondary.append({"gemm": f"int4 M=4096 N=4096 K=4096 G={G}", "us_per_launch": round(ms * 1e3, 2),
-                          "TFLOPs": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+        log(f"bench: int4 prefill G={G}")
+        g = Gemm(q, torch, "int4", 4096, 4096, 4096, G, (wi2, 0), rot // 2)
+        secondary.append(measure(torch, g, 20))
+        if G == 128:
+            host += host_overhead(q, torch, [g], iters=20)
         if args.all and G == 128:
-            comps.append(comparator_row(q, torch, "int4", 4096, 4096, 4096, G, (wi2, 0), 64 << 20, ms * 1e3))
-        del gg, g
+            comps.append(comparator_row(q, torch, "int4", 4096, 4096, 4096, G, (wi2, 0), rot // 2,
+                                        secondary[-1]["us_per_launch"]))
+        del g
         torch.cuda.empty_cache()
-
-    if args.all:
-        for name in ("fp8", "fp4", "fp8h", "int2", "nf4"):
-            wk = synthetic.WORKLOADS[name]
-            wix = synthetic.WORKLOAD_INDEX[name]
-            for si, (M, N, K) in enumerate(wk["shapes"]):
-                big = M >= 128
-                g = Gemm(q, torch, name, M, N, K, wk["group_sizes"][0], (wix, si), (64 << 20) if big else rot,
-                         with_bias=name == "fp8h")
-                n = 10 if big else 64
-                gg = graph_of(torch, g.launch, n)
-                ms = time_graph(torch, gg, 3) / n
-                tf = g.flops / (ms * 1e-3) / 1e12
-                gbs = g.wbytes / (ms * 1e-3) / 1e9
-                label = f"{name} M={M} N={N} K={K}" + (" +bias" if name == "fp8h" else "")
-                secondary.append({"gemm": label, "us_per_launch": round(ms * 1e3, 2),
-                                  "TFLOPs": round(tf, 1), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                  "weight_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
-                del gg, g
-                torch.cuda.empty_cache()
-                if name in ("fp8", "fp4", "fp8h"):
-                    comps.append(comparator_row(q, torch, name, M, N, K, 0, (wix, si),
-                                                (64 << 20) if big else rot, ms * 1e3))
+    names = ("fp8", "fp4") + (("fp8h", "int2", "nf4") if args.all else ())
+    for name in names:
+        wk = synthetic.WORKLOADS[name]
+        wix = synthetic.WORKLOAD_INDEX[name]
+        for si, (M, N, K) in enumerate(wk["shapes"]):
+            log(f"bench: {name} M={M} N={N} K={K}")
+            g = Gemm(q, torch, name, M, N, K, wk["group_sizes"][0], (wix, si), rot // 2, with_bias=name == "fp8h")
+            secondary.append(measure(torch, g, 10 if M >= 128 else 64))
+            del g
+            torch.cuda.empty_cache()
+            if args.all and name in ("fp8", "fp4", "fp8h"):
+                comps.append(comparator_row(q, torch, name, M, N, K, 0, (wix, si), rot // 2,
+                                            secondary[-1]["us_per_launch"]))
 
     cpu = None if args.no_cpu else cpu_baseline()
 
@@ -450,6 +505,7 @@ def main():
                      "algorithmic_bytes_per_launch": avg_bytes},
         "cpu_baseline": cpu,
         "hbm_context": hbm,
+        "host_overhead": host,
         "secondary": secondary,
         "comparators": comps,
     }

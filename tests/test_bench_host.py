@@ -35,3 +35,17 @@ def test_recorded_traffic_follows_the_kernel_sources(monkeypatch):
     # a different decode source hash makes the recorded counters stale
     monkeypatch.setattr(bench, "kernel_sha", lambda kind: "0" * 16)
     assert bench.recorded_traffic() is None
+
+
+def test_measurement_library_loads_and_sizes_the_stream_grid():
+    # the streaming-read and host-timing helpers live in their own library next to libqgemm.so
+    lib = bench._probe_lib()
+    for name in ("qgemm_probe_stream", "qgemm_probe_stream_groups", "qgemm_probe_host_ns"):
+        assert hasattr(lib, name)
+    # 8 MiB of 16-byte chunks with 4 loads per thread of 512 threads: 256 workgroups
+    assert lib.qgemm_probe_stream_groups((8 << 20) // 16, 4) == 256
+    assert lib.qgemm_probe_stream_groups(1, 8) == 1
+    # bad arguments are refused on the host, before any launch (no GPU needed)
+    assert lib.qgemm_probe_stream(None, 1024, None, 0, None, 4, None) == -1
+    assert lib.qgemm_probe_stream(16, 1000, None, 0, 16, 4, None) == -1       # not a multiple of 16
+    assert lib.qgemm_probe_stream(16, 1024, None, 0, 16, 3, None) == -1       # U not offered

@@ -11,6 +11,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemm.so")
+# measurement helpers for the benchmark (streaming-read kernel, host time per call): a library
+# of their own, outside the qgemm ABI
+PROBE_LIB = os.path.join(PKG, "libqgemm_probe.so")
 # Weight formats (the Format enum of csrc/qgemm_internal.h).  Each kernel source is compiled
 # once per format (-DQGEMM_FMT_UNIT), so the many kernel instances build in parallel.
 N_FORMATS = 6
@@ -57,9 +60,21 @@ def build(verbose=False):
         if rc != 0:
             raise RuntimeError("link failed:\n" + "\n".join(lines))
         msgs += lines
+        os.replace(tmp, LIB)
+        pobj = os.path.join(tmpdir, "probe.o")
+        rc, lines = _run([hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, "qgemm_probe.hip"), "-o", pobj])
+        if rc != 0:
+            raise RuntimeError("hipcc failed on qgemm_probe.hip:\n" + "\n".join(lines))
+        msgs += lines
+        ptmp = PROBE_LIB + ".tmp"
+        rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", pobj, "-L", PKG, "-lqgemm",
+                          "-Wl,-rpath,$ORIGIN", "-o", ptmp])
+        if rc != 0:
+            raise RuntimeError("link failed (probe library):\n" + "\n".join(lines))
+        msgs += lines
+        os.replace(ptmp, PROBE_LIB)
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
     return LIB
 
 
