@@ -140,7 +140,10 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // A is staged in LDS (at most 32 KiB per workgroup) when M is small: the MFMA fragment
     // loads would otherwise fetch each A value many times.  With larger M the rows are
     // distinct and fragments are loaded directly.
-    pl->astage = p->M <= 4;
+#ifndef QGEMM_DEC_ASTAGE_M
+#define QGEMM_DEC_ASTAGE_M 4
+#endif
+    pl->astage = p->M <= QGEMM_DEC_ASTAGE_M;
     // Column blocks per workgroup.  Every workgroup reads all M x K of A once, so wider
     // workgroups cut A traffic; narrower ones put more compute units to work.  M <= 4 (A
     // staged per wavefront): one block each up to three workgroups per compute unit, two

@@ -39,7 +39,10 @@ constexpr int kDecodeWaves = QGEMM_DEC_NW;
 constexpr int kDecodeWavesWide = 4;
 // Decode staging pass (A slice and scales into LDS): the largest staged A slice and scale
 // range per workgroup, and the 16-byte chunks per thread they take at most.
-constexpr int kDecodeMaxA = 32 * 1024;
+#ifndef QGEMM_DEC_MAXA
+#define QGEMM_DEC_MAXA (32 * 1024)
+#endif
+constexpr int kDecodeMaxA = QGEMM_DEC_MAXA;
 constexpr int kDecodeMaxScales = 16 * 1024;
 constexpr int kDecodeStageA = kDecodeMaxA / (16 * 64 * kDecodeWaves);
 constexpr int kDecodeStageS = kDecodeMaxScales / (16 * 64 * kDecodeWaves);
