@@ -228,6 +228,26 @@ qgemm_status_t qgemm_run_bias(const qgemm_problem_t* problem, const void* A, con
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qgemm_run_no_alloc -- qgemm_run_bias without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors as qgemm_run_bias (bias may be NULL);
+ * the launch plan, and so the result, is bitwise that of qgemm_run_bias on the same problem.
+ * The split-K workspace is a static device array of QGEMM_NO_ALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's first use on that GPU until the process ends; a problem whose plan
+ * needs more returns QGEMM_ERR_WORKSPACE_TOO_SMALL (qgemm_workspace_bytes tells in advance).
+ * The array holds a fixed region of split-K tickets (one per output tile, at most 16384) and
+ * the fp32 partial tiles after it.  The call allocates nothing.  The first call on a device
+ * that needs the array enqueues one clear of its ticket region on `stream` before its GEMM;
+ * every completed call leaves the tickets at zero again.  All calls on one GPU share the
+ * array: calls that may overlap in time on one GPU (different streams, different host
+ * threads) race and must not be made; calls in one stream's order are safe.
+ */
+#define QGEMM_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+qgemm_status_t qgemm_run_no_alloc(const qgemm_problem_t* problem, const void* A, const void* w_packed,
+                                  const void* s_packed, const float* alpha, const void* bias, void* out,
+                                  void* stream);
+
+/*
  * qgemm_status_string -- static, NUL-terminated name of a status code ("QGEMM_OK",
  * "QGEMM_ERR_MISALIGNED", ...; "QGEMM_ERR_UNKNOWN_STATUS" for a value outside the enum).
  * The pointer is owned by the library and valid for the life of the process.  Status codes

@@ -54,12 +54,15 @@ _lib.qgemm_pack.argtypes = [_P, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp, ctypes.
 _lib.qgemm_workspace_bytes.argtypes = [_P, ctypes.POINTER(_sz)]
 _lib.qgemm_run.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qgemm_run_bias.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.qgemm_run_no_alloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.qgemm_status_string.argtypes = [ctypes.c_int]
 _lib.qgemm_status_string.restype = ctypes.c_char_p
 _lib.qgemm_last_error.argtypes = []
 _lib.qgemm_last_error.restype = ctypes.c_char_p
 _lib.qgemm_version.restype = ctypes.c_int32
-for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run", "qgemm_run_bias"):
+NO_ALLOC_SCRATCH_BYTES = 32 << 20     # QGEMM_NO_ALLOC_SCRATCH_BYTES of include/qgemm.h
+for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run", "qgemm_run_bias",
+           "qgemm_run_no_alloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 lib = _lib
@@ -191,6 +194,19 @@ def run(p, A, w_packed, s_packed, alpha, out, workspace=None, stream=None, bias=
     else:
         _check(_lib.qgemm_run_bias(ctypes.byref(p), _ptr(A), _ptr(w_packed), _ptr(s_packed), _ptr(alpha),
                                    _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes, stream))
+
+
+def run_no_alloc(p, A, w_packed, s_packed, alpha, out, stream=None, bias=None):
+    """qgemm_run_no_alloc: as run(), with the library's static per-GPU scratch as the split-K
+    workspace (no workspace argument; nothing is allocated).  Calls that overlap in time on
+    one GPU race."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(_lib.qgemm_run_no_alloc(ctypes.byref(p), _ptr(A), _ptr(w_packed), _ptr(s_packed), _ptr(alpha),
+                                   _ptr(bias), _ptr(out), stream))
 
 
 def run_raw(p, A, w_packed, s_packed, alpha, out, workspace, workspace_bytes_, stream):
