@@ -90,6 +90,9 @@ typedef enum qgemm_scale_layout {
 #define QGEMM_KERNEL_AUTO 0
 #define QGEMM_KERNEL_DECODE 1     /* memory-bound skinny kernel, M <= 16 only            */
 #define QGEMM_KERNEL_PREFILL 2    /* MFMA tile kernel, any M                              */
+#define QGEMM_KERNEL_PREFILL_STREAMK 3  /* the MFMA tile kernel on a persistent grid: whole
+                                           tiles round-robin, the last rounds' tiles split
+                                           evenly in K over the workgroups (stream-K tail)   */
 
 /*
  * The problem descriptor, after the BitBLAS MatmulConfig (Bitblas lecture 033, API
@@ -102,7 +105,7 @@ typedef enum qgemm_scale_layout {
  *   FP8 weights take a_dtype BF16 (mm_bf16_fp8) or F16 (mm_fp16_fp8); the packed weights
  *   are the same for both.
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
- *   slices (1..64) the chosen kernel uses; tile_hint: 0 = automatic, else for the decode
+ *   slices (1..64) the chosen kernel uses (not with QGEMM_KERNEL_PREFILL_STREAMK); tile_hint: 0 = automatic, else for the decode
  *   kernel the number of 16-column blocks per workgroup (1 to 4), for the prefill
  *   kernel the rows of its workgroup tile (64: 64 x 128, 128: 128 x 128, 256: 256 x 256).
  *   Hints only change the work split and the reduction order of the fp32 accumulation,
@@ -231,7 +234,10 @@ qgemm_status_t qgemm_run_bias(const qgemm_problem_t* problem, const void* A, con
  * qgemm_run_no_alloc -- qgemm_run_bias without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Arguments, results and errors as qgemm_run_bias (bias may be NULL);
- * the launch plan, and so the result, is bitwise that of qgemm_run_bias on the same problem.
+ * the launch plan, and so the result, is bitwise that of qgemm_run_bias on the same problem,
+ * except where the automatic plan is the persistent stream-K schedule and its partial tiles
+ * exceed the array: then the one-tile launch of the same tiles runs (same tolerance, a
+ * different fp32 summation order for the tail tiles).
  * The split-K workspace is a static device array of QGEMM_NO_ALLOC_SCRATCH_BYTES per GPU,
  * held from the library's first use on that GPU until the process ends; a problem whose plan
  * needs more returns QGEMM_ERR_WORKSPACE_TOO_SMALL (qgemm_workspace_bytes tells in advance).

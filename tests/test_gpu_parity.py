@@ -376,6 +376,41 @@ def test_mid_m_auto_plan(q, fmt, G, M, N, K):
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
 
 
+STREAMK_CASES = [
+    # (format, G, M, N, K, tile rows): tiles vs resident workgroups (256 for the 256- and
+    # 128-row tiles, 512 for the 64-row tile): a tail of whole rounds plus a part, and far
+    # fewer tiles than workgroups (every tile cut among several workgroups)
+    ("fp8", None, 4352, 4096, 1024, 256),      # 17 x 16 = 272 tiles: 16 whole + 16 split in K
+    ("int4", 64, 4352, 4112, 768, 256),        # ragged N: 17 x 17 = 289 tiles
+    ("fp4", None, 2176, 2048, 1024, 128),      # 17 x 16 = 272 medium tiles
+    ("nf4", 128, 2112, 2048, 512, 64),         # 33 x 16 = 528 small tiles over 512 workgroups
+    ("int2", 32, 600, 784, 1024, 64),          # 10 x 7 = 70 tiles over 512 workgroups
+    ("fp8h", None, 300, 272, 2048, 256),       # 2 x 2 tiles, 16 k blocks each, over 256 workgroups
+    ("int4", 128, 1000, 4048, 1024, 128),      # 8 x 32 = 256 = one full round, no tail
+]
+
+
+@pytest.mark.parametrize("fmt,G,M,N,K,tile", STREAMK_CASES,
+                         ids=[f"{c[0]}-{c[2]}x{c[3]}x{c[4]}-t{c[5]}" for c in STREAMK_CASES])
+def test_prefill_persistent_stream_k(q, fmt, G, M, N, K, tile):
+    # The persistent prefill schedule (whole tiles round-robin, then the tail tiles' k blocks
+    # split evenly over the resident workgroups with a ticketed hand-off of fp32 partials):
+    # every row against the oracle, bitwise identical on a second run, tickets back at zero.
+    say(f"case stream-k fmt={fmt} G={G} M={M} N={N} K={K} tile={tile}")
+    prep = Prepared(q, fmt, N, K, G or 0, (64, N, K))
+    A = _act(fmt, M, K, (64, M))
+    st, y0 = check_against_oracle(q, prep, A, kernel_hint=3, tile_hint=tile)
+    y1, ws = run_gpu(q, prep, A, q.DT_F32, kernel_hint=3, tile_hint=tile)
+    assert np.array_equal(y0, y1)
+    p = q.problem(M, N, K, fmt, group_size=G, kernel_hint=3, tile_hint=tile)
+    assert ws is not None and q.workspace_bytes(p) > 0
+    T = -(-N // (256 if tile == 256 else 128)) * -(-M // tile)          # output tiles
+    P = 512 if tile == 64 else 256                                       # resident workgroups
+    tail = T - ((T // P - 1) * P if T > P else 0)                        # tiles with tickets
+    assert not ws[:4 * tail].cpu().numpy().any(), "stream-K tickets must return to zero"
+    say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
+
+
 def test_split_k_under_concurrent_load(q):
     # Split-K must not rely on its workgroups being resident together (FlashInfer PR #7495
     # analysis, section 3(d)): with a long GEMM occupying compute units from another stream,
@@ -384,7 +419,7 @@ def test_split_k_under_concurrent_load(q):
     import torch as T
     say("case split-k under concurrent load")
     cases = [("int4", 1, 256, 128 * 64, 128, 1, 16), ("fp4", 128, 2048, 8192, 0, 2, 4),
-             ("fp8", 16, 512, 128 * 40, 0, 1, 5)]
+             ("fp8", 16, 512, 128 * 40, 0, 1, 5), ("fp8", 300, 272, 2048, 0, 3, 0)]
     preps = []
     for fmt, M, N, K, G, hint, split in cases:
         prep = Prepared(q, fmt, N, K, G, (62, N, K))

@@ -73,6 +73,23 @@ def test_no_alloc_matches_workspace_entry_point_bitwise(q):
     say(f"  fp4 128x8192x8192 E1={st['E1']:.3e}")
 
 
+def test_no_alloc_runs_the_one_tile_launch_where_stream_k_partials_exceed_the_scratch(q):
+    # The automatic plan of this shape is the persistent stream-K schedule, whose partial tiles
+    # (two 256 x 256 fp32 slots per resident workgroup) exceed the static scratch: the entry
+    # point then runs the one-tile launch of the same tiles, bitwise what qgemm_run_bias gives
+    # with the prefill kernel hint (which never picks the persistent schedule).
+    M, N, K = 4352, 4096, 4096
+    say("case no-alloc stream-k fallback int4 4352x4096x4096")
+    auto = q.problem(M, N, K, "int4")
+    assert q.workspace_bytes(auto) > q.NO_ALLOC_SCRATCH_BYTES
+    prep = Prepared(q, "int4", N, K, 128, (71, N, K))
+    A = synthetic.activations(M, K, "f16", (71, M))
+    for odt in (q.DT_F32, q.DT_F16):
+        want, _ = run_gpu(q, prep, A, odt, kernel_hint=2)
+        got = _no_alloc(q, prep, A, odt)
+        assert np.array_equal(got, want)
+
+
 def test_no_alloc_rejects_plans_beyond_the_scratch(q):
     # FP4 1024 x 8192 x 8192 plans 64 MiB of partial tiles, more than the static scratch holds:
     # the call is refused before anything is enqueued, and the workspace entry point is not.

@@ -70,6 +70,11 @@ struct KArgs {
   int out_dtype;
   int splits, kb_per_split;
   int tiles_n;                // prefill: output tiles along N
+  // persistent prefill (grid of `persist` workgroups, 0 = one tile per workgroup): tiles
+  // 0 .. dp_tiles - 1 go round-robin to the workgroups, the k blocks of the rest (the stream-K
+  // tail) are split into ranges of sk_q + 1 (the first sk_r workgroups) or sk_q
+  int persist, tiles_total, dp_tiles;
+  int sk_q, sk_r;
 };
 
 // ----------------------------------------------------------------------------- dequant
@@ -429,23 +434,29 @@ __device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v,
 // (the relaxed device-scope atomics of the same bits move 4 bytes per instruction).
 constexpr int kCPolDevice = 16;   // buffer-instruction cache policy: sc1 (device scope)
 
-template <int NF, int NT = 256>
-__device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
+// Hand-off of one contributor's fp32 partial tile, shared by split-K and the stream-K tail of
+// the persistent prefill.  The tile's contributors use partial slots base .. base + span - 1
+// (slot = tile_elems fp32 values); this one writes its partial to slot `my`, then takes a
+// ticket on `counter`; the contributor that draws ticket nslots - 1 sums the partials of
+// contributors 0 .. nslots - 1 (slot rel(i)) in that order, resets the ticket and returns true.
+template <int NF, int NT, class RelSlot>
+__device__ bool fixup_finish(unsigned* counter, float* base, int span, int my, int nslots, RelSlot rel,
+                             int tile_elems, bool active, f32x4 (&v)[NF]) {
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
-      a.partials + (size_t)tile * a.splits * tile_elems, (short)0, a.splits * tile_elems * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t part =
+      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, span * tile_elems * 4, 0x00020000);
   if (active) {
 #pragma unroll
     for (int f = 0; f < NF; ++f)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[f]), part,
-                                             (split * tile_elems + 4 * (f * NT + tid)) * 4, 0, kCPolDevice);
+                                             (my * tile_elems + 4 * (f * NT + tid)) * 4, 0, kCPolDevice);
   }
   __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores are complete
   __syncthreads();
   if (tid == 0) {
-    const unsigned ticket = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ticket == (unsigned)(a.splits - 1);
+    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ticket == (unsigned)(nslots - 1);
   }
   __syncthreads();
   if (!s_last) return false;
@@ -453,7 +464,8 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
 #pragma unroll
     for (int f = 0; f < NF; ++f) v[f] = f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int B = NF < 8 ? NF : 8;                // loads in flight per batch
-    for (int s = 0; s < a.splits; ++s) {
+    for (int i = 0; i < nslots; ++i) {
+      const int s = rel(i);
 #pragma unroll
       for (int f0 = 0; f0 < NF; f0 += B) {
         f32x4 p[B];
@@ -467,8 +479,15 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
       }
     }
   }
-  if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
+}
+
+// Split-K: the splits of a tile use slots tile * splits .. + splits - 1, contributor i = slot i.
+template <int NF, int NT = 256>
+__device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elems, bool active, f32x4 (&v)[NF]) {
+  return fixup_finish<NF, NT>(a.counters + tile, a.partials + (size_t)tile * a.splits * tile_elems, a.splits, split,
+                              a.splits, [](int i) { return i; }, tile_elems, active, v);
 }
 
 // ----------------------------------------------------------------------------- launchers

@@ -95,8 +95,11 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
     return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, INT2, NF4, FP8_E4M3, FP4_E2M1)", dtype_name(w));
   }
 
-  if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint must be 0, 1 or 2, got %d", p->kernel_hint);
+  if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL_STREAMK)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint must be 0, 1, 2 or 3, got %d", p->kernel_hint);
+  if (p->kernel_hint == QGEMM_KERNEL_PREFILL_STREAMK && p->split_k_hint != 0)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint PREFILL_STREAMK splits K itself; split_k_hint must be 0, got %d",
+                p->split_k_hint);
   if (p->kernel_hint == QGEMM_KERNEL_DECODE && p->M > 16)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint DECODE needs M <= 16, got M=%lld", (long long)p->M);
   if (p->split_k_hint < 0 || p->split_k_hint > 64)
@@ -128,7 +131,7 @@ static void finish_split(Plan* pl, int kblocks, int requested) {
   pl->splits = ceil_div(kblocks, pl->kb_per_split);   // no empty split
 }
 
-qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
+qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl, bool allow_persist) {
   std::memset(pl, 0, sizeof(*pl));
   pl->fmt = format_of(p);
   if (p->M == 0) return QGEMM_OK;                    // empty product: no launch, no workspace
@@ -252,6 +255,44 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->grid_y = (unsigned)pl->splits;
     pl->tiles = (int)(mt * nt);
     pl->tile_elems = pl->bm * pl->bn;
+    // Persistent schedule with a stream-K tail: as many workgroups as are resident at once
+    // (one per CU for the 256- and 128-row tiles, whose A stages take 128 KiB of LDS; two for
+    // the 64-row tile); each takes whole tiles round-robin (the same tile ids, and so the same
+    // XCD-aware walk, as the one-tile launch) for all rounds but the last full one, and the
+    // tiles left (between one and two rounds' worth) are split evenly in K over all of them,
+    // so no round runs partly idle.  The cost is a partial-tile hand-off for the tail tiles
+    // that a workgroup boundary cuts.  Chosen when the model's time, with the hand-off priced
+    // like split-K's, beats the one-tile launch: the last round must be at most ~3/4 full.
+    const int64_t T = mt * nt;
+    const int P = kCUs * (pl->bm == pf_bm(kPfSmall) ? 2 : 1);
+    const double t_kb = best_c == 0 ? 0.8 : best_c == 1 ? 1.3 : 3.4;
+    bool persist = p->kernel_hint == QGEMM_KERNEL_PREFILL_STREAMK;
+    if (!persist && allow_persist && p->kernel_hint == QGEMM_KERNEL_AUTO && p->split_k_hint == 0 && pl->splits == 1 && T > P &&
+        T % P != 0) {
+      const double one_tile = (double)((T + P - 1) / P) * (kblocks + kFill) * t_kb;
+      const int64_t dp = (T / P - 1) * P;
+      const double tail = (double)((T - dp) * kblocks) / P;
+      // about one partial tile written per workgroup and read back once, all at the same time
+      const double handoff = (double)P * pl->tile_elems * 4 * 2 / kBytesPerUs + 2 * kPartialLatency;
+      const double streamk = ((double)(dp / P) * (kblocks + kFill) + tail + 2 * kFill) * t_kb + handoff;
+      persist = streamk < one_tile;
+    }
+    if (persist) {
+      const int64_t dp = T > P ? (T / P - 1) * P : 0;
+      if ((T - dp) * kblocks > 0x7fffffffLL)
+        return fail(QGEMM_ERR_UNSUPPORTED, "the stream-K tail of %lld tiles x %d k blocks is too long",
+                    (long long)(T - dp), kblocks);
+      pl->persist = P;
+      pl->dp_tiles = (int)dp;
+      pl->sk_units = (long long)(T - dp) * kblocks;
+      pl->splits = 1;
+      pl->kb_per_split = kblocks;
+      pl->grid_x = (unsigned)P;
+      pl->grid_y = 1;
+      pl->tiles = (int)(T - dp);                      // tickets: one per tail tile
+      pl->counters_bytes = ((size_t)pl->tiles * 4 + 255) / 256 * 256;
+      pl->ws_bytes = pl->counters_bytes + (size_t)2 * P * pl->tile_elems * 4;   // two partial slots per workgroup
+    }
   }
   if ((int64_t)pl->grid_x * pl->grid_y > 0x7fffffffLL)
     return fail(QGEMM_ERR_UNSUPPORTED, "problem needs %lld workgroups, more than one launch allows",

@@ -109,6 +109,11 @@ struct Plan {
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
   int splits;
   int kb_per_split;
+  // prefill, persistent schedule (0 = one tile per workgroup): resident workgroups, whole tiles
+  // handed out round-robin, and the k blocks of the remaining (stream-K tail) tiles
+  int persist;
+  int dp_tiles;
+  long long sk_units;
   // grid
   unsigned grid_x, grid_y;
   int tiles;              // output tiles that own a split-K counter
@@ -117,6 +122,8 @@ struct Plan {
   size_t ws_bytes;        // total workspace (0 when splits == 1)
 };
 
-qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* plan);
+// allow_persist = false plans the one-tile prefill launch even where the persistent schedule
+// would be chosen (for callers whose workspace cannot hold the stream-K partials).
+qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* plan, bool allow_persist = true);
 
 }  // namespace qgemm

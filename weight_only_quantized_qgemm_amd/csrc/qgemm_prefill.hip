@@ -69,7 +69,82 @@ __device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& t
   tn = in / gm;
 }
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST>
+// One piece of work of a prefill workgroup: output tile (tm, tn), its k blocks
+// [kb_begin, kb_end), and how the tile's sum is completed.  nslots == 1: this segment is the
+// whole sum and writes the output.  Otherwise the tile's nslots contributors hand off fp32
+// partials through slots base .. base + span - 1 (this one's is `my`), ticket `counter`; for
+// split-K contributor i uses slot i (v0 < 0), for the stream-K tail contributor i is
+// workgroup v0 + i, whose slot is 2 (v0 + i) + [the tile is not that workgroup's first].
+struct PfSeg {
+  int tm, tn, kb_begin, kb_end;
+  int nslots, span, my, v0, t;
+  unsigned* counter;
+  float* base;
+};
+
+// Stream-K tail of the persistent schedule: the sk_units k blocks of the tail tiles are cut
+// into P contiguous ranges of q or q + 1 units (the first r ranges are one longer; q and r are
+// computed on the host), range v = [start(v), start(v + 1)).  owner(x) is the workgroup whose
+// range holds unit x.  All of it fits 32-bit arithmetic (sk_units < 2^31).
+__device__ __forceinline__ int sk_start(int v, int q, int r) { return v * q + min(v, r); }
+__device__ __forceinline__ int sk_owner(int x, int q, int r) {
+  const int big = r * (q + 1);                       // units in the r longer ranges
+  return x < big ? x / (q + 1) : r + (x - big) / q;  // q > 0 whenever x >= big
+}
+
+// The item-th segment of this workgroup (false when it has no more).  Without persistence a
+// workgroup owns one tile (blockIdx.x) and one K slice (blockIdx.y).  With it, workgroup w of
+// the a.persist resident ones first takes the whole tiles w, w + P, ... below dp_tiles (the
+// same XCD-aware walk of tile ids as the one-tile launch: id b runs on XCD b mod 8 in both,
+// since P is a multiple of 8), then its contiguous range of the tail's k blocks, one segment
+// per tail tile the range touches.
+template <bool PERSIST>
+__device__ __forceinline__ bool pf_next(const KArgs& a, int item, int KB, int tile_elems, PfSeg& g) {
+  if constexpr (!PERSIST) {
+    const int tile = blockIdx.x, split = blockIdx.y;
+    pf_tile_of(tile, gridDim.x, a.tiles_n, g.tm, g.tn);
+    g.kb_begin = split * a.kb_per_split;
+    g.kb_end = min(KB, g.kb_begin + a.kb_per_split);
+    g.nslots = a.splits;
+    g.span = a.splits;
+    g.my = split;
+    g.v0 = -1;
+    g.t = tile;
+    g.counter = a.counters + tile;
+    g.base = a.partials + (size_t)tile * a.splits * tile_elems;
+    return item == 0;
+  } else {
+    const int P = a.persist, w = blockIdx.x;
+    const int ndp = w < a.dp_tiles ? (a.dp_tiles - w + P - 1) / P : 0;
+    if (item < ndp) {
+      pf_tile_of(w + item * P, a.tiles_total, a.tiles_n, g.tm, g.tn);
+      g.kb_begin = 0;
+      g.kb_end = KB;
+      g.nslots = 1;
+      return true;
+    }
+    const int q = a.sk_q, r = a.sk_r;
+    const int u0 = sk_start(w, q, r), u1 = sk_start(w + 1, q, r);
+    const int t0 = u0 / KB;
+    const int t = t0 + (item - ndp);
+    const int s0 = max(u0, t * KB), s1 = min(u1, (t + 1) * KB);
+    if (s0 >= s1) return false;
+    g.kb_begin = s0 - t * KB;
+    g.kb_end = s1 - t * KB;
+    const int v0 = sk_owner(t * KB, q, r), vl = sk_owner((t + 1) * KB - 1, q, r);
+    g.nslots = vl - v0 + 1;
+    g.span = 2 * g.nslots;
+    g.my = 2 * (w - v0) + (t == t0 ? 0 : 1);
+    g.v0 = v0;
+    g.t = t;
+    g.counter = a.counters + t;
+    g.base = a.partials + (size_t)(2 * v0) * tile_elems;
+    pf_tile_of(a.dp_tiles + t, a.tiles_total, a.tiles_n, g.tm, g.tn);
+    return true;
+  }
+}
+
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST, bool PERSIST>
 __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   constexpr int NW = WGM * WGN;                      // wavefronts
   constexpr int NT = 64 * NW;                        // threads
@@ -109,13 +184,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   const int wm = wave / WGN, wn = wave % WGN;
   Lut lut;                                           // NF4 code book (wavefront-uniform)
   load_lut<FMT>(a, lut);
-  const int tile = blockIdx.x, split = blockIdx.y;
-  int tm, tn;
-  pf_tile_of(tile, gridDim.x, a.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
   const int KB = a.K >> 7, NB = a.N >> 4;
-  const int kb_begin = split * a.kb_per_split;
-  const int kb_end = min(KB, kb_begin + a.kb_per_split);
+  for (int item = 0; item < (PERSIST ? 0x7fffffff : 1); ++item) {
+  PfSeg sg;
+  if (!pf_next<PERSIST>(a, item, KB, BM * BN, sg)) break;
+  if (item > 0) {
+    // the previous segment's output stores and LDS reads are done before this one's loads
+    // and DMA writes start (the load counts below assume nothing older is outstanding)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  const int tm = sg.tm, tn = sg.tn;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb_begin = sg.kb_begin, kb_end = sg.kb_end;
 
   // DMA load i of this wavefront fills LDS bytes [(NW i + wave) KiB, +1 KiB): tile rows
   // 4 (NW i + wave) + lane / 16, chunk position lane & 15.  Since 4 NW is a multiple of 16,
@@ -238,8 +319,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) v[TN * i + j] = acc[i][j];
-  if (a.splits > 1) {
-    if (!splitk_finish<TM * TN, NT>(a, tile, split, BM * BN, true, v)) return;
+  if (sg.nslots > 1) {
+    const int v0 = sg.v0, t = sg.t;
+    auto rel = [&](int i) {
+      if constexpr (!PERSIST) return i;              // split-K
+      else                                           // stream-K: workgroup v0 + i's slot for tail tile t
+        return 2 * i + (t == sk_start(v0 + i, a.sk_q, a.sk_r) / KB ? 0 : 1);
+    };
+    if (!fixup_finish<TM * TN, NT>(sg.counter, sg.base, sg.span, sg.my, sg.nslots, rel, BM * BN, true, v))
+      continue;                                      // another contributor completes this tile
   }
   const float alpha = qgemm::group_scaled(FMT) ? 1.0f : *a.alpha;
   auto scaled = [&](f32x4 x) {
@@ -264,7 +352,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
         if (m < a.M) store_out4(a, m, n, scaled(v[TN * i + j]), bv);
       }
     }
-    return;
+    continue;
   }
 
   // 16-bit output: the tile goes through the (now idle) A stages in LDS, row-major, so that
@@ -302,12 +390,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(stage(R / RPA) + (R % RPA) * OROW + 16 * (c ^ (R & 15)));
     if (col_ok && m0 + R < a.M) *reinterpret_cast<u32x4*>(out + (size_t)(m0 + R) * a.N * 2) = x;
   }
+  }   // segments
 }
 
 template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST>
 void launch_shape(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST>), dim3(pl.grid_x, pl.grid_y),
-                     dim3(64 * WGM * WGN), 0, stream, a);
+  if (pl.persist)
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST, true>), dim3(pl.grid_x, pl.grid_y),
+                       dim3(64 * WGM * WGN), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST, false>), dim3(pl.grid_x, pl.grid_y),
+                       dim3(64 * WGM * WGN), 0, stream, a);
 }
 
 template <int FMT, int G>

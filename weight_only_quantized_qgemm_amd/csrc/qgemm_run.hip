@@ -93,6 +93,11 @@ qgemm_status_t enqueue(const qgemm_problem_t* p, const qgemm::Plan& pl, const vo
   a.splits = pl.splits;
   a.kb_per_split = pl.kb_per_split;
   a.tiles_n = (int)((p->N + pl.bn - 1) / (pl.bn ? pl.bn : 1));
+  a.persist = pl.persist;
+  a.tiles_total = pl.persist ? (int)(((p->M + pl.bm - 1) / pl.bm) * a.tiles_n) : 0;
+  a.dp_tiles = pl.dp_tiles;
+  a.sk_q = pl.persist ? (int)(pl.sk_units / pl.persist) : 0;
+  a.sk_r = pl.persist ? (int)(pl.sk_units % pl.persist) : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = pl.kind == KIND_PREFILL ? dev::launch_prefill(pl, p->group_size, a, s)
@@ -202,6 +207,11 @@ extern "C" qgemm_status_t qgemm_run_no_alloc(const qgemm_problem_t* p, const voi
   Plan pl;
   st = make_plan(p, &pl);
   if (st != QGEMM_OK) return st;
+  if (pl.persist && p->kernel_hint == QGEMM_KERNEL_AUTO &&
+      ((size_t)pl.tiles * 4 > kScratchTicketBytes || pl.ws_bytes - pl.counters_bytes > kScratchBytes - kScratchTicketBytes)) {
+    st = make_plan(p, &pl, false);                   // the one-tile launch of the same tiles
+    if (st != QGEMM_OK) return st;
+  }
   char* sc = nullptr;
   if (pl.ws_bytes) {
     const size_t partial_bytes = pl.ws_bytes - pl.counters_bytes;
