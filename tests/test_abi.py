@@ -207,3 +207,26 @@ def test_nf4_needs_its_scale_layout():
     assert _valid_run_status(p, S=0x3008) == q.ERR_MISALIGNED
     p.scale_layout = 4
     assert _valid_run_status(p) == q.ERR_INVALID_ARGUMENT
+
+
+def test_planner_sweep_sizes_are_consistent():
+    # The launch planner over a grid of shapes, formats and hints (run also under the host
+    # sanitizers by test_host_asan.py): every valid problem gets a plan, the workspace size is
+    # a multiple of 256 plus whole fp32 tiles or 0, and forcing the persistent stream-K
+    # schedule always asks for a workspace (its tickets and partial slots).
+    sizes = [1, 2, 15, 16, 17, 64, 65, 128, 255, 300, 1000, 4097, 9000, 70000]
+    for fmt in ("int4", "int2", "nf4", "fp8", "fp8h", "fp4"):
+        for M in sizes:
+            for N, K in ((16, 128), (272, 768), (4096, 4096), (12800, 5120), (256, 131072)):
+                for hint, tile in ((0, 0), (2, 64), (2, 128), (2, 256), (3, 0), (3, 64)):
+                    if hint == 2 and tile and tile * K * 2 >= 2 ** 31:
+                        continue
+                    p = q.problem(M, N, K, fmt, kernel_hint=hint, tile_hint=tile)
+                    try:
+                        ws = q.workspace_bytes(p)
+                    except q.QgemmError as e:
+                        assert e.status == q.ERR_UNSUPPORTED and "prefill kernel needs" in e.detail
+                        continue
+                    assert ws >= 0
+                    if hint == 3:
+                        assert ws > 0

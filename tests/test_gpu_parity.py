@@ -440,3 +440,36 @@ def test_split_k_under_concurrent_load(q):
             assert not ws[:256].cpu().numpy().any()
     side.synchronize()
     del z
+
+
+@pytest.mark.parametrize("fmt,M,N,K,hint,split,tile", [("int4", 1, 256, 128 * 64, 1, 16, 0),
+                                                       ("fp8", 16, 512, 128 * 40, 1, 5, 2),
+                                                       ("fp4", 128, 2048, 8192, 2, 4, 128),
+                                                       ("nf4", 300, 272, 1024, 2, 3, 64),
+                                                       ("fp8", 4352, 4096, 1024, 3, 0, 256),
+                                                       ("int2", 600, 784, 1024, 3, 0, 64)])
+def test_workspace_guard_bytes_survive(q, fmt, M, N, K, hint, split, tile):
+    # The workspace handed over is the planned size plus 64 KiB of guard bytes: no split-K or
+    # stream-K hand-off (tickets or partial tiles) writes past the size qgemm_workspace_bytes
+    # reports, and the tickets are back at zero afterwards.
+    import torch as T
+    G = {"int4": 128, "int2": 32, "nf4": 64}.get(fmt, 0)
+    say(f"case workspace guard fmt={fmt} M={M} N={N} K={K} hint={hint} split={split} tile={tile}")
+    prep = Prepared(q, fmt, N, K, G, (65, N, K))
+    A = _act(fmt, M, K, (65, M))
+    p = q.problem(M, N, K, fmt, group_size=G or None, kernel_hint=hint, split_k_hint=split, tile_hint=tile)
+    need = q.workspace_bytes(p)
+    assert need > 0
+    ws = T.zeros(need + 65536, dtype=T.uint8, device="cuda")
+    ws[need:] = 0xA5
+    y = []
+    for odt in (q.DT_F32, out16_dtype(q, fmt)):
+        y.append(run_gpu(q, prep, A, odt, hint, split, workspace=ws, tile_hint=tile)[0])
+    tail = ws[need:].cpu().numpy()
+    assert (tail == 0xA5).all(), f"{int((tail != 0xA5).sum())} guard bytes overwritten"
+    head = ws[:256].cpu().numpy()
+    assert not head.any()
+    # the fp32 result itself is right (the run with the exact workspace is covered elsewhere)
+    from oracle import reference
+    r = reference.gemm_fp64(A.to(T.float64).numpy(), prep.wdq, prep.alpha)
+    tolerance.check_e1_e2(y[0], r)

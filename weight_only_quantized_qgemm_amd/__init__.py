@@ -22,7 +22,9 @@ import numpy as np
 import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqgemm.so")
+# QGEMM_LIB_PATH selects another build of the same library (the CPU tests load the
+# host-sanitizer build this way); by default the in-tree libqgemm.so.
+LIB_PATH = os.environ.get("QGEMM_LIB_PATH") or os.path.join(_PKG, "libqgemm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "

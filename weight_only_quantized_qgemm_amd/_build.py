@@ -1,16 +1,18 @@
 """Builds the HIP library (libqgemm.so) in-tree for gfx950 with hipcc.
 
 Each source compiles to its own objects in parallel (the kernel sources once per weight format), then hipcc links the shared library.
+The objects stay in _build/obj next to this file (not committed), where the host-sanitizer
+build of the host code (_build_asan.py) finds the kernel objects it links against.
 """
 import os
 import subprocess
-import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemm.so")
+OBJ_DIR = os.path.join(PKG, "_build", "obj")
 # measurement helpers for the benchmark (streaming-read kernel, host time per call): a library
 # of their own, outside the qgemm ABI
 PROBE_LIB = os.path.join(PKG, "libqgemm_probe.so")
@@ -32,6 +34,12 @@ HIPCC_FLAGS = [
 ]
 
 
+def unit_object(source, defs):
+    """Path of the object file of one compilation unit (a source and its defines)."""
+    tag = "".join(d.split("=")[-1] for d in defs)
+    return os.path.join(OBJ_DIR, f"{source.replace('.', '_')}{'_' + tag if tag else ''}.o")
+
+
 def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the gfx-only target feature; that warning is noise
@@ -43,36 +51,36 @@ def build(verbose=False):
     """Compile every source into libqgemm.so next to this file; returns its path."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     inc = ["-I", os.path.join(ROOT, "include")]
-    with tempfile.TemporaryDirectory(prefix="qgemm_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, f"{i}_{s}.o") for i, (s, _) in enumerate(UNITS)]
-        cmds = [[hipcc, *HIPCC_FLAGS, *defs, *inc, "-c", os.path.join(CSRC, s), "-o", o]
-                for (s, defs), o in zip(UNITS, objs)]
-        workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
-        with ThreadPoolExecutor(max_workers=workers) as ex:
-            results = list(ex.map(_run, cmds))
-        msgs = []
-        for (s, defs), (rc, lines) in zip(UNITS, results):
-            if rc != 0:
-                raise RuntimeError(f"hipcc failed on {s} {' '.join(defs)}:\n" + "\n".join(lines))
-            msgs += lines
-        tmp = LIB + ".tmp"
-        rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [unit_object(s, defs) for s, defs in UNITS]
+    cmds = [[hipcc, *HIPCC_FLAGS, *defs, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+            for (s, defs), o in zip(UNITS, objs)]
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(_run, cmds))
+    msgs = []
+    for (s, defs), (rc, lines) in zip(UNITS, results):
         if rc != 0:
-            raise RuntimeError("link failed:\n" + "\n".join(lines))
+            raise RuntimeError(f"hipcc failed on {s} {' '.join(defs)}:\n" + "\n".join(lines))
         msgs += lines
-        os.replace(tmp, LIB)
-        pobj = os.path.join(tmpdir, "probe.o")
-        rc, lines = _run([hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, "qgemm_probe.hip"), "-o", pobj])
-        if rc != 0:
-            raise RuntimeError("hipcc failed on qgemm_probe.hip:\n" + "\n".join(lines))
-        msgs += lines
-        ptmp = PROBE_LIB + ".tmp"
-        rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", pobj, "-L", PKG, "-lqgemm",
-                          "-Wl,-rpath,$ORIGIN", "-o", ptmp])
-        if rc != 0:
-            raise RuntimeError("link failed (probe library):\n" + "\n".join(lines))
-        msgs += lines
-        os.replace(ptmp, PROBE_LIB)
+    tmp = LIB + ".tmp"
+    rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(lines))
+    msgs += lines
+    os.replace(tmp, LIB)
+    pobj = os.path.join(OBJ_DIR, "qgemm_probe_hip.o")
+    rc, lines = _run([hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, "qgemm_probe.hip"), "-o", pobj])
+    if rc != 0:
+        raise RuntimeError("hipcc failed on qgemm_probe.hip:\n" + "\n".join(lines))
+    msgs += lines
+    ptmp = PROBE_LIB + ".tmp"
+    rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", pobj, "-L", PKG, "-lqgemm",
+                      "-Wl,-rpath,$ORIGIN", "-o", ptmp])
+    if rc != 0:
+        raise RuntimeError("link failed (probe library):\n" + "\n".join(lines))
+    msgs += lines
+    os.replace(ptmp, PROBE_LIB)
     if verbose and msgs:
         print("\n".join(msgs))
     return LIB

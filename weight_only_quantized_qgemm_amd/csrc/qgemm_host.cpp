@@ -398,7 +398,12 @@ using namespace qgemm;
 // ============================================================================= C ABI
 extern "C" {
 
-const char* qgemm_status_string(qgemm_status_t st) {
+const char* qgemm_status_string(qgemm_status_t status) {
+  // A C caller may pass any int; read the raw value (in C++ a load of an enum object holding a
+  // value outside the enumeration's range is undefined)
+  int32_t st;
+  std::memcpy(&st, &status, sizeof st);
+  static_assert(sizeof(qgemm_status_t) == sizeof(int32_t), "status is passed as a 32-bit int");
   switch (st) {
     case QGEMM_OK: return "QGEMM_OK";
     case QGEMM_ERR_INVALID_ARGUMENT: return "QGEMM_ERR_INVALID_ARGUMENT";
