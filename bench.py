@@ -385,15 +385,22 @@ def main():
         return
 
     if args.counter_pass == "prefill":
+        # the prefill workloads with the planned launch, then FP8 32768 x 3200 x 5120 with the
+        # persistent stream-K schedule (kernel_hint PREFILL_STREAMK) and with one tile per
+        # workgroup (kernel_hint PREFILL)
         done = []
-        for name, si, G in (("int4_prefill", 0, 128), ("fp8", 2, 0), ("fp4", 2, 0)):
+        for name, si, G, hint in (("int4_prefill", 0, 128, 0), ("fp8", 2, 0, 0), ("fp4", 2, 0, 0),
+                                  ("fp8", 3, 0, q.KERNEL_PREFILL_STREAMK), ("fp8", 3, 0, q.KERNEL_PREFILL)):
             wk = synthetic.WORKLOADS[name]
             M, N, K = wk["shapes"][si]
             g = Gemm(q, torch, wk["fmt"], M, N, K, G, (synthetic.WORKLOAD_INDEX[name], si), rot // 2)
+            if hint:
+                g.p = q.problem(M, N, K, wk["fmt"], group_size=G or None, kernel_hint=hint)
+                g.ws = q.alloc_workspace(g.p)
             for _ in range(3):
                 g.launch()
             torch.cuda.synchronize()
-            done.append(f"{wk['fmt']} M={M} N={N} K={K}")
+            done.append(f"{wk['fmt']} M={M} N={N} K={K}" + (f" kernel_hint={hint}" if hint else ""))
             del g
             torch.cuda.empty_cache()
         print(json.dumps({"counter_pass": done, "launches_each": 3}))

@@ -92,7 +92,8 @@ typedef enum qgemm_scale_layout {
 #define QGEMM_KERNEL_PREFILL 2    /* MFMA tile kernel, any M                              */
 #define QGEMM_KERNEL_PREFILL_STREAMK 3  /* the MFMA tile kernel on a persistent grid: whole
                                            tiles round-robin, the last rounds' tiles split
-                                           evenly in K over the workgroups (stream-K tail)   */
+                                           evenly in K over the workgroups (stream-K tail);
+                                           never chosen automatically                        */
 
 /*
  * The problem descriptor, after the BitBLAS MatmulConfig (Bitblas lecture 033, API
@@ -234,10 +235,7 @@ qgemm_status_t qgemm_run_bias(const qgemm_problem_t* problem, const void* A, con
  * qgemm_run_no_alloc -- qgemm_run_bias without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Arguments, results and errors as qgemm_run_bias (bias may be NULL);
- * the launch plan, and so the result, is bitwise that of qgemm_run_bias on the same problem,
- * except where the automatic plan is the persistent stream-K schedule and its partial tiles
- * exceed the array: then the one-tile launch of the same tiles runs (same tolerance, a
- * different fp32 summation order for the tail tiles).
+ * the launch plan, and so the result, is bitwise that of qgemm_run_bias on the same problem.
  * The split-K workspace is a static device array of QGEMM_NO_ALLOC_SCRATCH_BYTES per GPU,
  * held from the library's first use on that GPU until the process ends; a problem whose plan
  * needs more returns QGEMM_ERR_WORKSPACE_TOO_SMALL (qgemm_workspace_bytes tells in advance).
@@ -248,7 +246,7 @@ qgemm_status_t qgemm_run_bias(const qgemm_problem_t* problem, const void* A, con
  * array: calls that may overlap in time on one GPU (different streams, different host
  * threads) race and must not be made; calls in one stream's order are safe.
  */
-#define QGEMM_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+#define QGEMM_NO_ALLOC_SCRATCH_BYTES ((32u << 20) + (64u << 10))
 qgemm_status_t qgemm_run_no_alloc(const qgemm_problem_t* problem, const void* A, const void* w_packed,
                                   const void* s_packed, const float* alpha, const void* bias, void* out,
                                   void* stream);

@@ -73,21 +73,28 @@ def test_no_alloc_matches_workspace_entry_point_bitwise(q):
     say(f"  fp4 128x8192x8192 E1={st['E1']:.3e}")
 
 
-def test_no_alloc_runs_the_one_tile_launch_where_stream_k_partials_exceed_the_scratch(q):
-    # The automatic plan of this shape is the persistent stream-K schedule, whose partial tiles
-    # (two 256 x 256 fp32 slots per resident workgroup) exceed the static scratch: the entry
-    # point then runs the one-tile launch of the same tiles, bitwise what qgemm_run_bias gives
-    # with the prefill kernel hint (which never picks the persistent schedule).
-    M, N, K = 4352, 4096, 4096
-    say("case no-alloc stream-k fallback int4 4352x4096x4096")
-    auto = q.problem(M, N, K, "int4")
-    assert q.workspace_bytes(auto) > q.NO_ALLOC_SCRATCH_BYTES
+def test_no_alloc_runs_the_persistent_stream_k_schedule(q):
+    # The persistent schedule with the 128- and 64-row tiles keeps its two partial slots per
+    # resident workgroup (32 MiB) and its tail tickets inside the static scratch: bitwise the
+    # result of qgemm_run_bias with a workspace, twice in a row; with the 256-row tile it needs
+    # 128 MiB and is refused.
+    M, N, K = 2176, 2048, 1024
+    say("case no-alloc stream-k int4 2176x2048x1024")
     prep = Prepared(q, "int4", N, K, 128, (71, N, K))
     A = synthetic.activations(M, K, "f16", (71, M))
-    for odt in (q.DT_F32, q.DT_F16):
-        want, _ = run_gpu(q, prep, A, odt, kernel_hint=2)
-        got = _no_alloc(q, prep, A, odt)
-        assert np.array_equal(got, want)
+    for tile in (128, 64):
+        assert 0 < q.workspace_bytes(q.problem(M, N, K, "int4", kernel_hint=3, tile_hint=tile)) <= q.NO_ALLOC_SCRATCH_BYTES
+        for odt in (q.DT_F32, q.DT_F16):
+            want, _ = run_gpu(q, prep, A, odt, kernel_hint=3, tile_hint=tile)
+            for _ in range(2):
+                got = _no_alloc(q, prep, A, odt, kernel_hint=3, tile_hint=tile)
+                assert np.array_equal(got, want)
+    big = q.problem(M, N, K, "int4", kernel_hint=3, tile_hint=256)
+    assert q.workspace_bytes(big) > q.NO_ALLOC_SCRATCH_BYTES
+    out = torch.full((M, N), 3.0, dtype=torch.float16, device="cuda")
+    with pytest.raises(q.QgemmError) as ei:
+        q.run_no_alloc(big, A.cuda(), prep.w, prep.s, None, out)
+    assert ei.value.status == q.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_no_alloc_rejects_plans_beyond_the_scratch(q):

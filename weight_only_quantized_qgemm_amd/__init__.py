@@ -62,7 +62,7 @@ _lib.qgemm_status_string.restype = ctypes.c_char_p
 _lib.qgemm_last_error.argtypes = []
 _lib.qgemm_last_error.restype = ctypes.c_char_p
 _lib.qgemm_version.restype = ctypes.c_int32
-NO_ALLOC_SCRATCH_BYTES = 32 << 20     # QGEMM_NO_ALLOC_SCRATCH_BYTES of include/qgemm.h
+NO_ALLOC_SCRATCH_BYTES = (32 << 20) + (64 << 10)    # QGEMM_NO_ALLOC_SCRATCH_BYTES of include/qgemm.h
 for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run", "qgemm_run_bias",
            "qgemm_run_no_alloc"):
     getattr(_lib, _f).restype = ctypes.c_int

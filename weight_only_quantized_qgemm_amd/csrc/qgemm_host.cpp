@@ -131,7 +131,7 @@ static void finish_split(Plan* pl, int kblocks, int requested) {
   pl->splits = ceil_div(kblocks, pl->kb_per_split);   // no empty split
 }
 
-qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl, bool allow_persist) {
+qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
   std::memset(pl, 0, sizeof(*pl));
   pl->fmt = format_of(p);
   if (p->M == 0) return QGEMM_OK;                    // empty product: no launch, no workspace
@@ -229,16 +229,42 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl, bool allow_persist)
     const double kFill = 3.0, kPartialLatency = 1.5, kBytesPerUs = 5.0e6;
     int best_c = -1, best = 1;
     double best_cost = 0.0;
+    // Persistent schedule with a stream-K tail (split 0 below), on request only
+    // (QGEMM_KERNEL_PREFILL_STREAMK): as many workgroups as are resident at once (one per CU
+    // for the 256- and 128-row tiles, whose A stages take 128 KiB of LDS; two for the 64-row
+    // tile); each takes whole tiles round-robin (the same tile ids, and so the same XCD-aware
+    // walk, as the one-tile launch) for all rounds but the last full one, and the tiles left
+    // (between one and two rounds' worth) are split evenly in K over all of them, so no round
+    // runs partly idle.  Its cost: the k blocks of a workgroup's share plus two pipeline fills,
+    // and about one partial tile per workgroup written and read back at once; the tile is the
+    // one this model prices lowest.  The automatic plan never takes it: measured against the
+    // one-tile launch it was at best even (FP8 32768 x 3200 x 5120, 6.5 rounds: 786.6 vs 786.0
+    // us; 16384 x 12800 x 5120, 12.5 rounds: 1472 vs 1471 us; INT4 4352 x 4096 x 4096, 1.06
+    // rounds: 171.0 vs 171.6 us with the 128 x 128 tile, 204 us with the 256 x 256 tile, whose
+    // workgroup ranges cut nearly every tail tile) -- the chip's clock rises while a last round
+    // runs partly idle -- and the one-tile launch needs no workspace.
+    const bool sk_forced = p->kernel_hint == QGEMM_KERNEL_PREFILL_STREAMK;
     for (int c = 0; c < 3; ++c) {
       const PfShape sh = cands[c].sh;
       if (p->tile_hint ? p->tile_hint != pf_bm(sh) : (c > 0 && p->M <= pf_bm(cands[c - 1].sh))) continue;
       if ((int64_t)pf_bm(sh) * p->K * 2 > 0x7fffffffLL) continue;     // the A tile uses 32-bit offsets
       const int64_t mt = (p->M + pf_bm(sh) - 1) / pf_bm(sh), nt = (p->N + pf_bn(sh) - 1) / pf_bn(sh);
-      for (int s = 1; s <= 64 && (s == 1 || s <= kblocks / 2); ++s) {
-        const double rounds = (double)((mt * nt * s + kCUs - 1) / kCUs);
-        const double partials = (double)(mt * nt * s) * pf_bm(sh) * pf_bn(sh) * 4 * 2 / kBytesPerUs;
-        const double cost = rounds * (ceil_div(kblocks, s) + kFill) * cands[c].t_kb +
-                            (s > 1 ? partials + kPartialLatency * s : 0.0);
+      const int64_t T = mt * nt;
+      const int P = kCUs * (c == 0 ? 2 : 1);
+      for (int s = 0; s <= 64 && (s <= 1 || s <= kblocks / 2); ++s) {
+        double cost;
+        if (s == 0) {                                  // persistent, stream-K tail
+          if (!sk_forced) continue;
+          const int64_t dp = T > P ? (T / P - 1) * P : 0;
+          const double tail = (double)((T - dp) * kblocks) / P;
+          const double handoff = (double)P * pf_bm(sh) * pf_bn(sh) * 4 * 2 / kBytesPerUs + 2 * kPartialLatency;
+          cost = ((double)(dp / P) * (kblocks + kFill) + tail + 2 * kFill) * cands[c].t_kb + handoff;
+        } else {
+          if (sk_forced) continue;
+          const double rounds = (double)((T * s + kCUs - 1) / kCUs);
+          const double partials = (double)(T * s) * pf_bm(sh) * pf_bn(sh) * 4 * 2 / kBytesPerUs;
+          cost = rounds * (ceil_div(kblocks, s) + kFill) * cands[c].t_kb + (s > 1 ? partials + kPartialLatency * s : 0.0);
+        }
         if (best_c < 0 || cost < best_cost) { best_c = c; best = s; best_cost = cost; }
       }
     }
@@ -248,35 +274,16 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl, bool allow_persist)
     pl->bm = pf_bm(cands[best_c].sh);
     pl->bn = pf_bn(cands[best_c].sh);
     const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
-    pl->splits = best;
+    const bool persist = best == 0;
+    pl->splits = persist ? 1 : best;
     finish_split(pl, kblocks, p->split_k_hint);
     if (mt * nt > 0x7fffffffLL) return fail(QGEMM_ERR_UNSUPPORTED, "too many output tiles (%lld)", (long long)(mt * nt));
     pl->grid_x = (unsigned)(mt * nt);
     pl->grid_y = (unsigned)pl->splits;
     pl->tiles = (int)(mt * nt);
     pl->tile_elems = pl->bm * pl->bn;
-    // Persistent schedule with a stream-K tail: as many workgroups as are resident at once
-    // (one per CU for the 256- and 128-row tiles, whose A stages take 128 KiB of LDS; two for
-    // the 64-row tile); each takes whole tiles round-robin (the same tile ids, and so the same
-    // XCD-aware walk, as the one-tile launch) for all rounds but the last full one, and the
-    // tiles left (between one and two rounds' worth) are split evenly in K over all of them,
-    // so no round runs partly idle.  The cost is a partial-tile hand-off for the tail tiles
-    // that a workgroup boundary cuts.  Chosen when the model's time, with the hand-off priced
-    // like split-K's, beats the one-tile launch: the last round must be at most ~3/4 full.
     const int64_t T = mt * nt;
     const int P = kCUs * (pl->bm == pf_bm(kPfSmall) ? 2 : 1);
-    const double t_kb = best_c == 0 ? 0.8 : best_c == 1 ? 1.3 : 3.4;
-    bool persist = p->kernel_hint == QGEMM_KERNEL_PREFILL_STREAMK;
-    if (!persist && allow_persist && p->kernel_hint == QGEMM_KERNEL_AUTO && p->split_k_hint == 0 && pl->splits == 1 && T > P &&
-        T % P != 0) {
-      const double one_tile = (double)((T + P - 1) / P) * (kblocks + kFill) * t_kb;
-      const int64_t dp = (T / P - 1) * P;
-      const double tail = (double)((T - dp) * kblocks) / P;
-      // about one partial tile written per workgroup and read back once, all at the same time
-      const double handoff = (double)P * pl->tile_elems * 4 * 2 / kBytesPerUs + 2 * kPartialLatency;
-      const double streamk = ((double)(dp / P) * (kblocks + kFill) + tail + 2 * kFill) * t_kb + handoff;
-      persist = streamk < one_tile;
-    }
     if (persist) {
       const int64_t dp = T > P ? (T / P - 1) * P : 0;
       if ((T - dp) * kblocks > 0x7fffffffLL)

@@ -122,8 +122,6 @@ struct Plan {
   size_t ws_bytes;        // total workspace (0 when splits == 1)
 };
 
-// allow_persist = false plans the one-tile prefill launch even where the persistent schedule
-// would be chosen (for callers whose workspace cannot hold the stream-K partials).
-qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* plan, bool allow_persist = true);
+qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* plan);
 
 }  // namespace qgemm

@@ -207,11 +207,6 @@ extern "C" qgemm_status_t qgemm_run_no_alloc(const qgemm_problem_t* p, const voi
   Plan pl;
   st = make_plan(p, &pl);
   if (st != QGEMM_OK) return st;
-  if (pl.persist && p->kernel_hint == QGEMM_KERNEL_AUTO &&
-      ((size_t)pl.tiles * 4 > kScratchTicketBytes || pl.ws_bytes - pl.counters_bytes > kScratchBytes - kScratchTicketBytes)) {
-    st = make_plan(p, &pl, false);                   // the one-tile launch of the same tiles
-    if (st != QGEMM_OK) return st;
-  }
   char* sc = nullptr;
   if (pl.ws_bytes) {
     const size_t partial_bytes = pl.ws_bytes - pl.counters_bytes;
