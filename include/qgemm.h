@@ -274,6 +274,19 @@ const char* qgemm_status_string(qgemm_status_t status);
  */
 const char* qgemm_last_error(void);
 
+/*
+ * qgemm_plan_describe -- one NUL-terminated line naming the launch qgemm_run would make for
+ * this problem: the kernel ("decode", "prefill" or "empty" for M = 0), its grid, its K split
+ * and, for decode, the column blocks per workgroup, the k blocks per wavefront run, the runs
+ * per share and how A reaches the MFMA fragments ("a=direct", "a=staged" or "a=dma"); for
+ * prefill, the tile and the persistent schedule.  The dispatch decision of the FlashInfer
+ * PR #4466 analysis, section 2 (preparation and dispatch), made inspectable: the text is
+ * for people and tests, its fields may grow.  `buf` is caller-owned host memory of `len`
+ * bytes; a line that does not fit returns QGEMM_ERR_INVALID_ARGUMENT (buf then holds the
+ * truncated line); an invalid problem returns the status qgemm_workspace_bytes would.
+ */
+qgemm_status_t qgemm_plan_describe(const qgemm_problem_t* problem, char* buf, size_t len);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t qgemm_version(void);
 

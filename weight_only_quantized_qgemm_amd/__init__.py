@@ -57,6 +57,7 @@ _lib.qgemm_workspace_bytes.argtypes = [_P, ctypes.POINTER(_sz)]
 _lib.qgemm_run.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qgemm_run_bias.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qgemm_run_no_alloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.qgemm_plan_describe.argtypes = [_P, ctypes.c_char_p, _sz]
 _lib.qgemm_status_string.argtypes = [ctypes.c_int]
 _lib.qgemm_status_string.restype = ctypes.c_char_p
 _lib.qgemm_last_error.argtypes = []
@@ -64,7 +65,7 @@ _lib.qgemm_last_error.restype = ctypes.c_char_p
 _lib.qgemm_version.restype = ctypes.c_int32
 NO_ALLOC_SCRATCH_BYTES = (32 << 20) + (64 << 10)    # QGEMM_NO_ALLOC_SCRATCH_BYTES of include/qgemm.h
 for _f in ("qgemm_quantize", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_run", "qgemm_run_bias",
-           "qgemm_run_no_alloc"):
+           "qgemm_run_no_alloc", "qgemm_plan_describe"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 lib = _lib
@@ -169,6 +170,19 @@ def workspace_bytes(p):
     n = _sz(0)
     _check(_lib.qgemm_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
     return n.value
+
+
+def plan_describe(p):
+    """The launch qgemm_run would make for this problem, as one line of text."""
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib.qgemm_plan_describe(ctypes.byref(p), buf, 512))
+    return buf.value.decode()
+
+
+def plan_fields(p):
+    """plan_describe as a dict: {"kernel": ..., key: value, ...} (values as text)."""
+    head, *rest = plan_describe(p).split()
+    return {"kernel": head, **dict(f.split("=", 1) for f in rest)}
 
 
 # ----------------------------------------------------------------------------- device calls

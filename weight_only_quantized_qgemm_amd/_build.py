@@ -64,7 +64,9 @@ def build(verbose=False):
             raise RuntimeError(f"hipcc failed on {s} {' '.join(defs)}:\n" + "\n".join(lines))
         msgs += lines
     tmp = LIB + ".tmp"
-    rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose launch stub the host pass did not emit fails here, not at
+    # load time
+    rc, lines = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp])
     if rc != 0:
         raise RuntimeError("link failed:\n" + "\n".join(lines))
     msgs += lines

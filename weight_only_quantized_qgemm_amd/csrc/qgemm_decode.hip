@@ -20,8 +20,13 @@ namespace {
 // however few distinct bytes it carries.  Nothing staged is shared between wavefronts, so no
 // workgroup barrier holds a wavefront back once its own data has arrived.  With larger M
 // the rows are distinct: each wavefront loads its A fragments and its scales from global
-// memory with its weights.  Rows at or beyond M read row M - 1 (MFMA output row m depends
-// on A row m only; rows >= M are never stored).
+// memory with its weights, either straight into registers (A_DIRECT) or, with A_DMA,
+// through buffer-to-LDS DMA into a static LDS slot per k block of the run (4 KiB: 16 rows x
+// 16 chunks of 16 bytes, chunk c of row r at position c ^ r, so that the fragment reads are
+// free of bank conflicts); its fragments are then read from the slot.  A run overlapping the
+// next one uses the other of two slot sets, each its own array, so that the compiler's wait
+// before a slot read covers only the DMA loads of that set.  Rows at or beyond M read row
+// M - 1 (MFMA output row m depends on A row m only; rows >= M are never stored).
 // Control flow is wavefront-uniform and loads are clamped rather than predicated (the
 // compiler waits for every outstanding load at the end of a branch that contains one).
 // Each wavefront keeps two accumulators per column block (even / odd K steps) to halve the
@@ -37,7 +42,7 @@ constexpr bool DEC_ACC2 = true;                     // two accumulators per colu
 // arguments ahead of the full argument block: built with kernarg preloading, the dispatch
 // places them in scalar registers, so the weight and A loads go out without first waiting
 // for a scalar load of the argument block (2-4% of a decode launch).
-template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE, int NR>
+template <int FMT, int G, int CB, int KPW, int NW, int AMODE, int NR>
 __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const void* S, const uint16_t* A,
                                                          const unsigned* code_book, int M, int N, int K,
                                                          int kb_per_split, KArgs a) {
@@ -50,12 +55,16 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   a.K = K;
   a.kb_per_split = kb_per_split;
   constexpr bool MULTI = NR > 1;
+  constexpr bool ASTAGE = AMODE == qgemm::A_STAGED, ADMA = AMODE == qgemm::A_DMA;
   constexpr int NT = 64 * NW;
   // Scales are staged with the A share (small M); otherwise each wavefront loads its own
   // with its weights (staging them alone measured slower at M = 16).
   constexpr bool HAS_S = !qgemm::fp8_weights(FMT) && ASTAGE;
   constexpr bool STAGE = ASTAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char dec_lds[];
+  constexpr int DMA_SET = ADMA ? qgemm::dec_dma_set_bytes(NW, KPW) : 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char Ad0[DMA_SET];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ad1[ADMA && MULTI ? DMA_SET : 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = blockIdx.x, split = blockIdx.y;
@@ -76,9 +85,9 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   Lut lut;                                           // NF4 code book (wavefront-uniform)
   load_lut<FMT>(a, lut);
   const int ldw = share * 128 + 8;                   // LDS A row stride (halves)
-  const int aw_bytes = qgemm::dec_a_bytes(a.M, share, ASTAGE);
+  const int aw_bytes = qgemm::dec_a_bytes(a.M, share, AMODE);
   const int SW = HAS_S ? qgemm::dec_scale_span(FMT, G, share) : 0;   // scale bytes of a share, per column block
-  const int region = qgemm::dec_region_bytes(FMT, G, a.M, share, CB, ASTAGE);
+  const int region = qgemm::dec_region_bytes(FMT, G, a.M, share, CB, AMODE);
   unsigned char* w_lds = dec_lds + wave * region;
   const unsigned char* s_lds = w_lds + aw_bytes;
   f32x4* red = reinterpret_cast<f32x4*>(dec_lds + NW * region);     // [NW][CB][64]
@@ -146,10 +155,36 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   const int last = max(w_end - 1, w_begin);          // clamp target (valid even for an empty share)
   const int kb_cap = min(last, KB - 1);
 
+  // A_DMA: load j (0..3) of a k block fills bytes [1024 j, +1024) of its slot, lane l the 16
+  // bytes at 16 l: row r = 4 j + l / 16, position l & 15, which holds source chunk
+  // (l & 15) ^ r of row min(r, M - 1) (the k block's byte offset goes in the scalar offset).
+  // Fragment read t of a lane: row l & 15, source chunk 4 t + l / 16.
+  int aoff[ADMA ? 4 : 1];
+  __amdgpu_buffer_rsrc_t drsrc;
+  if constexpr (ADMA) {
+    drsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.A), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aoff[t] = (lane & 15) * 256 + 16 * ((4 * t + (lane >> 4)) ^ (lane & 15));
+  }
+  auto dma_slot = [&](unsigned char* set, int u) { return set + (wave * KPW + u) * 4096; };
+
   // one run: loads first (A fragments, then weights), then the k blocks in load order,
   // each waiting only for its own data
-  auto run_loads = [&](int run, u32x4 (&afr)[ASTAGE ? 1 : KPW][4], WFrag<FMT> (&wf)[KPW][CB]) {
-    if constexpr (!ASTAGE) {
+  constexpr int NAF = AMODE == qgemm::A_DIRECT ? KPW : 1;
+  auto run_loads = [&](int run, u32x4 (&afr)[NAF][4], WFrag<FMT> (&wf)[KPW][CB], unsigned char* set) {
+    if constexpr (ADMA) {
+#pragma unroll
+      for (int u = 0; u < KPW; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // the source offset is written out here: taken from a captured array or lambda, it
+          // makes the host pass drop the kernel's launch stub
+          const int r = 4 * j + (lane >> 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(drsrc, (lds_ptr_t)(dma_slot(set, u) + 1024 * j), 16,
+                                                   min(r, a.M - 1) * a.K * 2 + 16 * ((lane & 15) ^ r),
+                                                   min(run + u, kb_cap) * 256, 0, 0);
+        }
+    } else if constexpr (AMODE == qgemm::A_DIRECT) {
 #pragma unroll
       for (int u = 0; u < KPW; ++u) {
         const u32x4* ap = reinterpret_cast<const u32x4*>(arow_g + (size_t)min(run + u, kb_cap) * 128);
@@ -167,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   // MULTI: no branch around a k block (the compiler would wait for every load in flight,
   // the next run's included, at its end); a block past the share multiplies a zero A
   // fragment instead, and the staged reads stay inside the staged slice.
-  auto run_compute = [&](int run, const u32x4 (&afr)[ASTAGE ? 1 : KPW][4], WFrag<FMT> (&wf)[KPW][CB]) {
+  auto run_compute = [&](int run, const u32x4 (&afr)[NAF][4], WFrag<FMT> (&wf)[KPW][CB], const unsigned char* set) {
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
       const bool valid = run + u < w_end;
@@ -178,9 +213,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
           const uint16_t* ap = arow_l + (kbl - w_begin) * 128;
 #pragma unroll
           for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const u32x4*>(ap + 32 * t);
+        } else if constexpr (ADMA) {
+          const unsigned char* ap = set + (wave * KPW + u) * 4096;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const u32x4*>(ap + aoff[t]);
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) al[t] = afr[ASTAGE ? 0 : u][t];
+          for (int t = 0; t < 4; ++t) al[t] = afr[u][t];
         }
         if constexpr (MULTI) {
 #pragma unroll
@@ -208,10 +247,10 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
     }
   };
 
-  u32x4 afr[MULTI ? 2 : 1][ASTAGE ? 1 : KPW][4];
+  u32x4 afr[MULTI ? 2 : 1][NAF][4];
   WFrag<FMT> wf[MULTI ? 2 : 1][KPW][CB];
   // first run (every wavefront, with or without k blocks), then the staged share lands in LDS
-  run_loads(w_begin, afr[0], wf[0]);
+  run_loads(w_begin, afr[0], wf[0], Ad0);
   if constexpr (STAGE) {
 #pragma unroll
     for (int i = 0; i < SA + SS; ++i)
@@ -220,19 +259,22 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
     __builtin_amdgcn_wave_barrier();
   }
   if constexpr (!MULTI) {
-    if (w_begin < w_end) run_compute(w_begin, afr[0], wf[0]);
+    if (w_begin < w_end) run_compute(w_begin, afr[0], wf[0], Ad0);
     for (int run = w_begin + KPW; run < w_end; run += KPW) {
-      run_loads(run, afr[0], wf[0]);
-      run_compute(run, afr[0], wf[0]);
+      run_loads(run, afr[0], wf[0], Ad0);           // the previous run's slot reads fed its MFMAs already
+      run_compute(run, afr[0], wf[0], Ad0);
     }
   } else {
-    run_loads(w_begin + KPW, afr[1], wf[1]);
+    run_loads(w_begin + KPW, afr[1], wf[1], Ad1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      run_compute(w_begin + r * KPW, afr[r & 1], wf[r & 1]);
-      if (r + 2 < NR) run_loads(w_begin + (r + 2) * KPW, afr[r & 1], wf[r & 1]);
+      run_compute(w_begin + r * KPW, afr[r & 1], wf[r & 1], (r & 1) ? Ad1 : Ad0);
+      if (r + 2 < NR) run_loads(w_begin + (r + 2) * KPW, afr[r & 1], wf[r & 1], (r & 1) ? Ad1 : Ad0);
     }
   }
+  // A_DMA: slots of k blocks past the share may still be filling; the workgroup's LDS must
+  // not be released under them.
+  if constexpr (ADMA) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt left open
 
 #pragma unroll
   for (int c = 0; c < CB; ++c) red[(wave * CB + c) * 64 + lane] = DEC_ACC2 ? acc[c][0] + acc[c][1] : acc[c][0];
@@ -264,48 +306,63 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   }
 }
 
-template <int FMT, int G, int CB, int KPW, int NW, bool ASTAGE>
-void launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  const dim3 grid(pl.grid_x, pl.grid_y), block(64 * NW);
-  const size_t lds = pl.lds_bytes;
+template <int FMT, int G, int CB, int KPW, int NW, int AMODE, int NR>
+bool launch_one(const Plan& pl, const KArgs& a, hipStream_t stream) {
+  if constexpr (AMODE == qgemm::A_DMA && !qgemm::dec_dma_fits(NW, KPW, CB, NR)) {
+    return false;                                    // not instantiated; never planned
+  } else {
+    hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, AMODE, NR>), dim3(pl.grid_x, pl.grid_y), dim3(64 * NW),
+                       pl.lds_bytes, stream, a.W, a.S, a.A, a.lut, a.M, a.N, a.K, a.kb_per_split, a);
+    return true;
+  }
+}
+
+template <int FMT, int G, int CB, int KPW, int NW, int AMODE>
+bool launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
   switch (pl.nruns) {
-    case 2: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 2>), grid, block, lds, stream, a.W, a.S, a.A, a.lut, a.M, a.N, a.K, a.kb_per_split, a); break;
-    case 3: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 3>), grid, block, lds, stream, a.W, a.S, a.A, a.lut, a.M, a.N, a.K, a.kb_per_split, a); break;
-    case 4: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 4>), grid, block, lds, stream, a.W, a.S, a.A, a.lut, a.M, a.N, a.K, a.kb_per_split, a); break;
-    default: hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, ASTAGE, 1>), grid, block, lds, stream, a.W, a.S, a.A, a.lut, a.M, a.N, a.K, a.kb_per_split, a);
+    case 2: return launch_one<FMT, G, CB, KPW, NW, AMODE, 2>(pl, a, stream);
+    case 3: return launch_one<FMT, G, CB, KPW, NW, AMODE, 3>(pl, a, stream);
+    case 4: return launch_one<FMT, G, CB, KPW, NW, AMODE, 4>(pl, a, stream);
+    default: return launch_one<FMT, G, CB, KPW, NW, AMODE, 1>(pl, a, stream);
   }
 }
 
 // Staged A always runs kDecodeWaves wavefronts; unstaged A with two or more column blocks
 // runs kDecodeWavesWide (the plan's nw says which).
+template <int FMT, int G, int CB, int KPW, int NW>
+bool launch_unstaged(const Plan& pl, const KArgs& a, hipStream_t stream) {
+  if (pl.amode == qgemm::A_DMA) return launch_nr<FMT, G, CB, KPW, NW, qgemm::A_DMA>(pl, a, stream);
+  return launch_nr<FMT, G, CB, KPW, NW, qgemm::A_DIRECT>(pl, a, stream);
+}
 template <int FMT, int G, int CB, int KPW>
-void launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  if (pl.astage)
-    launch_nr<FMT, G, CB, KPW, kDecodeWaves, true>(pl, a, stream);
-  else if constexpr (CB >= 2)
-    launch_nr<FMT, G, CB, KPW, kDecodeWavesWide, false>(pl, a, stream);
+bool launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {
+  if (pl.amode == qgemm::A_STAGED) return launch_nr<FMT, G, CB, KPW, kDecodeWaves, qgemm::A_STAGED>(pl, a, stream);
+  if constexpr (CB >= 2)
+    return launch_unstaged<FMT, G, CB, KPW, kDecodeWavesWide>(pl, a, stream);
   else
-    launch_nr<FMT, G, CB, KPW, kDecodeWaves, false>(pl, a, stream);
+    return launch_unstaged<FMT, G, CB, KPW, kDecodeWaves>(pl, a, stream);
 }
 
 template <int FMT, int G>
 struct DecodeLauncher {
   static hipError_t run(const Plan& pl, const KArgs& a, hipStream_t stream) {
+    bool ok = false;
     switch (pl.cb * 16 + pl.kpw) {
-      case 16 + 8: launch_cb<FMT, G, 1, 8>(pl, a, stream); break;
-      case 16 + 5: launch_cb<FMT, G, 1, 5>(pl, a, stream); break;
-      case 16 + 4: launch_cb<FMT, G, 1, 4>(pl, a, stream); break;
-      case 16 + 2: launch_cb<FMT, G, 1, 2>(pl, a, stream); break;
-      case 16 + 1: launch_cb<FMT, G, 1, 1>(pl, a, stream); break;
-      case 32 + 4: launch_cb<FMT, G, 2, 4>(pl, a, stream); break;
-      case 32 + 2: launch_cb<FMT, G, 2, 2>(pl, a, stream); break;
-      case 32 + 1: launch_cb<FMT, G, 2, 1>(pl, a, stream); break;
-      case 48 + 2: launch_cb<FMT, G, 3, 2>(pl, a, stream); break;
-      case 48 + 1: launch_cb<FMT, G, 3, 1>(pl, a, stream); break;
-      case 64 + 2: launch_cb<FMT, G, 4, 2>(pl, a, stream); break;
-      case 64 + 1: launch_cb<FMT, G, 4, 1>(pl, a, stream); break;
-      default: return hipErrorInvalidConfiguration;
+      case 16 + 8: ok = launch_cb<FMT, G, 1, 8>(pl, a, stream); break;
+      case 16 + 5: ok = launch_cb<FMT, G, 1, 5>(pl, a, stream); break;
+      case 16 + 4: ok = launch_cb<FMT, G, 1, 4>(pl, a, stream); break;
+      case 16 + 2: ok = launch_cb<FMT, G, 1, 2>(pl, a, stream); break;
+      case 16 + 1: ok = launch_cb<FMT, G, 1, 1>(pl, a, stream); break;
+      case 32 + 4: ok = launch_cb<FMT, G, 2, 4>(pl, a, stream); break;
+      case 32 + 2: ok = launch_cb<FMT, G, 2, 2>(pl, a, stream); break;
+      case 32 + 1: ok = launch_cb<FMT, G, 2, 1>(pl, a, stream); break;
+      case 48 + 2: ok = launch_cb<FMT, G, 3, 2>(pl, a, stream); break;
+      case 48 + 1: ok = launch_cb<FMT, G, 3, 1>(pl, a, stream); break;
+      case 64 + 2: ok = launch_cb<FMT, G, 4, 2>(pl, a, stream); break;
+      case 64 + 1: ok = launch_cb<FMT, G, 4, 1>(pl, a, stream); break;
+      default: ok = false;
     }
+    if (!ok) return hipErrorInvalidConfiguration;
     return hipGetLastError();
   }
 };

@@ -55,6 +55,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// LDS destination of a buffer-to-LDS DMA load
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct KArgs {
   const uint16_t* A;          // [M][K] 16-bit

@@ -183,29 +183,41 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     if (pl->kb_per_split > max_kb)
       return fail(QGEMM_ERR_INVALID_ARGUMENT, "split_k_hint %d leaves %d k blocks per slice; the decode kernel "
                   "stages at most %d at M=%lld", p->split_k_hint, pl->kb_per_split, max_kb, (long long)p->M);
-    pl->lds_bytes = dec_lds_bytes(pl->fmt, p->group_size, (int)p->M, ceil_div(pl->kb_per_split, pl->nw),
-                                  pl->cb, pl->astage, pl->nw);
     // Each wavefront owns ceil(kb_per_split / waves) consecutive k blocks, streamed in runs
     // of KPW (at most 8 weight blocks in flight per wavefront): the whole share in one run
     // when an instance exists for it, else the largest instance below.  A share longer
-    // than one run alternates two register sets, each KPW x (4 A fragments unless A is
-    // staged + CB weight fragments of 5 registers, FP8 8); the run is shortened until both
-    // sets fit in 210 registers (measured: more spills).
+    // than one run alternates two register sets, each KPW x (4 A fragments when A is loaded
+    // straight into registers + CB weight fragments of 5 registers, FP8 8); the run is
+    // shortened until both sets fit in 210 registers (measured: more spills).
     const int share = ceil_div(pl->kb_per_split, pl->nw);
     static const int kRuns[] = {8, 5, 4, 2, 1};            // instantiated KPW values
     auto instantiated = [&](int k) {
       return k * pl->cb <= 8 && (k != 5 || pl->cb == 1) && (k != 8 || pl->cb == 1);
     };
-    auto fits_twice = [&](int k) {
-      const int wregs = fp8_weights(pl->fmt) ? 8 : 5;
-      const int budget = pl->fmt == FMT_NF4 ? 202 : 210;     // NF4 keeps its code book in 8 registers
-      return 2 * k * ((pl->astage ? 0 : 16) + pl->cb * wregs) <= budget;
+    auto choose_runs = [&](int amode) {
+      auto fits_twice = [&](int k) {
+        const int wregs = fp8_weights(pl->fmt) ? 8 : 5;
+        const int budget = pl->fmt == FMT_NF4 ? 202 : 210;   // NF4 keeps its code book in 8 registers
+        return 2 * k * ((amode == A_DIRECT ? 16 : 0) + pl->cb * wregs) <= budget;
+      };
+      pl->kpw = 1;
+      for (int k : kRuns)
+        if (instantiated(k) && k <= share && (k == share || (k < share && fits_twice(k)))) { pl->kpw = k; break; }
+      const int runs = ceil_div(share, pl->kpw);
+      pl->nruns = runs >= 2 && runs <= 4 ? runs : 1;
+      pl->amode = amode;
+      pl->lds_bytes = dec_lds_bytes(pl->fmt, p->group_size, (int)p->M, share, pl->cb, amode, pl->nw);
     };
-    pl->kpw = 1;
-    for (int k : kRuns)
-      if (instantiated(k) && k <= share && (k == share || (k < share && fits_twice(k)))) { pl->kpw = k; break; }
-    const int runs = ceil_div(share, pl->kpw);
-    pl->nruns = runs >= 2 && runs <= 4 ? runs : 1;
+    // Above the staging limit A goes through buffer-to-LDS DMA when its slots (one or two sets
+    // of KPW k blocks per wavefront, next to the wave tiles) fit in LDS: a DMA load reads 256
+    // contiguous bytes from each of 4 rows (8 whole cache lines) where a fragment load reads
+    // 64 bytes from each of 16 rows (16 half lines), for the same kilobyte.
+    if (pl->astage) {
+      choose_runs(A_STAGED);
+    } else {
+      choose_runs(QGEMM_DEC_ADMA ? A_DMA : A_DIRECT);
+      if (pl->amode == A_DMA && !dec_dma_fits(pl->nw, pl->kpw, pl->cb, pl->nruns)) choose_runs(A_DIRECT);
+    }
     pl->grid_x = (unsigned)groups;
     pl->grid_y = (unsigned)pl->splits;
     pl->tiles = groups;
@@ -435,6 +447,32 @@ qgemm_status_t qgemm_workspace_bytes(const qgemm_problem_t* p, size_t* bytes) {
   st = make_plan(p, &pl);
   if (st != QGEMM_OK) return st;
   *bytes = pl.ws_bytes;
+  return QGEMM_OK;
+}
+
+qgemm_status_t qgemm_plan_describe(const qgemm_problem_t* p, char* buf, size_t len) {
+  clear_error();
+  if (!buf || len == 0) return fail(QGEMM_ERR_INVALID_ARGUMENT, "buf is NULL or len is 0");
+  buf[0] = '\0';
+  qgemm_status_t st = validate_problem(p);
+  if (st != QGEMM_OK) return st;
+  Plan pl;
+  st = make_plan(p, &pl);
+  if (st != QGEMM_OK) return st;
+  int n;
+  if (p->M == 0) {
+    n = std::snprintf(buf, len, "empty");
+  } else if (pl.kind == KIND_DECODE) {
+    static const char* const kA[] = {"direct", "staged", "dma"};
+    n = std::snprintf(buf, len, "decode grid=%ux%u waves=%d cb=%d kpw=%d runs=%d a=%s splits=%d kb_per_split=%d "
+                      "lds=%d ws=%zu", pl.grid_x, pl.grid_y, pl.nw, pl.cb, pl.kpw, pl.nruns, kA[pl.amode], pl.splits,
+                      pl.kb_per_split, pl.lds_bytes, pl.ws_bytes);
+  } else {
+    n = std::snprintf(buf, len, "prefill grid=%ux%u tile=%dx%d splits=%d kb_per_split=%d persist=%d dp_tiles=%d "
+                      "ws=%zu", pl.grid_x, pl.grid_y, pl.bm, pl.bn, pl.splits, pl.kb_per_split, pl.persist,
+                      pl.dp_tiles, pl.ws_bytes);
+  }
+  if (n < 0 || (size_t)n >= len) return fail(QGEMM_ERR_INVALID_ARGUMENT, "len %zu is too small (needs %d)", len, n + 1);
   return QGEMM_OK;
 }
 

@@ -46,6 +46,11 @@ constexpr int kDecodeMaxA = QGEMM_DEC_MAXA;
 constexpr int kDecodeMaxScales = 16 * 1024;
 constexpr int kDecodeStageA = kDecodeMaxA / (16 * 64 * kDecodeWaves);
 constexpr int kDecodeStageS = kDecodeMaxScales / (16 * 64 * kDecodeWaves);
+// Decode with M above the staging limit takes A through buffer-to-LDS DMA when its slots fit
+// (0 turns it off).
+#ifndef QGEMM_DEC_ADMA
+#define QGEMM_DEC_ADMA 1
+#endif
 
 // Kernel formats.  FMT_FP8H is FP8 weights with fp16 activations (mm_fp16_fp8): the weight
 // layout, quantization and alpha are FP8's, the MFMA is the fp16 one.  FMT_INT2 (W2A16)
@@ -68,21 +73,36 @@ constexpr int dec_scale_span(int fmt, int group_size, int nkb) {
          : group_size <= 128 ? 32 * (128 / group_size) * nkb
                              : 32 * (nkb / 2 + 1);
 }
-// Per wavefront: its A share (M rows of share x 128 + 8 halves) and its scales (cb column
-// blocks), each padded to 16 bytes.
-constexpr int dec_a_bytes(int M, int share, bool astage) {
-  return astage ? (M * (share * 128 + 8) * 2 + 15) / 16 * 16 : 0;
+// How a decode wavefront gets its A fragments: straight from memory into registers
+// (A_DIRECT), from its private LDS region after a register-staged copy of its whole A share
+// and scales (A_STAGED, small M), or from LDS slots that buffer-to-LDS DMA fills run by run,
+// 4 KiB (16 rows x 128 halves) per k block (A_DMA, larger M).  The A_DMA slots are static
+// arrays of the kernel instance, not part of the dynamic region below.
+enum AMode : int { A_DIRECT = 0, A_STAGED = 1, A_DMA = 2 };
+// LDS a workgroup may take (160 KiB on gfx950).
+constexpr int kMaxLds = 160 * 1024;
+// A_DMA: bytes of one slot set (one k block per wavefront and run position); a kernel that
+// overlaps runs (two or more runs per share) holds two sets.  An instance exists, and the plan
+// takes A_DMA, only when its sets and the wave tiles of the final reduction fit in LDS.
+constexpr int dec_dma_set_bytes(int waves, int kpw) { return waves * kpw * 4096; }
+constexpr bool dec_dma_fits(int waves, int kpw, int cb, int nruns) {
+  return (nruns > 1 ? 2 : 1) * dec_dma_set_bytes(waves, kpw) + waves * cb * 64 * 16 <= kMaxLds;
 }
-constexpr int dec_s_bytes(int fmt, int group_size, int share, int cb, bool astage) {
-  return astage ? (cb * dec_scale_span(fmt, group_size, share) + 15) / 16 * 16 : 0;
+// Per wavefront (dynamic region): its staged A share (M rows of share x 128 + 8 halves) and
+// its staged scales (cb column blocks), each padded to 16 bytes; A_STAGED only.
+constexpr int dec_a_bytes(int M, int share, int amode) {
+  return amode == A_STAGED ? (M * (share * 128 + 8) * 2 + 15) / 16 * 16 : 0;
 }
-constexpr int dec_region_bytes(int fmt, int group_size, int M, int share, int cb, bool astage) {
-  return dec_a_bytes(M, share, astage) + dec_s_bytes(fmt, group_size, share, cb, astage);
+constexpr int dec_s_bytes(int fmt, int group_size, int share, int cb, int amode) {
+  return amode == A_STAGED ? (cb * dec_scale_span(fmt, group_size, share) + 15) / 16 * 16 : 0;
+}
+constexpr int dec_region_bytes(int fmt, int group_size, int M, int share, int cb, int amode) {
+  return dec_a_bytes(M, share, amode) + dec_s_bytes(fmt, group_size, share, cb, amode);
 }
 // Whole workgroup: the regions, then the wave tiles of the final reduction (64 lanes x 16 B
 // per wavefront and column block).
-constexpr int dec_lds_bytes(int fmt, int group_size, int M, int share, int cb, bool astage, int waves) {
-  return waves * dec_region_bytes(fmt, group_size, M, share, cb, astage) + waves * cb * 64 * 16;
+constexpr int dec_lds_bytes(int fmt, int group_size, int M, int share, int cb, int amode, int waves) {
+  return waves * dec_region_bytes(fmt, group_size, M, share, cb, amode) + waves * cb * 64 * 16;
 }
 enum Kind : int { KIND_DECODE = 1, KIND_PREFILL = 2 };
 
@@ -101,6 +121,7 @@ struct Plan {
   // decode: column blocks (16 columns each) per workgroup, k blocks per wavefront run
   int cb, kpw;
   bool astage;            // decode: stage the A slice in LDS (small M)
+  int amode;              // decode: AMode (A_STAGED when astage)
   int nw;                 // decode: wavefronts per workgroup
   int nruns;              // decode: runs per wavefront share, pipelined when 2..4 (else 1)
   int lds_bytes;          // decode: dynamic LDS per workgroup (staged A, staged scales, wave tiles)

@@ -34,7 +34,6 @@ namespace {
 // load is unconditional (the last step re-loads its own block, never used) and
 // sched_barrier pins the phase order (a load under a branch, or a consumer scheduled
 // early, would make the wavefront wait for all outstanding loads).
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Workgroup barrier without the release fence of __syncthreads(), which waits for every
 // outstanding load, the A stages still meant to be in flight included.  Callers first
