@@ -230,3 +230,51 @@ def test_planner_sweep_sizes_are_consistent():
                     assert ws >= 0
                     if hint == 3:
                         assert ws > 0
+
+
+def test_plan_describe_fields_and_errors():
+    # qgemm_plan_describe: one line naming the kernel and its launch; an invalid problem
+    # returns the validation status, a buffer too small for the line QGEMM_ERR_INVALID_ARGUMENT.
+    import ctypes
+    assert q.plan_describe(q.problem(0, 256, 512, "int4")) == "empty"
+    d = q.plan_fields(q.problem(16, 4096, 4096, "int4"))
+    assert d["kernel"] == "decode" and d["a"] == "dma" and int(d["splits"]) >= 1
+    assert q.plan_fields(q.problem(1, 4096, 4096, "int4"))["a"] == "staged"
+    d = q.plan_fields(q.problem(4096, 4096, 4096, "int4"))
+    assert d["kernel"] == "prefill" and d["tile"] in ("64x128", "128x128", "256x256")
+    assert q.plan_fields(q.problem(2176, 2048, 1024, "int4", kernel_hint=3))["persist"] != "0"
+    with pytest.raises(q.QgemmError) as e:
+        q.plan_describe(q.problem(16, 250, 512, "int4"))
+    assert e.value.status == q.ERR_INVALID_ARGUMENT
+    p = q.problem(16, 4096, 4096, "int4")
+    buf = ctypes.create_string_buffer(8)
+    assert q.lib.qgemm_plan_describe(ctypes.byref(p), buf, 8) == q.ERR_INVALID_ARGUMENT
+    assert len(buf.value) == 7                        # truncated, still NUL-terminated
+    assert q.lib.qgemm_plan_describe(ctypes.byref(p), None, 64) == q.ERR_INVALID_ARGUMENT
+
+
+def test_decode_plans_fit_lds_and_take_dma_above_staging():
+    # Decode plans: A is staged for M <= 4 and goes through the DMA slots above; the slots (two
+    # sets when runs overlap), the dynamic region and the 2 KiB reserve for the kernel's other
+    # LDS fit the 160 KiB of a workgroup; runs of KPW k blocks cover each wavefront's share.
+    for fmt in ("int4", "int2", "nf4", "fp8", "fp8h", "fp4"):
+        for M in (1, 4, 5, 9, 16):
+            for N, K in ((16, 128), (272, 768), (4096, 4096), (11008, 4096), (4096, 14336), (12800, 5120),
+                         (28672, 8192), (256, 131072)):
+                for tile, split in ((0, 0), (1, 0), (4, 0), (2, 3)):
+                    p = q.problem(M, N, K, fmt, kernel_hint=q.KERNEL_DECODE, tile_hint=tile, split_k_hint=split)
+                    try:
+                        d = q.plan_fields(p)
+                    except q.QgemmError as e:
+                        # a split hint too coarse for staging, or finer than K
+                        assert "stages at most" in e.detail or "exceeds the" in e.detail, e.detail
+                        continue
+                    assert d["kernel"] == "decode"
+                    assert d["a"] == ("staged" if M <= 4 else "dma"), (fmt, M, N, K, d)
+                    waves, kpw, runs = int(d["waves"]), int(d["kpw"]), int(d["runs"])
+                    share = -(-int(d["kb_per_split"]) // waves)
+                    assert 1 <= kpw <= share or share == 0
+                    assert runs == 1 or (2 <= runs <= 4 and -(-share // kpw) == runs)
+                    if d["a"] == "dma":
+                        sets = 2 if runs > 1 else 1
+                        assert sets * waves * kpw * 4096 + int(d["lds"]) + 2048 <= 160 * 1024, (fmt, M, N, K, d)

@@ -167,6 +167,39 @@ def test_decode_multi_run(q, fmt, G, M, N, K):
     check_against_oracle(q, prep, A)
 
 
+DMA_CASES = [
+    # (format, G, M, N, K, expected plan: cb, kpw, runs, splits) -- every case takes A through
+    # the DMA slots; together they cover one run per share (with wavefronts whose share is
+    # empty), two slot sets alternating over 2, 3 and 4 runs, shares ending mid-run, runs one
+    # after another reusing one set, runs shortened to fit LDS, split K, 1 to 4 column blocks.
+    ("int4", 128, 5, 256, 512, (1, 1, 1, 1)),       # 4 k blocks over 8 wavefronts
+    ("int4", 64, 16, 2048, 5120, (1, 2, 3, 1)),     # share 5 in runs of 2
+    ("nf4", 32, 9, 1024, 5120, (1, 2, 2, 2)),       # split K, share 3
+    ("int4", 128, 16, 2048, 16384, (1, 2, 1, 1)),   # share 16: eight runs, one slot set
+    ("fp8", None, 16, 4096, 8192, (1, 2, 4, 1)),    # runs shortened from 8 to fit LDS
+    ("fp4", None, 12, 4352, 2944, (2, 4, 2, 1)),
+    ("int2", 32, 16, 8448, 2048, (3, 2, 2, 1)),
+    ("fp8h", None, 7, 12288, 1024, (3, 2, 1, 1)),
+    ("int4", 256, 16, 16384, 2048, (4, 2, 2, 1)),
+    ("fp4", None, 16, 1024, 16384, (1, 2, 4, 2)),
+    ("nf4", 128, 13, 4096, 3072, (1, 2, 2, 1)),
+]
+
+
+@pytest.mark.parametrize("fmt,G,M,N,K,plan", DMA_CASES,
+                         ids=[f"{c[0]}-{c[2]}x{c[3]}x{c[4]}" for c in DMA_CASES])
+def test_decode_dma_paths(q, fmt, G, M, N, K, plan):
+    # The decode kernel with A in DMA-filled LDS slots, in each launch shape the planner makes
+    # (checked through qgemm_plan_describe), every row against the fp64 oracle.
+    d = q.plan_fields(q.problem(M, N, K, fmt, group_size=G))
+    got = tuple(int(d[k]) for k in ("cb", "kpw", "runs", "splits"))
+    assert d["kernel"] == "decode" and d["a"] == "dma" and got == plan, d
+    say(f"case decode-dma fmt={fmt} G={G} M={M} N={N} K={K} plan={d}")
+    prep = Prepared(q, fmt, N, K, G or 0, (64, N, K))
+    A = _act(fmt, M, K, (64, M))
+    check_against_oracle(q, prep, A)
+
+
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int2", 32), ("nf4", 64), ("fp8", None),
                                    ("fp4", None)])
 @pytest.mark.parametrize("tile,split", [(64, 1), (64, 3), (128, 1), (128, 3), (256, 1), (256, 3)])

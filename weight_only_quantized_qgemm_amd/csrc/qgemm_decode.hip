@@ -157,8 +157,11 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
 
   // A_DMA: load j (0..3) of a k block fills bytes [1024 j, +1024) of its slot, lane l the 16
   // bytes at 16 l: row r = 4 j + l / 16, position l & 15, which holds source chunk
-  // (l & 15) ^ r of row min(r, M - 1) (the k block's byte offset goes in the scalar offset).
-  // Fragment read t of a lane: row l & 15, source chunk 4 t + l / 16.
+  // (l & 15) ^ r of row min(r, M - 1) (the k block's byte offset goes in the scalar offset;
+  // fetching nothing for rows >= M instead, through offsets past a bounded resource, measured
+  // no faster at M = 5..12).  Fragment read t of a lane: row l & 15, source chunk 4 t + l / 16.
+  // The A slots of a run go out before its weights: issued after them, they made the first
+  // k block wait for the whole run's weights (M = 16, N = 4096: 5.4 -> 5.9 us).
   int aoff[ADMA ? 4 : 1];
   __amdgpu_buffer_rsrc_t drsrc;
   if constexpr (ADMA) {
@@ -311,6 +314,16 @@ bool launch_one(const Plan& pl, const KArgs& a, hipStream_t stream) {
   if constexpr (AMODE == qgemm::A_DMA && !qgemm::dec_dma_fits(NW, KPW, CB, NR)) {
     return false;                                    // not instantiated; never planned
   } else {
+    // The instance's static LDS (slot sets, flags) plus the plan's dynamic region must fit the
+    // workgroup limit: a larger request fails at dispatch, after the call has returned.
+    static const size_t static_lds = [] {
+      hipFuncAttributes at{};
+      return hipFuncGetAttributes(&at, reinterpret_cast<const void*>(&qgemm_decode<FMT, G, CB, KPW, NW, AMODE, NR>)) ==
+                     hipSuccess
+                 ? at.sharedSizeBytes
+                 : (size_t)qgemm::kMaxLds + 1;
+    }();
+    if (static_lds + (size_t)pl.lds_bytes > (size_t)qgemm::kMaxLds) return false;
     hipLaunchKernelGGL((qgemm_decode<FMT, G, CB, KPW, NW, AMODE, NR>), dim3(pl.grid_x, pl.grid_y), dim3(64 * NW),
                        pl.lds_bytes, stream, a.W, a.S, a.A, a.lut, a.M, a.N, a.K, a.kb_per_split, a);
     return true;
@@ -329,10 +342,13 @@ bool launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
 
 // Staged A always runs kDecodeWaves wavefronts; unstaged A with two or more column blocks
 // runs kDecodeWavesWide (the plan's nw says which).
+// Only the A path the build plans is instantiated (A_DIRECT only when built with the DMA path
+// off, QGEMM_DEC_ADMA=0); a plan for the other one is refused.
 template <int FMT, int G, int CB, int KPW, int NW>
 bool launch_unstaged(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  if (pl.amode == qgemm::A_DMA) return launch_nr<FMT, G, CB, KPW, NW, qgemm::A_DMA>(pl, a, stream);
-  return launch_nr<FMT, G, CB, KPW, NW, qgemm::A_DIRECT>(pl, a, stream);
+  constexpr int kPath = QGEMM_DEC_ADMA ? qgemm::A_DMA : qgemm::A_DIRECT;
+  if (pl.amode != kPath) return false;
+  return launch_nr<FMT, G, CB, KPW, NW, kPath>(pl, a, stream);
 }
 template <int FMT, int G, int CB, int KPW>
 bool launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {

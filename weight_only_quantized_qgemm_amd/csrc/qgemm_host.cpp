@@ -194,7 +194,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     auto instantiated = [&](int k) {
       return k * pl->cb <= 8 && (k != 5 || pl->cb == 1) && (k != 8 || pl->cb == 1);
     };
-    auto choose_runs = [&](int amode) {
+    auto choose_runs = [&](int amode, int kmax) {
       auto fits_twice = [&](int k) {
         const int wregs = fp8_weights(pl->fmt) ? 8 : 5;
         const int budget = pl->fmt == FMT_NF4 ? 202 : 210;   // NF4 keeps its code book in 8 registers
@@ -202,7 +202,10 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       };
       pl->kpw = 1;
       for (int k : kRuns)
-        if (instantiated(k) && k <= share && (k == share || (k < share && fits_twice(k)))) { pl->kpw = k; break; }
+        if (k <= kmax && instantiated(k) && k <= share && (k == share || (k < share && fits_twice(k)))) {
+          pl->kpw = k;
+          break;
+        }
       const int runs = ceil_div(share, pl->kpw);
       pl->nruns = runs >= 2 && runs <= 4 ? runs : 1;
       pl->amode = amode;
@@ -211,12 +214,20 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // Above the staging limit A goes through buffer-to-LDS DMA when its slots (one or two sets
     // of KPW k blocks per wavefront, next to the wave tiles) fit in LDS: a DMA load reads 256
     // contiguous bytes from each of 4 rows (8 whole cache lines) where a fragment load reads
-    // 64 bytes from each of 16 rows (16 half lines), for the same kilobyte.
+    // 64 bytes from each of 16 rows (16 half lines), for the same kilobyte (M = 16: N = 4096
+    // 6.9 -> 5.5 us, N = 11008 9.1 -> 8.3 us; FP4 8192 x 8192 16.4 -> 13.0 us).
     if (pl->astage) {
-      choose_runs(A_STAGED);
+      choose_runs(A_STAGED, 8);
     } else {
-      choose_runs(QGEMM_DEC_ADMA ? A_DMA : A_DIRECT);
-      if (pl->amode == A_DMA && !dec_dma_fits(pl->nw, pl->kpw, pl->cb, pl->nruns)) choose_runs(A_DIRECT);
+      // Runs are shortened until the slots fit (M = 16, N = 4096: K = 8192 11.6 -> 8.5 us with
+      // runs of 2 instead of direct runs of 8, K = 14336 18.5 -> 12.4 us); runs of one k block
+      // always fit (two sets of 8 x 4 KiB at most).
+      choose_runs(QGEMM_DEC_ADMA ? A_DMA : A_DIRECT, 8);
+      while (pl->amode == A_DMA && pl->kpw > 1 && !dec_dma_fits(pl->nw, pl->kpw, pl->cb, pl->nruns))
+        choose_runs(A_DMA, pl->kpw - 1);
+      if (pl->amode == A_DMA && !dec_dma_fits(pl->nw, pl->kpw, pl->cb, pl->nruns))
+        return fail(QGEMM_ERR_UNSUPPORTED, "decode A slots of %d wavefronts x %d column blocks do not fit in LDS",
+                    pl->nw, pl->cb);
     }
     pl->grid_x = (unsigned)groups;
     pl->grid_y = (unsigned)pl->splits;

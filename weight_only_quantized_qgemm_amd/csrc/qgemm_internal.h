@@ -81,12 +81,16 @@ constexpr int dec_scale_span(int fmt, int group_size, int nkb) {
 enum AMode : int { A_DIRECT = 0, A_STAGED = 1, A_DMA = 2 };
 // LDS a workgroup may take (160 KiB on gfx950).
 constexpr int kMaxLds = 160 * 1024;
+// LDS the decode kernel holds besides its slot sets and its dynamic region: the split-K
+// hand-off flag and the 1 KiB-aligned placeholder of an unused slot set, with their padding.
+constexpr int kDecodeStaticReserve = 2048;
 // A_DMA: bytes of one slot set (one k block per wavefront and run position); a kernel that
 // overlaps runs (two or more runs per share) holds two sets.  An instance exists, and the plan
-// takes A_DMA, only when its sets and the wave tiles of the final reduction fit in LDS.
+// takes A_DMA, only when its sets, the wave tiles of the final reduction and the reserve fit
+// in LDS.
 constexpr int dec_dma_set_bytes(int waves, int kpw) { return waves * kpw * 4096; }
 constexpr bool dec_dma_fits(int waves, int kpw, int cb, int nruns) {
-  return (nruns > 1 ? 2 : 1) * dec_dma_set_bytes(waves, kpw) + waves * cb * 64 * 16 <= kMaxLds;
+  return (nruns > 1 ? 2 : 1) * dec_dma_set_bytes(waves, kpw) + waves * cb * 64 * 16 + kDecodeStaticReserve <= kMaxLds;
 }
 // Per wavefront (dynamic region): its staged A share (M rows of share x 128 + 8 halves) and
 // its staged scales (cb column blocks), each padded to 16 bytes; A_STAGED only.
