@@ -302,10 +302,21 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   const float alpha = qgemm::group_scaled(FMT) ? 1.0f : *a.alpha;
   const int n = (nb0 + c) * 16 + (ln & 15);
   const float bv = bias_of(a, n);
+  // Every value is formed before the first store: a store counts as an outstanding memory
+  // operation here, so a wait for the bias or alpha load placed between two stores also waited
+  // for the stores before it (at M = 16, four write round trips in a row).
+  // (the empty asm pins the four values ahead of the stores: the compiler would otherwise sink
+  // each add into its store's branch)
+  float o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o[r] = (qgemm::group_scaled(FMT) ? v[0][r] : v[0][r] * alpha) + bv;
+    asm volatile("" : "+v"(o[r]));
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * (ln >> 4) + r;
-    if (m < a.M) store_out(a, m, n, qgemm::group_scaled(FMT) ? v[0][r] : v[0][r] * alpha, bv);
+    if (m < a.M) store_val(a, m, n, o[r]);
   }
 }
 

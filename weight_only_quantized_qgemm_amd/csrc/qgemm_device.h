@@ -396,23 +396,8 @@ __device__ __forceinline__ u32x2 pack4_out16(const KArgs& a, f32x4 v, f32x4 bias
   return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
-// Columns n .. n + 3 of row m (n a multiple of 4; N is a multiple of 16 and out 16-byte
-// aligned, so the store is aligned): each fp32 result (alpha already applied) plus its bias
-// in fp32, rounded once to the output type, written with one 16- or 8-byte store.
-__device__ __forceinline__ void store_out4(const KArgs& a, int m, int n, f32x4 v, f32x4 bias) {
-  const size_t i = (size_t)m * a.N + n;
-  if (a.out_dtype == QGEMM_DT_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + i) =
-        f32x4{v[0] + bias[0], v[1] + bias[1], v[2] + bias[2], v[3] + bias[3]};
-  } else {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + i) = pack4_out16(a, v, bias);
-  }
-}
-
-// v is the fp32 result (alpha already applied); the bias is added in fp32, then the value is
-// rounded once to the output type.
-__device__ __forceinline__ void store_out(const KArgs& a, int m, int n, float v, float bias) {
-  v += bias;
+// v is the final fp32 value (alpha and bias already applied), rounded once to the output type.
+__device__ __forceinline__ void store_val(const KArgs& a, int m, int n, float v) {
   const size_t i = (size_t)m * a.N + n;
   if (a.out_dtype == QGEMM_DT_F32) {
     static_cast<float*>(a.out)[i] = v;

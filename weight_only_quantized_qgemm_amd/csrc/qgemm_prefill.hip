@@ -339,16 +339,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     return x;
   };
   if (a.out_dtype == QGEMM_DT_F32) {                 // fp32 output: 16-byte stores from the fragments
+    // Every value is formed before the first store (the empty asm keeps the compiler from
+    // sinking the adds into the stores' branches): a store counts as an outstanding memory
+    // operation, so a wait for a bias load between two stores would also wait for the stores
+    // before it.
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int nb = min((n0 >> 4) + TN * wn + j, NB - 1);    // a block past N is formed, never stored
+      const f32x4 bv = bias4_of(a, nb * 16 + 4 * (lane >> 4));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        f32x4 x = scaled(v[TN * i + j]);
+        x = f32x4{x[0] + bv[0], x[1] + bv[1], x[2] + bv[2], x[3] + bv[3]};
+        asm volatile("" : "+v"(x));
+        v[TN * i + j] = x;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int nb = (n0 >> 4) + TN * wn + j;
       if (nb >= NB) continue;
       const int n = nb * 16 + 4 * (lane >> 4);
-      const f32x4 bv = bias4_of(a, n);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = m0 + 16 * TM * wm + 16 * i + (lane & 15);
-        if (m < a.M) store_out4(a, m, n, scaled(v[TN * i + j]), bv);
+        if (m < a.M) *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (size_t)m * a.N + n) = v[TN * i + j];
       }
     }
     continue;
