@@ -239,7 +239,8 @@ def test_plan_describe_fields_and_errors():
     assert q.plan_describe(q.problem(0, 256, 512, "int4")) == "empty"
     d = q.plan_fields(q.problem(16, 4096, 4096, "int4"))
     assert d["kernel"] == "decode" and d["a"] == "dma" and int(d["splits"]) >= 1
-    assert q.plan_fields(q.problem(1, 4096, 4096, "int4"))["a"] == "staged"
+    assert q.plan_fields(q.problem(1, 4096, 4096, "int4"))["a"] == "staged-early"
+    assert q.plan_fields(q.problem(1, 11008, 4096, "int4"))["a"] == "staged"        # 688 workgroups
     d = q.plan_fields(q.problem(4096, 4096, 4096, "int4"))
     assert d["kernel"] == "prefill" and d["tile"] in ("64x128", "128x128", "256x256")
     assert q.plan_fields(q.problem(2176, 2048, 1024, "int4", kernel_hint=3))["persist"] != "0"
@@ -270,7 +271,10 @@ def test_decode_plans_fit_lds_and_take_dma_above_staging():
                         assert "stages at most" in e.detail or "exceeds the" in e.detail, e.detail
                         continue
                     assert d["kernel"] == "decode"
-                    assert d["a"] == ("staged" if M <= 4 else "dma"), (fmt, M, N, K, d)
+                    assert d["a"] in (("staged", "staged-early") if M <= 4 else ("dma",)), (fmt, M, N, K, d)
+                    if d["a"] == "staged-early":
+                        g = [int(x) for x in d["grid"].split("x")]
+                        assert d["cb"] == "1" and int(d["kpw"]) <= 5 and g[0] * g[1] <= 256, d
                     waves, kpw, runs = int(d["waves"]), int(d["kpw"]), int(d["runs"])
                     share = -(-int(d["kb_per_split"]) // waves)
                     assert 1 <= kpw <= share or share == 0

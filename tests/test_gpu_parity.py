@@ -167,6 +167,30 @@ def test_decode_multi_run(q, fmt, G, M, N, K):
     check_against_oracle(q, prep, A)
 
 
+STAGED_CASES = [
+    # (format, G, M, N, K, A path): staged A with the first weight block issued before the
+    # staging loads ("staged-early": one column block, short runs, one workgroup per CU at
+    # most) and after them ("staged")
+    ("int4", 128, 1, 4096, 4096, "staged-early"),
+    ("int4", 32, 4, 11008, 4096, "staged"),          # 688 workgroups
+    ("fp4", None, 1, 8192, 8192, "staged"),          # runs of eight k blocks, 512 workgroups
+    ("nf4", 64, 3, 1024, 2048, "staged-early"),      # split K
+    ("fp8", None, 2, 4096, 5120, "staged-early"),    # runs of five
+    ("int2", 256, 4, 8192, 4096, "staged"),          # 512 workgroups
+]
+
+
+@pytest.mark.parametrize("fmt,G,M,N,K,path", STAGED_CASES,
+                         ids=[f"{c[0]}-{c[2]}x{c[3]}x{c[4]}" for c in STAGED_CASES])
+def test_decode_staged_paths(q, fmt, G, M, N, K, path):
+    d = q.plan_fields(q.problem(M, N, K, fmt, group_size=G))
+    assert d["kernel"] == "decode" and d["a"] == path, d
+    say(f"case decode-staged fmt={fmt} G={G} M={M} N={N} K={K} plan={d}")
+    prep = Prepared(q, fmt, N, K, G or 0, (65, N, K))
+    A = _act(fmt, M, K, (65, M))
+    check_against_oracle(q, prep, A)
+
+
 DMA_CASES = [
     # (format, G, M, N, K, expected plan: cb, kpw, runs, splits) -- every case takes A through
     # the DMA slots; together they cover one run per share (with wavefronts whose share is

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   a.K = K;
   a.kb_per_split = kb_per_split;
   constexpr bool MULTI = NR > 1;
-  constexpr bool ASTAGE = AMODE == qgemm::A_STAGED, ADMA = AMODE == qgemm::A_DMA;
+  constexpr bool ASTAGE = qgemm::a_staged(AMODE), ADMA = AMODE == qgemm::A_DMA;
   constexpr int NT = 64 * NW;
   // Scales are staged with the A share (small M); otherwise each wavefront loads its own
   // with its weights (staging them alone measured slower at M = 16).
@@ -107,6 +107,13 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   const int s_chunks = nkw > 0 ? CB * spc : 0;
   int soff[SA + SS + 1];
   u32x4 stage[SA + SS + 1];
+  // A_STAGED_EARLY: the first weight block goes out before the staging loads, whose address
+  // arithmetic otherwise delays it by ~0.5 us (M = 1 N = 4096 4.49 -> 4.27 us, M = 2 4.64 ->
+  // 4.43, NF4 M = 1 5.32 -> 5.03).  Planned for one column block, runs of at most five k blocks
+  // and at most one workgroup per CU: otherwise it measured 2-6% slower (M = 4 N = 11008, two
+  // or three workgroups per CU; FP4 M = 1 K = 8192, runs of eight).
+  constexpr bool W0FIRST = AMODE == qgemm::A_STAGED_EARLY;
+  auto issue_staging = [&]() {
   if constexpr (ASTAGE) {
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.A + (size_t)w_begin * 128), (short)0, 0x7fffffff, 0x00020000);
@@ -145,6 +152,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
     }
   }
   if constexpr (STAGE) __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (!W0FIRST) issue_staging();
 
   f32x4 acc[CB][2];
 #pragma unroll
@@ -174,7 +183,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   // one run: loads first (A fragments, then weights), then the k blocks in load order,
   // each waiting only for its own data
   constexpr int NAF = AMODE == qgemm::A_DIRECT ? KPW : 1;
-  auto run_loads = [&](int run, u32x4 (&afr)[NAF][4], WFrag<FMT> (&wf)[KPW][CB], unsigned char* set) {
+  auto run_loads = [&](int run, u32x4 (&afr)[NAF][4], WFrag<FMT> (&wf)[KPW][CB], unsigned char* set, int u0 = 0,
+                       int u1 = KPW) {
     if constexpr (ADMA) {
 #pragma unroll
       for (int u = 0; u < KPW; ++u)
@@ -197,9 +207,10 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
     }
 #pragma unroll
     for (int u = 0; u < KPW; ++u)
+      if (u >= u0 && u < u1)                         // compile-time after unrolling
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-        load_wfrag<FMT, G, true, !HAS_S>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
+        for (int c = 0; c < CB; ++c)
+          load_wfrag<FMT, G, true, !HAS_S>(a, min(nb0 + c, NB - 1), min(run + u, kb_cap), lane, wf[u][c]);
     __builtin_amdgcn_sched_barrier(0);
   };
   // MULTI: no branch around a k block (the compiler would wait for every load in flight,
@@ -253,13 +264,20 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   u32x4 afr[MULTI ? 2 : 1][NAF][4];
   WFrag<FMT> wf[MULTI ? 2 : 1][KPW][CB];
   // first run (every wavefront, with or without k blocks), then the staged share lands in LDS
-  run_loads(w_begin, afr[0], wf[0], Ad0);
+  if constexpr (W0FIRST) {
+    run_loads(w_begin, afr[0], wf[0], Ad0, 0, 1);
+    issue_staging();
+    run_loads(w_begin, afr[0], wf[0], Ad0, 1, KPW);
+  } else {
+    run_loads(w_begin, afr[0], wf[0], Ad0);
+  }
   if constexpr (STAGE) {
 #pragma unroll
     for (int i = 0; i < SA + SS; ++i)
       if (soff[i] >= 0) *reinterpret_cast<u32x4*>(w_lds + soff[i]) = stage[i];
     __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the wavefront's own LDS writes have landed
     __builtin_amdgcn_wave_barrier();
+    if constexpr (W0FIRST) __builtin_amdgcn_sched_barrier(0);   // the next run's loads stay behind
   }
   if constexpr (!MULTI) {
     if (w_begin < w_end) run_compute(w_begin, afr[0], wf[0], Ad0);
@@ -364,6 +382,12 @@ bool launch_unstaged(const Plan& pl, const KArgs& a, hipStream_t stream) {
 template <int FMT, int G, int CB, int KPW>
 bool launch_cb(const Plan& pl, const KArgs& a, hipStream_t stream) {
   if (pl.amode == qgemm::A_STAGED) return launch_nr<FMT, G, CB, KPW, kDecodeWaves, qgemm::A_STAGED>(pl, a, stream);
+  if (pl.amode == qgemm::A_STAGED_EARLY) {
+    if constexpr (CB == 1 && KPW <= 5)
+      return launch_nr<FMT, G, CB, KPW, kDecodeWaves, qgemm::A_STAGED_EARLY>(pl, a, stream);
+    else
+      return false;                                  // not instantiated; never planned
+  }
   if constexpr (CB >= 2)
     return launch_unstaged<FMT, G, CB, KPW, kDecodeWavesWide>(pl, a, stream);
   else

@@ -218,6 +218,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // 6.9 -> 5.5 us, N = 11008 9.1 -> 8.3 us; FP4 8192 x 8192 16.4 -> 13.0 us).
     if (pl->astage) {
       choose_runs(A_STAGED, 8);
+      if (pl->cb == 1 && pl->kpw <= 5 && (int64_t)groups * pl->splits <= kCUs) pl->amode = A_STAGED_EARLY;
     } else {
       // Runs are shortened until the slots fit (M = 16, N = 4096: K = 8192 11.6 -> 8.5 us with
       // runs of 2 instead of direct runs of 8, K = 14336 18.5 -> 12.4 us); runs of one k block
@@ -474,7 +475,7 @@ qgemm_status_t qgemm_plan_describe(const qgemm_problem_t* p, char* buf, size_t l
   if (p->M == 0) {
     n = std::snprintf(buf, len, "empty");
   } else if (pl.kind == KIND_DECODE) {
-    static const char* const kA[] = {"direct", "staged", "dma"};
+    static const char* const kA[] = {"direct", "staged", "dma", "staged-early"};
     n = std::snprintf(buf, len, "decode grid=%ux%u waves=%d cb=%d kpw=%d runs=%d a=%s splits=%d kb_per_split=%d "
                       "lds=%d ws=%zu", pl.grid_x, pl.grid_y, pl.nw, pl.cb, pl.kpw, pl.nruns, kA[pl.amode], pl.splits,
                       pl.kb_per_split, pl.lds_bytes, pl.ws_bytes);

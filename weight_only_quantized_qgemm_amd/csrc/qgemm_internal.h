@@ -78,7 +78,10 @@ constexpr int dec_scale_span(int fmt, int group_size, int nkb) {
 // and scales (A_STAGED, small M), or from LDS slots that buffer-to-LDS DMA fills run by run,
 // 4 KiB (16 rows x 128 halves) per k block (A_DMA, larger M).  The A_DMA slots are static
 // arrays of the kernel instance, not part of the dynamic region below.
-enum AMode : int { A_DIRECT = 0, A_STAGED = 1, A_DMA = 2 };
+// A_STAGED_EARLY is A_STAGED with the first weight block issued ahead of the staging loads
+// (one column block, runs of at most five k blocks, a grid of at most one workgroup per CU).
+enum AMode : int { A_DIRECT = 0, A_STAGED = 1, A_DMA = 2, A_STAGED_EARLY = 3 };
+constexpr bool a_staged(int amode) { return amode == A_STAGED || amode == A_STAGED_EARLY; }
 // LDS a workgroup may take (160 KiB on gfx950).
 constexpr int kMaxLds = 160 * 1024;
 // LDS the decode kernel holds besides its slot sets and its dynamic region: the split-K
@@ -95,10 +98,10 @@ constexpr bool dec_dma_fits(int waves, int kpw, int cb, int nruns) {
 // Per wavefront (dynamic region): its staged A share (M rows of share x 128 + 8 halves) and
 // its staged scales (cb column blocks), each padded to 16 bytes; A_STAGED only.
 constexpr int dec_a_bytes(int M, int share, int amode) {
-  return amode == A_STAGED ? (M * (share * 128 + 8) * 2 + 15) / 16 * 16 : 0;
+  return a_staged(amode) ? (M * (share * 128 + 8) * 2 + 15) / 16 * 16 : 0;
 }
 constexpr int dec_s_bytes(int fmt, int group_size, int share, int cb, int amode) {
-  return amode == A_STAGED ? (cb * dec_scale_span(fmt, group_size, share) + 15) / 16 * 16 : 0;
+  return a_staged(amode) ? (cb * dec_scale_span(fmt, group_size, share) + 15) / 16 * 16 : 0;
 }
 constexpr int dec_region_bytes(int fmt, int group_size, int M, int share, int cb, int amode) {
   return dec_a_bytes(M, share, amode) + dec_s_bytes(fmt, group_size, share, cb, amode);
