@@ -278,7 +278,7 @@ def test_decode_plans_fit_lds_and_take_dma_above_staging():
                     waves, kpw, runs = int(d["waves"]), int(d["kpw"]), int(d["runs"])
                     share = -(-int(d["kb_per_split"]) // waves)
                     assert 1 <= kpw <= share or share == 0
-                    assert runs == 1 or (2 <= runs <= 4 and -(-share // kpw) == runs)
+                    assert runs == 1 or (2 <= runs <= (8 if d["a"] == "dma" else 4) and -(-share // kpw) == runs)
                     if d["a"] == "dma":
                         sets = 2 if runs > 1 else 1
                         assert sets * waves * kpw * 4096 + int(d["lds"]) + 2048 <= 160 * 1024, (fmt, M, N, K, d)

@@ -194,12 +194,14 @@ def test_decode_staged_paths(q, fmt, G, M, N, K, path):
 DMA_CASES = [
     # (format, G, M, N, K, expected plan: cb, kpw, runs, splits) -- every case takes A through
     # the DMA slots; together they cover one run per share (with wavefronts whose share is
-    # empty), two slot sets alternating over 2, 3 and 4 runs, shares ending mid-run, runs one
+    # empty), two slot sets alternating over 2 to 8 runs, shares ending mid-run, runs one
     # after another reusing one set, runs shortened to fit LDS, split K, 1 to 4 column blocks.
     ("int4", 128, 5, 256, 512, (1, 1, 1, 1)),       # 4 k blocks over 8 wavefronts
     ("int4", 64, 16, 2048, 5120, (1, 2, 3, 1)),     # share 5 in runs of 2
     ("nf4", 32, 9, 1024, 5120, (1, 2, 2, 2)),       # split K, share 3
-    ("int4", 128, 16, 2048, 16384, (1, 2, 1, 1)),   # share 16: eight runs, one slot set
+    ("int4", 128, 16, 2048, 16384, (1, 2, 8, 1)),   # share 16: eight overlapped runs
+    ("int4", 128, 16, 2048, 18432, (1, 2, 1, 1)),   # share 18: nine runs, one slot set
+    ("int4", 32, 6, 9216, 6144, (3, 2, 6, 1)),      # six overlapped runs
     ("fp8", None, 16, 4096, 8192, (1, 2, 4, 1)),    # runs shortened from 8 to fit LDS
     ("fp4", None, 12, 4352, 2944, (2, 4, 2, 1)),
     ("int2", 32, 16, 8448, 2048, (3, 2, 2, 1)),

@@ -34,8 +34,9 @@ namespace {
 // NR >= 2 (a share of NR runs): two register sets alternate and the loads of run r + 1
 // are issued before run r is computed, so consecutive runs overlap their memory round
 // trips.  The runs are unrolled (a loop carrying loads across its back edge defeats the
-// compiler's wait tracking, which then drains every load at the loop head).  NR = 1: one
-// run, or, for shares longer than four runs, runs one after another.
+// compiler's wait tracking, which then drains every load at the loop head): up to four
+// runs, or eight with A in DMA slots.  NR = 1: one run, or, for longer shares, runs one after
+// another.
 constexpr bool DEC_ACC2 = true;                     // two accumulators per column block
 
 // The pointers and sizes that the first loads depend on come as separate leading
@@ -340,7 +341,8 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
 
 template <int FMT, int G, int CB, int KPW, int NW, int AMODE, int NR>
 bool launch_one(const Plan& pl, const KArgs& a, hipStream_t stream) {
-  if constexpr (AMODE == qgemm::A_DMA && !qgemm::dec_dma_fits(NW, KPW, CB, NR)) {
+  // five to eight overlapped runs only with A in DMA slots (A in registers or staged: at most four)
+  if constexpr ((AMODE == qgemm::A_DMA && !qgemm::dec_dma_fits(NW, KPW, CB, NR)) || (NR > 4 && AMODE != qgemm::A_DMA)) {
     return false;                                    // not instantiated; never planned
   } else {
     // The instance's static LDS (slot sets, flags) plus the plan's dynamic region must fit the
@@ -365,6 +367,10 @@ bool launch_nr(const Plan& pl, const KArgs& a, hipStream_t stream) {
     case 2: return launch_one<FMT, G, CB, KPW, NW, AMODE, 2>(pl, a, stream);
     case 3: return launch_one<FMT, G, CB, KPW, NW, AMODE, 3>(pl, a, stream);
     case 4: return launch_one<FMT, G, CB, KPW, NW, AMODE, 4>(pl, a, stream);
+    case 5: return launch_one<FMT, G, CB, KPW, NW, AMODE, 5>(pl, a, stream);
+    case 6: return launch_one<FMT, G, CB, KPW, NW, AMODE, 6>(pl, a, stream);
+    case 7: return launch_one<FMT, G, CB, KPW, NW, AMODE, 7>(pl, a, stream);
+    case 8: return launch_one<FMT, G, CB, KPW, NW, AMODE, 8>(pl, a, stream);
     default: return launch_one<FMT, G, CB, KPW, NW, AMODE, 1>(pl, a, stream);
   }
 }

@@ -130,7 +130,7 @@ struct Plan {
   bool astage;            // decode: stage the A slice in LDS (small M)
   int amode;              // decode: AMode (A_STAGED when astage)
   int nw;                 // decode: wavefronts per workgroup
-  int nruns;              // decode: runs per wavefront share, pipelined when 2..4 (else 1)
+  int nruns;              // decode: runs per wavefront share, pipelined when 2..8 (A_DMA) or 2..4 (else 1)
   int lds_bytes;          // decode: dynamic LDS per workgroup (staged A, staged scales, wave tiles)
   // prefill: workgroup tile (bm selects the shape: pf_bm of kPfSmall, kPfMedium or kPfLarge)
   int bm, bn;
