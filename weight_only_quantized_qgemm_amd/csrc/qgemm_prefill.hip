@@ -57,6 +57,10 @@ __device__ __forceinline__ void barrier_no_fence() {
 #ifndef QGEMM_PF_DS
 #define QGEMM_PF_DS 1
 #endif
+// wavefronts with no column inside N skip their MFMAs (0 turns it off)
+#ifndef QGEMM_PF_IDLE
+#define QGEMM_PF_IDLE 1
+#endif
 __device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& tm, int& tn) {
   const int x = b & 7, slot = b >> 3, q = tiles >> 3, r = tiles & 7;
   const int L = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
@@ -241,11 +245,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     for (int r = 0; r < RU; ++r) dst[r] = *reinterpret_cast<const u32x4*>(As + aoff[t] + (i0 + r) * 16 * ROWB);
   };
 
+  // A wavefront whose column blocks all lie past N (the last tile column of an N that is not
+  // a multiple of the tile width) computes nothing; it still issues its share of the A DMA
+  // and its (clamped) weight loads, so the load counts the waits rely on stay the same.
+  const bool idle = QGEMM_PF_IDLE && (n0 >> 4) + TN * wn >= NB;
   // Computes one k block from As / wf while issuing the DMA loads of a later one (into
   // Ad), DS read units apart: issued all at once they would fill the memory pipeline's
   // queue and stall the wavefront's MFMAs behind it.  An is the stage of the next block.
   auto compute = [&](const unsigned char* As, const WFrag<FMT> (&wf)[TN], int kb_next, unsigned char* Ad,
                      const unsigned char* An) {
+    if (idle) {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) load_a(kb_next, Ad, i);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     float fs[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
