@@ -257,9 +257,8 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     int best_c = -1, best = 1;
     double best_cost = 0.0;
     // Persistent schedule with a stream-K tail (split 0 below), on request only
-    // (QGEMM_KERNEL_PREFILL_STREAMK): as many workgroups as are resident at once (one per CU
-    // for the 256- and 128-row tiles, whose A stages take 128 KiB of LDS; two for the 64-row
-    // tile); each takes whole tiles round-robin (the same tile ids, and so the same XCD-aware
+    // (QGEMM_KERNEL_PREFILL_STREAMK): as many workgroups as are resident at once (as many per CU
+    // as their A stages fit in its 160 KiB of LDS: pf_per_cu); each takes whole tiles round-robin (the same tile ids, and so the same XCD-aware
     // walk, as the one-tile launch) for all rounds but the last full one, and the tiles left
     // (between one and two rounds' worth) are split evenly in K over all of them, so no round
     // runs partly idle.  Its cost: the k blocks of a workgroup's share plus two pipeline fills,
@@ -277,7 +276,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
       if ((int64_t)pf_bm(sh) * p->K * 2 > 0x7fffffffLL) continue;     // the A tile uses 32-bit offsets
       const int64_t mt = (p->M + pf_bm(sh) - 1) / pf_bm(sh), nt = (p->N + pf_bn(sh) - 1) / pf_bn(sh);
       const int64_t T = mt * nt;
-      const int P = kCUs * (c == 0 ? 2 : 1);
+      const int P = kCUs * pf_per_cu(sh);            // resident workgroups
       for (int s = 0; s <= 64 && (s <= 1 || s <= kblocks / 2); ++s) {
         double cost;
         if (s == 0) {                                  // persistent, stream-K tail
@@ -310,7 +309,8 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->tiles = (int)(mt * nt);
     pl->tile_elems = pl->bm * pl->bn;
     const int64_t T = mt * nt;
-    const int P = kCUs * (pl->bm == pf_bm(kPfSmall) ? 2 : 1);
+    const int P = kCUs * (pl->bm == pf_bm(kPfSmall) ? pf_per_cu(kPfSmall) : pl->bm == pf_bm(kPfMedium) ? pf_per_cu(kPfMedium)
+                                                                                           : pf_per_cu(kPfLarge));
     if (persist) {
       const int64_t dp = T > P ? (T / P - 1) * P : 0;
       if ((T - dp) * kblocks > 0x7fffffffLL)

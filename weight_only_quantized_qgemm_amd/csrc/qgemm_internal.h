@@ -14,20 +14,27 @@ namespace qgemm {
 // k steps are short and it keeps four A stages in flight instead of two; the small one
 // (M up to a few hundred) halves the medium tile's rows again, doubling the workgroups.
 // RU: row tiles per LDS read unit; LA: units read ahead of the MFMAs that consume them;
-// ST: A stages in LDS (ST - 1 k blocks are loaded ahead of the one being computed).
-struct PfShape { int wgm, wgn, tm, tn, ru, la, st; };
+// ST: A stages in LDS; BB: k blocks per workgroup barrier (ST - BB k blocks are loaded ahead
+// of the one being computed).
+struct PfShape { int wgm, wgn, tm, tn, ru, la, st, bb; };
 #ifndef QGEMM_PF_LARGE
-#define QGEMM_PF_LARGE 1, 8, 16, 2, 4, 1, 2
-#define QGEMM_PF_MEDIUM 1, 8, 8, 1, 8, 1, 4
+#define QGEMM_PF_LARGE 1, 8, 16, 2, 4, 1, 2, 1
+#define QGEMM_PF_MEDIUM 1, 8, 8, 1, 8, 1, 4, 1
 #endif
+// The small tile meets at a barrier every second k block, with six A stages (96 KiB, one
+// workgroup per CU): FP4 128 x 8192 x 8192 28.4 -> 26.8 us, INT4 384 x 4096 x 4096 22.9 -> 21.2
+// us against four stages and a barrier per block; eight stages measured slower (deeper
+// prefetch alone: 28.2 and 23.0 us).
 #ifndef QGEMM_PF_SMALL
-#define QGEMM_PF_SMALL 1, 8, 4, 1, 4, 1, 4
+#define QGEMM_PF_SMALL 1, 8, 4, 1, 4, 1, 6, 2
 #endif
 constexpr PfShape kPfLarge{QGEMM_PF_LARGE};    // 256 x 256 output tile
 constexpr PfShape kPfMedium{QGEMM_PF_MEDIUM};  // 128 x 128 output tile
 constexpr PfShape kPfSmall{QGEMM_PF_SMALL};    // 64 x 128 output tile
 constexpr int pf_bm(PfShape s) { return 16 * s.wgm * s.tm; }
 constexpr int pf_bn(PfShape s) { return 16 * s.wgn * s.tn; }
+// Workgroups of a shape that fit one compute unit's 160 KiB of LDS (the A stages dominate).
+constexpr int pf_per_cu(PfShape s) { return (160 * 1024) / (s.st * pf_bm(s) * 256 + 1024); }
 // Decode kernel: wavefronts per workgroup (with A staged in LDS, and whenever a workgroup
 // owns a single column block), and the smaller count for wider workgroups of unstaged A:
 // half the wavefronts with twice the K share each pipeline longer runs (M = 16: N = 11008

@@ -27,10 +27,10 @@ namespace {
 // have the same lane map), so the MFMA computes the transposed 16 x 16 tile: lane l holds
 // output row l & 15, columns 4 (l >> 4) .. 4 (l >> 4) + 3, and the epilogue writes them
 // with one 8-byte (16-bit output) or 16-byte (fp32) store.
-// One barrier per k block: step k issues the weight loads of block k + 1, computes block k
-// while spreading the A DMA loads of block k + 1 over its first read units, waits for its
-// own loads and meets the other wavefronts at the barrier.  The
-// loop is unrolled by two so buffers and register sets alternate without copies; every
+// One barrier per BB k blocks: step k issues the weight loads of block k + ST - BB, computes
+// block k while spreading the A DMA loads of that block over its first read units, and at the
+// end of each window of BB blocks waits for its own loads and meets the other wavefronts at
+// the barrier.  The loop is unrolled by ST so buffers and register sets rotate without copies; every
 // load is unconditional (the last step re-loads its own block, never used) and
 // sched_barrier pins the phase order (a load under a branch, or a consumer scheduled
 // early, would make the wavefront wait for all outstanding loads).
@@ -147,7 +147,7 @@ __device__ __forceinline__ bool pf_next(const KArgs& a, int item, int KB, int ti
   }
 }
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST, bool PERSIST>
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST, int BB, bool PERSIST>
 __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   constexpr int NW = WGM * WGN;                      // wavefronts
   constexpr int NT = 64 * NW;                        // threads
@@ -160,24 +160,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   static_assert(TU * RU == TM, "RU must divide TM");
   constexpr int DS = QGEMM_PF_DS;                    // read units between two DMA issues
   static_assert(DS * (NDMA - 1) < NU, "the DMA loads must all be issued within one k block");
-  static_assert(ST >= 2 && ST <= 4, "two to four A stages");
+  static_assert(ST >= 2 && ST <= 8, "two to eight A stages");
+  // BB k blocks between two workgroup barriers; block kb + D is loaded while block kb is
+  // computed, into the stage block kb - BB left, which every wavefront finished reading before
+  // the last barrier.
+  static_assert(BB >= 1 && ST % BB == 0 && ST > BB, "whole barrier windows per stage ring");
+  constexpr int D = ST - BB;
   // Each stage is its own array, so that the compiler can tell the buffer being read from
   // the ones being filled (it would otherwise wait for every DMA load before a read).
   __shared__ __attribute__((aligned(1024))) unsigned char As0[BM * ROWB];
   __shared__ __attribute__((aligned(1024))) unsigned char As1[BM * ROWB];
   __shared__ __attribute__((aligned(1024))) unsigned char As2[ST > 2 ? BM * ROWB : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char As3[ST > 3 ? BM * ROWB : 16];
-  auto stage = [&](int i) -> unsigned char* { return i == 0 ? As0 : i == 1 ? As1 : i == 2 ? As2 : As3; };
+  __shared__ __attribute__((aligned(1024))) unsigned char As4[ST > 4 ? BM * ROWB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char As5[ST > 5 ? BM * ROWB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char As6[ST > 6 ? BM * ROWB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char As7[ST > 7 ? BM * ROWB : 16];
+  auto stage = [&](int i) -> unsigned char* {
+    return i == 0 ? As0 : i == 1 ? As1 : i == 2 ? As2 : i == 3 ? As3 : i == 4 ? As4 : i == 5 ? As5 : i == 6 ? As6 : As7;
+  };
   // With three or more stages the first LA read units of the next block are read during
   // the current one (after its own last reads), so a block starts with its A fragments in
   // flight instead of behind the barrier; the unit ring must then line up across blocks.
   constexpr bool XPF = ST >= 3 && NU % (LA + 1) == 0;
   // Vector-memory instructions per k block per wavefront: NDMA A loads and, per weight
-  // column block, two (the fragment and its scales, or FP8's two fragment halves).  At the
-  // end of a step the next block must have landed (with XPF: the next two, since the step
-  // after reads ahead into the second) while the blocks after them may still be in flight;
-  // loads complete in issue order, so that is this many pending.
-  constexpr int PEND = (ST - (XPF ? 3 : 2)) * (NDMA + 2 * TN);
+  // column block, two (the fragment and its scales, or FP8's two fragment halves).  At a
+  // barrier the next window of BB blocks must have landed (with XPF one more, since the last
+  // step of the window reads ahead into it) while the D - BB (- 1) blocks after them may
+  // still be in flight; loads complete in issue order, so that is this many pending.
+  static_assert(ST - 2 * BB - (XPF ? 1 : 0) >= 0, "the next window must be loaded before its barrier");
+  constexpr int PEND = (ST - 2 * BB - (XPF ? 1 : 0)) * (NDMA + 2 * TN);
   static_assert(PEND <= 63, "vmcnt counts at most 63 outstanding loads");
   // s_waitcnt immediate: vmcnt = PEND (bits 3:0 and 15:14), expcnt and lgkmcnt left open.
   // Through the builtin (not inline asm) the compiler's own wait insertion knows of it.
@@ -294,11 +306,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
     }
   };
 
-  // Prologue: blocks kb_begin .. kb_begin + ST - 2 into stages 0 .. ST - 2.  Step kb computes
-  // stage kb mod ST while loading block kb + ST - 1 into the stage the previous step read.
+  // Prologue: blocks kb_begin .. kb_begin + D - 1 into stages 0 .. D - 1.  Step kb computes
+  // stage kb mod ST while loading block kb + D into the stage block kb - BB was read from.
   WFrag<FMT> w[ST][TN];
 #pragma unroll
-  for (int s = 0; s < ST - 1; ++s) {
+  for (int s = 0; s < D; ++s) {
     const int kb = min(kb_begin + s, kb_end - 1);
     load_w(kb, w[s]);
 #pragma unroll
@@ -314,13 +326,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   for (int kb = kb_begin; kb < kb_end; kb += ST) {
 #pragma unroll
     for (int j = 0; j < ST; ++j) {
-      const int sn = (j + ST - 1) % ST;                // stage that receives block kn
-      const int kn = min(kb + j + ST - 1, kb_end - 1);
+      const int sn = (j + D) % ST;                     // stage that receives block kn
+      const int kn = min(kb + j + D, kb_end - 1);
       load_w(kn, w[sn]);
       __builtin_amdgcn_sched_barrier(0);
       compute(stage(j), w[j], kn, stage(sn), stage((j + 1) % ST));
-      __builtin_amdgcn_s_waitcnt(WAIT_PEND);
-      barrier_no_fence();
+      if ((j + 1) % BB == 0) {
+        __builtin_amdgcn_s_waitcnt(WAIT_PEND);
+        barrier_no_fence();
+      }
       if (kb + j + 1 >= kb_end) break;
     }
   }
@@ -421,13 +435,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void qgemm_prefill(KArgs a) {
   }   // segments
 }
 
-template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST>
+template <int FMT, int G, int WGM, int WGN, int TM, int TN, int RU, int LA, int ST, int BB>
 void launch_shape(const Plan& pl, const KArgs& a, hipStream_t stream) {
   if (pl.persist)
-    hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST, true>), dim3(pl.grid_x, pl.grid_y),
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST, BB, true>), dim3(pl.grid_x, pl.grid_y),
                        dim3(64 * WGM * WGN), 0, stream, a);
   else
-    hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST, false>), dim3(pl.grid_x, pl.grid_y),
+    hipLaunchKernelGGL((qgemm_prefill<FMT, G, WGM, WGN, TM, TN, RU, LA, ST, BB, false>), dim3(pl.grid_x, pl.grid_y),
                        dim3(64 * WGM * WGN), 0, stream, a);
 }
 
@@ -436,11 +450,11 @@ struct PrefillLauncher {
   static hipError_t run(const Plan& pl, const KArgs& a, hipStream_t stream) {
     constexpr PfShape L = kPfLarge, M = kPfMedium, S = kPfSmall;
     if (pl.bm == pf_bm(L))
-      launch_shape<FMT, G, L.wgm, L.wgn, L.tm, L.tn, L.ru, L.la, L.st>(pl, a, stream);
+      launch_shape<FMT, G, L.wgm, L.wgn, L.tm, L.tn, L.ru, L.la, L.st, L.bb>(pl, a, stream);
     else if (pl.bm == pf_bm(M))
-      launch_shape<FMT, G, M.wgm, M.wgn, M.tm, M.tn, M.ru, M.la, M.st>(pl, a, stream);
+      launch_shape<FMT, G, M.wgm, M.wgn, M.tm, M.tn, M.ru, M.la, M.st, M.bb>(pl, a, stream);
     else
-      launch_shape<FMT, G, S.wgm, S.wgn, S.tm, S.tn, S.ru, S.la, S.st>(pl, a, stream);
+      launch_shape<FMT, G, S.wgm, S.wgn, S.tm, S.tn, S.ru, S.la, S.st, S.bb>(pl, a, stream);
     return hipGetLastError();
   }
 };
