@@ -387,10 +387,11 @@ def main():
     if args.counter_pass == "prefill":
         # the prefill workloads with the planned launch, then FP8 32768 x 3200 x 5120 with the
         # persistent stream-K schedule (kernel_hint PREFILL_STREAMK) and with one tile per
-        # workgroup (kernel_hint PREFILL)
+        # workgroup (kernel_hint PREFILL), then FP4 M = 128 (the 64 x 128 tile, split K)
         done = []
         for name, si, G, hint in (("int4_prefill", 0, 128, 0), ("fp8", 2, 0, 0), ("fp4", 2, 0, 0),
-                                  ("fp8", 3, 0, q.KERNEL_PREFILL_STREAMK), ("fp8", 3, 0, q.KERNEL_PREFILL)):
+                                  ("fp8", 3, 0, q.KERNEL_PREFILL_STREAMK), ("fp8", 3, 0, q.KERNEL_PREFILL),
+                                  ("fp4", 1, 0, 0)):
             wk = synthetic.WORKLOADS[name]
             M, N, K = wk["shapes"][si]
             g = Gemm(q, torch, wk["fmt"], M, N, K, G, (synthetic.WORKLOAD_INDEX[name], si), rot // 2)
