@@ -226,6 +226,30 @@ def test_decode_dma_paths(q, fmt, G, M, N, K, plan):
     check_against_oracle(q, prep, A)
 
 
+SMALL_WINDOW_CASES = [
+    # (format, G, K, split): the 64-row tile meets at a barrier every second k block and keeps
+    # six A stages, so slices of 1, 2, 3, 5 and 7 k blocks end on a full window, inside one, or
+    # before the first barrier; with splits, the last slice is the shorter one.
+    ("int4", 128, 128, 1), ("fp8", None, 256, 1), ("fp4", None, 384, 1), ("nf4", 32, 640, 1),
+    ("int2", 64, 896, 1), ("fp8h", None, 128 * 13, 2), ("int4", 256, 128 * 18, 4), ("fp4", None, 128 * 11, 3),
+]
+
+
+@pytest.mark.parametrize("fmt,G,K,split", SMALL_WINDOW_CASES,
+                         ids=[f"{c[0]}-K{c[2]}-s{c[3]}" for c in SMALL_WINDOW_CASES])
+def test_prefill_small_tile_barrier_windows(q, fmt, G, K, split):
+    # 100 rows (a full and a ragged 64-row tile) x 400 columns (three 128-column tiles, the
+    # last one with its wavefronts past N idle): every element against the oracle.
+    M, N = 100, 400
+    say(f"case small-tile windows fmt={fmt} G={G} K={K} split={split}")
+    p = q.problem(M, N, K, fmt, group_size=G, kernel_hint=2, tile_hint=64, split_k_hint=split)
+    d = q.plan_fields(p)
+    assert d["tile"] == "64x128" and int(d["splits"]) == split, d
+    prep = Prepared(q, fmt, N, K, G or 0, (67, N, K))
+    A = _act(fmt, M, K, (67, M))
+    check_against_oracle(q, prep, A, kernel_hint=2, split_k_hint=split, tile_hint=64)
+
+
 @pytest.mark.parametrize("fmt,G", [("int4", 32), ("int4", 128), ("int2", 32), ("nf4", 64), ("fp8", None),
                                    ("fp4", None)])
 @pytest.mark.parametrize("tile,split", [(64, 1), (64, 3), (128, 1), (128, 3), (256, 1), (256, 3)])
@@ -436,14 +460,15 @@ def test_mid_m_auto_plan(q, fmt, G, M, N, K):
 
 
 STREAMK_CASES = [
-    # (format, G, M, N, K, tile rows): tiles vs resident workgroups (256 for the 256- and
-    # 128-row tiles, 512 for the 64-row tile): a tail of whole rounds plus a part, and far
-    # fewer tiles than workgroups (every tile cut among several workgroups)
+    # (format, G, M, N, K, tile rows): tiles vs resident workgroups (256 for every tile: one
+    # workgroup per CU, as each tile's A stages take at least 96 KiB of LDS): a tail of whole
+    # rounds plus a part, and far fewer tiles than workgroups (every tile cut among several
+    # workgroups)
     ("fp8", None, 4352, 4096, 1024, 256),      # 17 x 16 = 272 tiles: 16 whole + 16 split in K
     ("int4", 64, 4352, 4112, 768, 256),        # ragged N: 17 x 17 = 289 tiles
     ("fp4", None, 2176, 2048, 1024, 128),      # 17 x 16 = 272 medium tiles
-    ("nf4", 128, 2112, 2048, 512, 64),         # 33 x 16 = 528 small tiles over 512 workgroups
-    ("int2", 32, 600, 784, 1024, 64),          # 10 x 7 = 70 tiles over 512 workgroups
+    ("nf4", 128, 2112, 2048, 512, 64),         # 33 x 16 = 528 small tiles: 256 whole + 272 split
+    ("int2", 32, 600, 784, 1024, 64),          # 10 x 7 = 70 tiles over 256 workgroups
     ("fp8h", None, 300, 272, 2048, 256),       # 2 x 2 tiles, 16 k blocks each, over 256 workgroups
     ("int4", 128, 1000, 4048, 1024, 128),      # 8 x 32 = 256 = one full round, no tail
 ]
@@ -464,7 +489,8 @@ def test_prefill_persistent_stream_k(q, fmt, G, M, N, K, tile):
     p = q.problem(M, N, K, fmt, group_size=G, kernel_hint=3, tile_hint=tile)
     assert ws is not None and q.workspace_bytes(p) > 0
     T = -(-N // (256 if tile == 256 else 128)) * -(-M // tile)          # output tiles
-    P = 512 if tile == 64 else 256                                       # resident workgroups
+    P = int(q.plan_fields(p)["persist"])                                 # resident workgroups
+    assert P == 256, P
     tail = T - ((T // P - 1) * P if T > P else 0)                        # tiles with tickets
     assert not ws[:4 * tail].cpu().numpy().any(), "stream-K tickets must return to zero"
     say(f"  E1={st['E1']:.3e} worstE2={st['E2_worst_ratio']:.3f}")
