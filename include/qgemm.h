@@ -94,6 +94,11 @@ typedef enum qgemm_scale_layout {
                                            tiles round-robin, the last rounds' tiles split
                                            evenly in K over the workgroups (stream-K tail);
                                            never chosen automatically                        */
+#define QGEMM_KERNEL_PREFILL_TRANSFORM 4 /* the MFMA tile kernel with dedicated dequantization
+                                           wavefronts (the transform warpgroup of FlashInfer
+                                           PR #7495 analysis, section 1): 64 x 128 tiles only
+                                           (tile_hint 0 or 64), any split; never chosen
+                                           automatically                                      */
 
 /*
  * The problem descriptor, after the BitBLAS MatmulConfig (Bitblas lecture 033, API
@@ -108,7 +113,8 @@ typedef enum qgemm_scale_layout {
  *   kernel_hint: QGEMM_KERNEL_*; split_k_hint: 0 = automatic, else the number of K
  *   slices (1..64) the chosen kernel uses (not with QGEMM_KERNEL_PREFILL_STREAMK); tile_hint: 0 = automatic, else for the decode
  *   kernel the number of 16-column blocks per workgroup (1 to 4), for the prefill
- *   kernel the rows of its workgroup tile (64: 64 x 128, 128: 128 x 128, 256: 256 x 256).
+ *   kernel the rows of its workgroup tile (64: 64 x 128, 128: 128 x 128, 256: 256 x 256;
+ *   QGEMM_KERNEL_PREFILL_TRANSFORM: 64 only).
  *   Hints only change the work split and the reduction order of the fp32 accumulation,
  *   never the packed layout; the automatic choice depends only on M, N, K and the formats
  *   (never on out_dtype or pointers).

@@ -59,6 +59,8 @@ BAD = [
     (dict(M=1, N=256, K=512, fmt="fp4", group_size=32), q.ERR_INVALID_ARGUMENT, "group_size 16"),
     (dict(M=17, N=256, K=512, fmt="int4", kernel_hint=q.KERNEL_DECODE), q.ERR_INVALID_ARGUMENT, "DECODE needs"),
     (dict(M=1, N=256, K=512, fmt="int4", kernel_hint=7), q.ERR_INVALID_ARGUMENT, "kernel_hint"),
+    (dict(M=1, N=256, K=512, fmt="int4", kernel_hint=5), q.ERR_INVALID_ARGUMENT, "kernel_hint"),
+    (dict(M=100, N=256, K=512, fmt="fp4", kernel_hint=4, tile_hint=128), q.ERR_INVALID_ARGUMENT, "PREFILL_TRANSFORM"),
     (dict(M=1, N=256, K=512, fmt="int4", split_k_hint=5), q.ERR_INVALID_ARGUMENT, "split_k_hint"),
     (dict(M=1, N=256, K=512, fmt="int4", split_k_hint=-1), q.ERR_INVALID_ARGUMENT, "split_k_hint"),
 ]
@@ -218,7 +220,7 @@ def test_planner_sweep_sizes_are_consistent():
     for fmt in ("int4", "int2", "nf4", "fp8", "fp8h", "fp4"):
         for M in sizes:
             for N, K in ((16, 128), (272, 768), (4096, 4096), (12800, 5120), (256, 131072)):
-                for hint, tile in ((0, 0), (2, 64), (2, 128), (2, 256), (3, 0), (3, 64)):
+                for hint, tile in ((0, 0), (2, 64), (2, 128), (2, 256), (3, 0), (3, 64), (4, 0), (4, 64)):
                     if hint == 2 and tile and tile * K * 2 >= 2 ** 31:
                         continue
                     p = q.problem(M, N, K, fmt, kernel_hint=hint, tile_hint=tile)
@@ -244,6 +246,11 @@ def test_plan_describe_fields_and_errors():
     d = q.plan_fields(q.problem(4096, 4096, 4096, "int4"))
     assert d["kernel"] == "prefill" and d["tile"] in ("64x128", "128x128", "256x256")
     assert q.plan_fields(q.problem(2176, 2048, 1024, "int4", kernel_hint=3))["persist"] != "0"
+    # dedicated dequantization wavefronts: the 64 x 128 tile, one-tile launch, any M (also M <= 16)
+    for M in (1, 100, 4096):
+        d = q.plan_fields(q.problem(M, 2048, 1024, "fp4", kernel_hint=q.KERNEL_PREFILL_TRANSFORM))
+        assert d["kernel"] == "prefill" and d["transform"] == "1" and d["tile"] == "64x128" and d["persist"] == "0", d
+    assert q.plan_fields(q.problem(4096, 4096, 4096, "int4"))["transform"] == "0"
     with pytest.raises(q.QgemmError) as e:
         q.plan_describe(q.problem(16, 250, 512, "int4"))
     assert e.value.status == q.ERR_INVALID_ARGUMENT

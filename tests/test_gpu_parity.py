@@ -226,6 +226,33 @@ def test_decode_dma_paths(q, fmt, G, M, N, K, plan):
     check_against_oracle(q, prep, A)
 
 
+TRANSFORM_CASES = [
+    # (format, G, M, N, K, split): the prefill kernel with dedicated dequantization wavefronts
+    # (64 x 128 tiles): ragged rows and columns (idle MFMA wavefronts past N), slices of one to
+    # many k blocks, every format and group size family
+    ("int4", 128, 100, 400, 1024, 1), ("int4", 32, 64, 256, 128, 1), ("int2", 64, 130, 528, 896, 2),
+    ("nf4", 128, 64, 1024, 2048, 3), ("fp8", None, 200, 272, 640, 1), ("fp8h", None, 17, 400, 1664, 2),
+    ("fp4", None, 128, 2048, 4096, 2), ("int4", 256, 300, 784, 2304, 4),
+]
+
+
+@pytest.mark.parametrize("fmt,G,M,N,K,split", TRANSFORM_CASES,
+                         ids=[f"{c[0]}-{c[2]}x{c[3]}x{c[4]}-s{c[5]}" for c in TRANSFORM_CASES])
+def test_prefill_transform_waves(q, fmt, G, M, N, K, split):
+    # kernel_hint PREFILL_TRANSFORM: every element against the oracle, and bitwise the same
+    # result on a second run.
+    say(f"case transform fmt={fmt} G={G} M={M} N={N} K={K} split={split}")
+    p = q.problem(M, N, K, fmt, group_size=G, kernel_hint=q.KERNEL_PREFILL_TRANSFORM, split_k_hint=split)
+    d = q.plan_fields(p)
+    assert d["kernel"] == "prefill" and d["transform"] == "1" and d["tile"] == "64x128", d
+    assert int(d["splits"]) == split, d
+    prep = Prepared(q, fmt, N, K, G or 0, (68, N, K))
+    A = _act(fmt, M, K, (68, M))
+    st, y0 = check_against_oracle(q, prep, A, kernel_hint=q.KERNEL_PREFILL_TRANSFORM, split_k_hint=split)
+    y1, _ = run_gpu(q, prep, A, q.DT_F32, kernel_hint=q.KERNEL_PREFILL_TRANSFORM, split_k_hint=split)
+    assert np.array_equal(y0, y1)
+
+
 SMALL_WINDOW_CASES = [
     # (format, G, K, split): the 64-row tile meets at a barrier every second k block and keeps
     # six A stages, so slices of 1, 2, 3, 5 and 7 k blocks end on a full window, inside one, or

@@ -35,7 +35,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(6)
 DT_F16, DT_BF16, DT_F32, DT_INT4, DT_FP8_E4M3, DT_FP4_E2M1, DT_INT2, DT_NF4 = range(8)
 SCALE_GROUP_F16, SCALE_TENSOR_F32, SCALE_BLOCK16_E4M3, SCALE_GROUP_F16_LUT16 = range(4)
-KERNEL_AUTO, KERNEL_DECODE, KERNEL_PREFILL, KERNEL_PREFILL_STREAMK = range(4)
+KERNEL_AUTO, KERNEL_DECODE, KERNEL_PREFILL, KERNEL_PREFILL_STREAMK, KERNEL_PREFILL_TRANSFORM = range(5)
 
 
 class Problem(ctypes.Structure):

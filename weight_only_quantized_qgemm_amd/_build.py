@@ -20,7 +20,7 @@ PROBE_LIB = os.path.join(PKG, "libqgemm_probe.so")
 # once per format (-DQGEMM_FMT_UNIT), so the many kernel instances build in parallel.
 N_FORMATS = 6
 UNITS = ([("qgemm_host.cpp", []), ("qgemm_run.hip", [])]
-         + [(k, [f"-DQGEMM_FMT_UNIT={f}"]) for k in ("qgemm_decode.hip", "qgemm_prefill.hip")
+         + [(k, [f"-DQGEMM_FMT_UNIT={f}"]) for k in ("qgemm_decode.hip", "qgemm_prefill.hip", "qgemm_prefill_tw.hip")
             for f in range(N_FORMATS)])
 
 HIPCC_FLAGS = [

@@ -477,6 +477,39 @@ __device__ bool splitk_finish(const KArgs& a, int tile, int split, int tile_elem
                               a.splits, [](int i) { return i; }, tile_elems, active, v);
 }
 
+// ----------------------------------------------------------------------------- barrier
+// Workgroup barrier without the release fence of __syncthreads(), which waits for every
+// outstanding load, the A stages still meant to be in flight included.  Callers first
+// wait for the loads that must have landed; every LDS read before the barrier has been
+// consumed (so completed) by then; the clobbers keep the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ----------------------------------------------------------------------------- tile walk
+// Output tile of workgroup b.  Workgroups are dispatched to the eight XCDs (each with its
+// own L2) round-robin by id, so the id is first mapped to a position such that each XCD
+// owns one contiguous range of positions; positions then walk the tile grid in bands of
+// GM tile rows, column by column, so that the tiles an XCD runs at the same time share
+// few A row blocks and weight column blocks.
+#ifndef QGEMM_PF_GM
+#define QGEMM_PF_GM 4
+#endif
+__device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& tm, int& tn) {
+  const int x = b & 7, slot = b >> 3, q = tiles >> 3, r = tiles & 7;
+  const int L = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+  const int tiles_m = tiles / tiles_n;
+  const int band = L / (QGEMM_PF_GM * tiles_n), first = band * QGEMM_PF_GM;
+  const int gm = min(QGEMM_PF_GM, tiles_m - first);
+  const int in = L - band * QGEMM_PF_GM * tiles_n;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+
 // ----------------------------------------------------------------------------- launchers
 // Launch the kernel instance the plan names on `stream`; return hipGetLastError().
 hipError_t launch_decode(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
@@ -486,6 +519,9 @@ template <int FMT>
 hipError_t launch_decode_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
 template <int FMT>
 hipError_t launch_prefill_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
+// The prefill kernel with dedicated dequantization wavefronts (kernel_hint PREFILL_TRANSFORM).
+template <int FMT>
+hipError_t launch_prefill_tw_format(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream);
 
 }  // namespace dev
 }  // namespace qgemm

@@ -95,8 +95,11 @@ qgemm_status_t validate_problem(const qgemm_problem_t* p) {
     return fail(QGEMM_ERR_UNSUPPORTED, "w_dtype %s is not a weight format (INT4, INT2, NF4, FP8_E4M3, FP4_E2M1)", dtype_name(w));
   }
 
-  if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL_STREAMK)
-    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint must be 0, 1, 2 or 3, got %d", p->kernel_hint);
+  if (p->kernel_hint < QGEMM_KERNEL_AUTO || p->kernel_hint > QGEMM_KERNEL_PREFILL_TRANSFORM)
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint must be 0 to 4, got %d", p->kernel_hint);
+  if (p->kernel_hint == QGEMM_KERNEL_PREFILL_TRANSFORM && p->tile_hint != 0 && p->tile_hint != pf_bm(kPfSmall))
+    return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint PREFILL_TRANSFORM has the %d x %d tile only; tile_hint must "
+                "be 0 or %d, got %d", pf_bm(kPfSmall), pf_bn(kPfSmall), pf_bm(kPfSmall), p->tile_hint);
   if (p->kernel_hint == QGEMM_KERNEL_PREFILL_STREAMK && p->split_k_hint != 0)
     return fail(QGEMM_ERR_INVALID_ARGUMENT, "kernel_hint PREFILL_STREAMK splits K itself; split_k_hint must be 0, got %d",
                 p->split_k_hint);
@@ -270,9 +273,13 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     // workgroup ranges cut nearly every tail tile) -- the chip's clock rises while a last round
     // runs partly idle -- and the one-tile launch needs no workspace.
     const bool sk_forced = p->kernel_hint == QGEMM_KERNEL_PREFILL_STREAMK;
+    // The kernel with dedicated dequantization wavefronts (on request only) has the 64 x 128
+    // tile; its split is priced like that tile's.
+    const bool tw = p->kernel_hint == QGEMM_KERNEL_PREFILL_TRANSFORM;
     for (int c = 0; c < 3; ++c) {
       const PfShape sh = cands[c].sh;
-      if (p->tile_hint ? p->tile_hint != pf_bm(sh) : (c > 0 && p->M <= pf_bm(cands[c - 1].sh))) continue;
+      if (tw && c > 0) continue;
+      if (!tw && (p->tile_hint ? p->tile_hint != pf_bm(sh) : (c > 0 && p->M <= pf_bm(cands[c - 1].sh)))) continue;
       if ((int64_t)pf_bm(sh) * p->K * 2 > 0x7fffffffLL) continue;     // the A tile uses 32-bit offsets
       const int64_t mt = (p->M + pf_bm(sh) - 1) / pf_bm(sh), nt = (p->N + pf_bn(sh) - 1) / pf_bn(sh);
       const int64_t T = mt * nt;
@@ -299,6 +306,7 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
                   p->tile_hint ? p->tile_hint : pf_bm(kPfSmall), (long long)p->K);
     pl->bm = pf_bm(cands[best_c].sh);
     pl->bn = pf_bn(cands[best_c].sh);
+    pl->transform = tw;
     const int64_t mt = (p->M + pl->bm - 1) / pl->bm, nt = (p->N + pl->bn - 1) / pl->bn;
     const bool persist = best == 0;
     pl->splits = persist ? 1 : best;
@@ -484,8 +492,8 @@ qgemm_status_t qgemm_plan_describe(const qgemm_problem_t* p, char* buf, size_t l
                       pl.kb_per_split, pl.lds_bytes, pl.ws_bytes);
   } else {
     n = std::snprintf(buf, len, "prefill grid=%ux%u tile=%dx%d splits=%d kb_per_split=%d persist=%d dp_tiles=%d "
-                      "ws=%zu", pl.grid_x, pl.grid_y, pl.bm, pl.bn, pl.splits, pl.kb_per_split, pl.persist,
-                      pl.dp_tiles, pl.ws_bytes);
+                      "transform=%d ws=%zu", pl.grid_x, pl.grid_y, pl.bm, pl.bn, pl.splits, pl.kb_per_split, pl.persist,
+                      pl.dp_tiles, pl.transform, pl.ws_bytes);
   }
   if (n < 0 || (size_t)n >= len) return fail(QGEMM_ERR_INVALID_ARGUMENT, "len %zu is too small (needs %d)", len, n + 1);
   return QGEMM_OK;

@@ -141,6 +141,7 @@ struct Plan {
   int lds_bytes;          // decode: dynamic LDS per workgroup (staged A, staged scales, wave tiles)
   // prefill: workgroup tile (bm selects the shape: pf_bm of kPfSmall, kPfMedium or kPfLarge)
   int bm, bn;
+  int transform;          // prefill: the kernel with dedicated dequantization wavefronts (64 x 128)
   // K split across workgroups (1 = none) and the 128-wide k-blocks each split covers
   int splits;
   int kb_per_split;

@@ -35,25 +35,7 @@ namespace {
 // sched_barrier pins the phase order (a load under a branch, or a consumer scheduled
 // early, would make the wavefront wait for all outstanding loads).
 
-// Workgroup barrier without the release fence of __syncthreads(), which waits for every
-// outstanding load, the A stages still meant to be in flight included.  Callers first
-// wait for the loads that must have landed; every LDS read before the barrier has been
-// consumed (so completed) by then; the clobbers keep the compiler from moving memory
-// operations across it.
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
-// Output tile of workgroup b.  Workgroups are dispatched to the eight XCDs (each with its
-// own L2) round-robin by id, so the id is first mapped to a position such that each XCD
-// owns one contiguous range of positions; positions then walk the tile grid in bands of
-// GM tile rows, column by column, so that the tiles an XCD runs at the same time share
-// few A row blocks and weight column blocks.
-#ifndef QGEMM_PF_GM
-#define QGEMM_PF_GM 4
-#endif
 #ifndef QGEMM_PF_DS
 #define QGEMM_PF_DS 1
 #endif
@@ -61,17 +43,6 @@ __device__ __forceinline__ void barrier_no_fence() {
 #ifndef QGEMM_PF_IDLE
 #define QGEMM_PF_IDLE 1
 #endif
-__device__ __forceinline__ void pf_tile_of(int b, int tiles, int tiles_n, int& tm, int& tn) {
-  const int x = b & 7, slot = b >> 3, q = tiles >> 3, r = tiles & 7;
-  const int L = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
-  const int tiles_m = tiles / tiles_n;
-  const int band = L / (QGEMM_PF_GM * tiles_n), first = band * QGEMM_PF_GM;
-  const int gm = min(QGEMM_PF_GM, tiles_m - first);
-  const int in = L - band * QGEMM_PF_GM * tiles_n;
-  tm = first + in % gm;
-  tn = in / gm;
-}
-
 // One piece of work of a prefill workgroup: output tile (tm, tn), its k blocks
 // [kb_begin, kb_end), and how the tile's sum is completed.  nslots == 1: this segment is the
 // whole sum and writes the output.  Otherwise the tile's nslots contributors hand off fp32

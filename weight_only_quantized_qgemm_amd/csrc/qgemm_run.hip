@@ -27,6 +27,17 @@ hipError_t launch_decode(const Plan& pl, int group_size, const KArgs& a, hipStre
 }
 
 hipError_t launch_prefill(const Plan& pl, int group_size, const KArgs& a, hipStream_t stream) {
+  if (pl.transform) {
+    switch (pl.fmt) {
+      case FMT_INT4: return launch_prefill_tw_format<FMT_INT4>(pl, group_size, a, stream);
+      case FMT_FP8: return launch_prefill_tw_format<FMT_FP8>(pl, group_size, a, stream);
+      case FMT_FP4: return launch_prefill_tw_format<FMT_FP4>(pl, group_size, a, stream);
+      case FMT_FP8H: return launch_prefill_tw_format<FMT_FP8H>(pl, group_size, a, stream);
+      case FMT_INT2: return launch_prefill_tw_format<FMT_INT2>(pl, group_size, a, stream);
+      case FMT_NF4: return launch_prefill_tw_format<FMT_NF4>(pl, group_size, a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (pl.fmt) {
     case FMT_INT4: return launch_prefill_format<FMT_INT4>(pl, group_size, a, stream);
     case FMT_FP8: return launch_prefill_format<FMT_FP8>(pl, group_size, a, stream);
