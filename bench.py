@@ -327,7 +327,7 @@ def cpu_baseline(budget_s=12.0):
             done_flops += fl
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 20:
+        if el >= budget_s or steps >= 64:
             break
     model = ""
     try:
