@@ -261,8 +261,9 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     double best_cost = 0.0;
     // Persistent schedule with a stream-K tail (split 0 below), on request only
     // (QGEMM_KERNEL_PREFILL_STREAMK): as many workgroups as are resident at once (as many per CU
-    // as their A stages fit in its 160 KiB of LDS: pf_per_cu); each takes whole tiles round-robin (the same tile ids, and so the same XCD-aware
-    // walk, as the one-tile launch) for all rounds but the last full one, and the tiles left
+    // as their A stages fit in its 160 KiB of LDS: pf_per_cu); each takes whole tiles
+    // round-robin (the same tile ids, and so the same XCD-aware walk, as the one-tile launch)
+    // for all rounds but the last full one, and the tiles left
     // (between one and two rounds' worth) are split evenly in K over all of them, so no round
     // runs partly idle.  Its cost: the k blocks of a workgroup's share plus two pipeline fills,
     // and about one partial tile per workgroup written and read back at once; the tile is the
@@ -317,8 +318,8 @@ qgemm_status_t make_plan(const qgemm_problem_t* p, Plan* pl) {
     pl->tiles = (int)(mt * nt);
     pl->tile_elems = pl->bm * pl->bn;
     const int64_t T = mt * nt;
-    const int P = kCUs * (pl->bm == pf_bm(kPfSmall) ? pf_per_cu(kPfSmall) : pl->bm == pf_bm(kPfMedium) ? pf_per_cu(kPfMedium)
-                                                                                           : pf_per_cu(kPfLarge));
+    const PfShape chosen = cands[best_c].sh;
+    const int P = kCUs * pf_per_cu(chosen);          // resident workgroups
     if (persist) {
       const int64_t dp = T > P ? (T / P - 1) * P : 0;
       if ((T - dp) * kblocks > 0x7fffffffLL)

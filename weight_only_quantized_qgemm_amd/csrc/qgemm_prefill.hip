@@ -10,8 +10,8 @@ namespace {
 // the workgroup tile is (16 WGM TM) x (16 WGN TN); one 128-wide k block per step.
 //
 // A goes from HBM straight into LDS (buffer loads with the LDS-destination bit: no VGPR
-// staging), double-buffered in two separate arrays so that the compiler can tell the
-// buffer being read from the one being filled.  A DMA load writes its 64 lanes' 16 bytes
+// staging), in ST stages (two to eight), each its own array so that the compiler can tell
+// the stage being read from the ones being filled.  A DMA load writes its 64 lanes' 16 bytes
 // contiguously, so LDS rows cannot be padded; instead the 16-byte chunk c of tile row r
 // is stored at chunk position c ^ (r & 15).  The MFMA A-fragment read (lane l: row l & 15,
 // chunk 4t + l / 16) then touches 16 distinct positions per 16 lanes: no bank conflicts.
@@ -19,8 +19,8 @@ namespace {
 // checked per-lane offset (the k block in the scalar offset never leaves its row), so rows
 // at or beyond M read as zero (and are never stored).
 //
-// Each wavefront loads its own packed weight fragments into registers (one k block
-// ahead) and dequantizes each once per K step, reusing it for its TM row tiles; the
+// Each wavefront loads its own packed weight fragments into registers (ST - BB k blocks
+// ahead, like its A) and dequantizes each once per K step, reusing it for its TM row tiles; the
 // dequantization of K step t + 1 is issued with the MFMAs of step t.  A fragments are
 // read from LDS in units of RU row tiles, LA units ahead of the MFMAs that consume them.
 // The weights enter each MFMA as its first operand and A as its second (both fragments
