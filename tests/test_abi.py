@@ -2,6 +2,8 @@
 return before anything is enqueued, workspace sizing.  No kernel is launched here."""
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -27,6 +29,15 @@ def test_every_declared_symbol_is_exported():
                           "qgemm_status_string", "qgemm_last_error", "qgemm_version"}
     for n in names:
         assert hasattr(q.lib, n), n
+
+
+def test_import_fails_loudly_without_the_library():
+    # no fallback: without the HIP library the binding refuses to load at all
+    env = dict(os.environ, QGEMM_LIB_PATH=os.path.join(ROOT, "_no_such_dir", "libqgemm.so"))
+    r = subprocess.run([sys.executable, "-c", "import weight_only_quantized_qgemm_amd"], capture_output=True,
+                       text=True, cwd=ROOT, env=env, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "is missing" in r.stderr and "_build" in r.stderr
 
 
 def test_status_strings_and_version():
