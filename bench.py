@@ -11,16 +11,16 @@ time) over them.
 Also reported: a `roofline` object for the decode kernel; `secondary`, every other
 workload shape timed the same way (rotating >= 512 MB of weight copies): the INT4 prefill
 M = 4096 over the group-size sweep, the FP8 shapes (M = 1, 16, 8192 x 10240 x 5120,
-32768 x 3200 x 5120, 16384 x 12800 x 5120) and the FP4 shapes (M = 1, 128, 8192 x 8192 x 8192),
-each with TFLOP/s and weight GB/s as fractions of the MFMA and HBM peaks; the CPU oracle
+32768 x 3200 x 5120, 16384 x 12800 x 5120), the FP4 shapes (M = 1, 128, 8192 x 8192 x 8192),
+FP8 with fp16 activations and a bias (M = 1, 16, 8192 x 10240 x 5120) and the INT2 and NF4
+shapes (M = 1, 16, 4096 x 4096 x 4096), each with TFLOP/s and weight GB/s as fractions of the MFMA and HBM peaks; the CPU oracle
 timed on the host as `cpu_baseline`; `hbm_context`, a hand-written streaming-read kernel
 (non-temporal 16-byte loads, no arithmetic) over the decode weight and scale byte counts
 and over 2 GiB, the time a kernel needs just to read those bytes; `host_overhead`, host
 time per qgemm_run call (validation, plan, launch); and `comparators`: on the decode
 shapes, the vendor 16-bit GEMM (hipBLASLt through torch) on a resident 16-bit weight and
 the cast-copy path (whole weight dequantized into HBM by torch ops, then that GEMM) --
-context, not target.  `--all` adds FP8 with fp16 activations and a bias, INT2 and NF4,
-and comparators for the FP8 / FP4 shapes and the INT4 prefill.
+context, not target.  `--all` adds comparators for the FP8 / FP4 shapes and the INT4 prefill.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
 """
@@ -349,8 +349,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--all", action="store_true",
-                    help="also time the FP8-with-fp16-activations (+bias), INT2 and NF4 workloads and the "
-                         "comparators of the FP8 / FP4 shapes and the INT4 prefill")
+                    help="also time the comparators of the FP8 / FP4 shapes and the INT4 prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--counter-pass", nargs="?", const="decode", choices=("decode", "prefill"),
@@ -469,8 +468,8 @@ def main():
                                     secondary[si]["us_per_launch"]))
 
     # every other workload shape, each on >= rot / 2 bytes of rotating weight copies: the INT4
-    # prefill over the group-size sweep, the FP8 and FP4 layer shapes (and with --all the FP8
-    # fp16-activation + bias, INT2 and NF4 workloads)
+    # prefill over the group-size sweep, the FP8 and FP4 layer shapes, the FP8 fp16-activation +
+    # bias, INT2 and NF4 workloads
     wi2 = synthetic.WORKLOAD_INDEX["int4_prefill"]
     for G in PREFILL_G:
         log(f"bench: int4 prefill G={G}")
@@ -483,7 +482,7 @@ def main():
                                         secondary[-1]["us_per_launch"]))
         del g
         torch.cuda.empty_cache()
-    names = ("fp8", "fp4") + (("fp8h", "int2", "nf4") if args.all else ())
+    names = ("fp8", "fp4", "fp8h", "int2", "nf4")
     for name in names:
         wk = synthetic.WORKLOADS[name]
         wix = synthetic.WORKLOAD_INDEX[name]
