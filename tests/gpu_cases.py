@@ -21,7 +21,11 @@ def say(msg):
 @functools.lru_cache(maxsize=8)
 def oracle_weights(fmt, N, K, G, key):
     """Oracle quantization of seeded weights: canonical bytes, scales, alpha, dequant [N,K]."""
-    w = synthetic.weights(N, K, SIGMA[fmt], key)
+    return quantize_weights(fmt, synthetic.weights(N, K, SIGMA[fmt], key), G)
+
+
+def quantize_weights(fmt, w, G):
+    """Oracle quantization of fp32 weights w [N, K]: canonical bytes, scales, alpha, dequant [N,K]."""
     if fmt == "int4":
         codes, sbits = quant.quantize_int4(w, G)
         return quant.pack_nibbles(codes), sbits, 1.0, reference.dequant_int4(codes, sbits, G)
@@ -48,10 +52,12 @@ def a_values(A16):
 class Prepared:
     """Device-resident packed weights for one (format, N, K, G)."""
 
-    def __init__(self, q, fmt, N, K, G, key, alpha_override=None):
+    def __init__(self, q, fmt, N, K, G, key, alpha_override=None, weights=None):
+        """key seeds the weights; or `weights` (fp32 [N, K]) gives them."""
         import torch
         self.fmt, self.N, self.K, self.G = fmt, N, K, G
-        canon, scales, alpha, self.wdq = oracle_weights(fmt, N, K, G, key)
+        canon, scales, alpha, self.wdq = (oracle_weights(fmt, N, K, G, key) if weights is None
+                                          else quantize_weights(fmt, weights, G))
         self.alpha = alpha if alpha_override is None else alpha_override
         p = q.problem(1, N, K, fmt, group_size=G if fmt in GROUPED else None)
         wpk, spk = q.pack(p, canon, scales)
