@@ -1,6 +1,7 @@
 """Host-side pieces of the benchmark (no GPU): the one-GPU guard, the algorithmic byte counts
 against the packer's sizes, and the recorded-traffic lookup."""
 import os
+import re
 import subprocess
 import sys
 
@@ -49,3 +50,21 @@ def test_measurement_library_loads_and_sizes_the_stream_grid():
     assert lib.qgemm_probe_stream(None, 1024, None, 0, None, 4, None) == -1
     assert lib.qgemm_probe_stream(16, 1000, None, 0, 16, 4, None) == -1       # not a multiple of 16
     assert lib.qgemm_probe_stream(16, 1024, None, 0, 16, 3, None) == -1       # U not offered
+
+
+def test_committed_counters_cover_the_algorithmic_bytes():
+    # bench sanity on the committed counter summaries: every profiled launch fetched at least
+    # the bytes it must read (weights and scales; for the prefill also A) and wrote at least its
+    # output, and the decode weight bytes there are the packer's sizes
+    txt = open(os.path.join(ROOT, "profiles", "qgemm_decode_int4_traffic.txt")).read()
+    rows = re.findall(r"M=(\d+)\s+N=(\d+)\s+K=(\d+).*->\s+([\d.]+) MB\s+\(weights\s+([\d.]+) MB", txt)
+    assert len(rows) == 4
+    for M, N, K, measured, weights in rows:
+        assert float(measured) >= float(weights)
+        assert abs(float(weights) * 1e6 - bench.weight_bytes("int4", int(N), int(K), 128)) < 1e3
+    txt = open(os.path.join(ROOT, "profiles", "qgemm_prefill_bench.txt")).read()
+    rows = re.findall(r"HBM fetch\s+([\d.]+) MB \(algorithmic A \+ weights\s+([\d.]+) MB\), "
+                      r"write\s+([\d.]+) MB \(output\s+([\d.]+) MB\)", txt)
+    assert len(rows) >= 5
+    for fetch, algorithmic, write, output in rows:
+        assert float(fetch) >= float(algorithmic) and float(write) >= float(output)
