@@ -1,5 +1,6 @@
 """Host-side pieces of the benchmark (no GPU): the one-GPU guard, the algorithmic byte counts
-against the packer's sizes, and the recorded-traffic lookup."""
+against the packer's sizes, the recorded-traffic lookup, and the committed counter summaries
+against the algorithmic bytes."""
 import os
 import re
 import subprocess
