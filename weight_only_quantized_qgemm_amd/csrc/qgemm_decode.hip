@@ -310,9 +310,15 @@ __global__ __launch_bounds__(64 * NW) void qgemm_decode(const uint8_t* W, const 
   const int c = tid >> 6, ln = tid & 63;
   f32x4 v[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
   if (active) {
-    v[0] = red[c * 64 + ln];
+    // every wave tile's read goes out before the first sum (summed in wave order as before):
+    // read and summed one after another, the compiler kept two reads in flight
+    f32x4 t[NW];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v[0] += red[(w * CB + c) * 64 + ln];
+    for (int w = 0; w < NW; ++w) t[w] = red[(w * CB + c) * 64 + ln];
+    __builtin_amdgcn_sched_barrier(0);
+    v[0] = t[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v[0] += t[w];
   }
   if (a.splits > 1) {
     if (!splitk_finish<1, NT>(a, group, split, CB * 256, active, v)) return;
