@@ -1,5 +1,5 @@
-"""Packed weights larger than 4 GiB (GPU): every weight byte offset past 2^32 must be formed in
-64-bit arithmetic, in the decode and in the prefill kernels.
+"""Packed weights, and activations, larger than 4 GiB (GPU): every byte offset past 2^32 must be
+formed in 64-bit arithmetic, in the decode and in the prefill kernels.
 
 The packed layout stores each 16-column block (its weights and its scales) contiguously, so
 the packed bytes of a matrix whose columns repeat with a period of three column blocks are
@@ -70,6 +70,52 @@ def test_weights_past_4_gib(q, ci):
         assert tolerance.gates_pass(st), st
     else:
         assert not st["nonfinite"] and not st["E2_fail_count"], st
+    say(f"  E1={st['E1']:.3e}")
+    del out
+    torch.cuda.empty_cache()
+
+
+# (format, row repeats T, N, kernel_hint): M = 48 T rows of A, 4.3 GB of activations
+A_CASES = [("int4", 11000, 256, 0),      # one 256 x 256 tile per workgroup
+           ("int4", 11000, 256, 3),      # persistent schedule with a stream-K tail
+           ("fp8", 11000, 384, 0)]       # ragged last tile column
+
+
+@pytest.mark.parametrize("ci", range(len(A_CASES)))
+def test_activations_past_4_gib(q, ci):
+    # A repeats with a period of 48 rows, so every output row must equal the row of its phase
+    # bitwise; a 32-bit wrap of A's offset at 2^32 bytes (row 524288 for K = 8192 bytes a row)
+    # would read a row of another phase (524288 mod 48 = 32).
+    fmt, T, N, hint = A_CASES[ci]
+    M, Kq = P * T, 4096
+    G = 128 if fmt in GROUPED else 0
+    p = q.problem(M, N, Kq, fmt, group_size=G or None, out_dtype=q.DT_F32, kernel_hint=hint)
+    assert M * Kq * 2 > (1 << 32), "the case must put activation offsets past 2^32"
+    say(f"case large-activations#{ci} fmt={fmt} M={M} N={N} K={Kq} A {M * Kq * 2 / 1e9:.2f} GB "
+        f"plan={q.plan_describe(p)}")
+    prep = Prepared(q, fmt, N, Kq, G, (76, ci))
+    A_small = synthetic.activations(P, Kq, out16_kind(fmt), (76, ci, P))
+    A = A_small.cuda().repeat(T, 1)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    q.run(p, A, prep.w, prep.s, None if fmt in GROUPED else prep.alpha_t, out, q.alloc_workspace(p))
+    torch.cuda.synchronize()
+    del A
+    per = out.view(T, P, N)
+    if hint != q.KERNEL_PREFILL_STREAMK:
+        bits = out.view(torch.int32).view(T, P, N)
+        assert bool((bits == bits[:1]).all()), "a row differs from the row of the same phase"
+    else:
+        # the stream-K tail sums a tile's K range in pieces handed between workgroups, so its
+        # rows round differently from rows computed in one pass: equal to rounding, and bitwise
+        # equal wherever both rows lie in whole tiles (the first dp_tiles tiles of the walk)
+        d = (per - per[:1]).abs()
+        rel = float((d / (per[:1].abs() + 1.0)).max())
+        rows = int((d.amax(dim=2) > 0).sum())
+        say(f"  stream-K: {rows} of {M} rows differ from the row of the same phase, by at most {rel:.2e}")
+        assert rel < 1e-5, rel
+    y = out[:P].cpu().numpy().astype(np.float64)
+    st = tolerance.error_stats(y, reference.gemm_fp64(a_values(A_small), prep.wdq, prep.alpha))
+    assert tolerance.gates_pass(st), st
     say(f"  E1={st['E1']:.3e}")
     del out
     torch.cuda.empty_cache()
