@@ -75,10 +75,11 @@ def test_weights_past_4_gib(q, ci):
     torch.cuda.empty_cache()
 
 
-# (format, row repeats T, N, kernel_hint): M = 48 T rows of A, 4.3 GB of activations
-A_CASES = [("int4", 11000, 256, 0),      # one 256 x 256 tile per workgroup
-           ("int4", 11000, 256, 3),      # persistent schedule with a stream-K tail
-           ("fp8", 11000, 384, 0)]       # ragged last tile column
+# (format, row repeats T, N, kernel_hint, 16-bit output): M = 48 T rows of A, 4.3 GB of activations
+A_CASES = [("int4", 11000, 256, 0, False),     # one 256 x 256 tile per workgroup
+           ("int4", 11000, 256, 3, False),     # persistent schedule with a stream-K tail
+           ("fp8", 11000, 384, 0, False),      # ragged last tile column
+           ("int4", 11000, 4096, 0, True)]     # and 4.3 GB of 16-bit output
 
 
 @pytest.mark.parametrize("ci", range(len(A_CASES)))
@@ -86,23 +87,25 @@ def test_activations_past_4_gib(q, ci):
     # A repeats with a period of 48 rows, so every output row must equal the row of its phase
     # bitwise; a 32-bit wrap of A's offset at 2^32 bytes (row 524288 for K = 8192 bytes a row)
     # would read a row of another phase (524288 mod 48 = 32).
-    fmt, T, N, hint = A_CASES[ci]
+    fmt, T, N, hint, out16 = A_CASES[ci]
     M, Kq = P * T, 4096
     G = 128 if fmt in GROUPED else 0
-    p = q.problem(M, N, Kq, fmt, group_size=G or None, out_dtype=q.DT_F32, kernel_hint=hint)
+    tdt = torch.float32 if not out16 else (torch.float16 if out16_kind(fmt) == "f16" else torch.bfloat16)
+    odt = q.DT_F32 if not out16 else (q.DT_F16 if out16_kind(fmt) == "f16" else q.DT_BF16)
+    p = q.problem(M, N, Kq, fmt, group_size=G or None, out_dtype=odt, kernel_hint=hint)
     assert M * Kq * 2 > (1 << 32), "the case must put activation offsets past 2^32"
     say(f"case large-activations#{ci} fmt={fmt} M={M} N={N} K={Kq} A {M * Kq * 2 / 1e9:.2f} GB "
         f"plan={q.plan_describe(p)}")
     prep = Prepared(q, fmt, N, Kq, G, (76, ci))
     A_small = synthetic.activations(P, Kq, out16_kind(fmt), (76, ci, P))
     A = A_small.cuda().repeat(T, 1)
-    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((M, N), float("nan"), dtype=tdt, device="cuda")
     q.run(p, A, prep.w, prep.s, None if fmt in GROUPED else prep.alpha_t, out, q.alloc_workspace(p))
     torch.cuda.synchronize()
     del A
     per = out.view(T, P, N)
     if hint != q.KERNEL_PREFILL_STREAMK:
-        bits = out.view(torch.int32).view(T, P, N)
+        bits = out.view(torch.int32 if not out16 else torch.int16).view(T, P, N)
         assert bool((bits == bits[:1]).all()), "a row differs from the row of the same phase"
     else:
         # the stream-K tail sums a tile's K range in pieces handed between workgroups, so its
@@ -113,9 +116,13 @@ def test_activations_past_4_gib(q, ci):
         rows = int((d.amax(dim=2) > 0).sum())
         say(f"  stream-K: {rows} of {M} rows differ from the row of the same phase, by at most {rel:.2e}")
         assert rel < 1e-5, rel
-    y = out[:P].cpu().numpy().astype(np.float64)
+    head = out[:P].cpu()
+    y = head.numpy().astype(np.float64) if not out16 else out16_values(head.view(torch.int16).numpy().view(np.uint16), fmt)
     st = tolerance.error_stats(y, reference.gemm_fp64(a_values(A_small), prep.wdq, prep.alpha))
-    assert tolerance.gates_pass(st), st
+    if not out16:
+        assert tolerance.gates_pass(st), st
+    else:
+        assert not st["nonfinite"] and not st["E2_fail_count"], st
     say(f"  E1={st['E1']:.3e}")
-    del out
+    del out, per
     torch.cuda.empty_cache()
