@@ -300,3 +300,32 @@ def test_decode_plans_fit_lds_and_take_dma_above_staging():
                     if d["a"] == "dma":
                         sets = 2 if runs > 1 else 1
                         assert sets * waves * kpw * 4096 + int(d["lds"]) + 2048 <= 160 * 1024, (fmt, M, N, K, d)
+
+
+def test_errors_and_plans_are_per_thread():
+    # qgemm_last_error is per calling thread and the validation / planning code keeps no shared
+    # state: eight threads (ctypes releases the GIL, so the calls overlap) interleave failing and
+    # valid queries, and each reads back its own message and the same plans as a lone caller
+    import threading
+    bad = [q.problem(1, 250 + 16 * i, 512, "int4") for i in range(8)]       # N not a multiple of 16
+    good = [q.problem(1 + 97 * i, 4096, 4096, "int4") for i in range(8)]
+    want = [q.plan_describe(p) for p in good]
+    errors = []
+
+    def worker(i):
+        try:
+            for _ in range(300):
+                assert q.run_raw(bad[i], 16, 16, 16, None, 16, None, 0, None) == q.ERR_INVALID_ARGUMENT
+                msg = q.last_error()
+                assert "N must be" in msg and str(250 + 16 * i) in msg, msg
+                assert q.plan_describe(good[i]) == want[i]
+                assert q.last_error() == ""
+        except Exception as e:                     # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[0]
